@@ -1,0 +1,247 @@
+/*
+ * msa_oracle.c — plain, slow, single-threaded CPU oracle of the MSA forward
+ * pass.  TEST INFRASTRUCTURE ONLY (see msa_oracle.h for the pages followed,
+ * the readings taken and the layouts).  Every loop here is the definition
+ * written out; there is no tiling, fusion or reordering.
+ */
+#include "msa_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Exact value of a bf16 bit pattern: the top half of an IEEE binary32. */
+static double bf16_value(uint16_t bits) {
+  uint32_t w = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &w, sizeof f);
+  return (double)f;
+}
+
+static int problem_ok(const oracle_problem* p) {
+  if (!p) return 0;
+  if (p->batch <= 0 || p->seq_q <= 0 || p->seq_kv <= 0 || p->q_start < 0) return 0;
+  if (p->n_q_heads <= 0 || p->n_kv_heads <= 0 || p->n_q_heads % p->n_kv_heads != 0) return 0;
+  if (p->head_dim <= 0 || p->idx_head_dim <= 0 || p->block_size <= 0 || p->top_k <= 0) return 0;
+  /* every KV head needs at least one index head attributed to it */
+  if (p->n_idx_heads < p->n_kv_heads || p->n_idx_heads % p->n_kv_heads != 0) return 0;
+  if (p->decode) {
+    if (p->seq_q != 1) return 0;
+  } else if ((int64_t)p->q_start + p->seq_q > p->seq_kv) {
+    return 0;
+  }
+  return 1;
+}
+
+int32_t oracle_num_blocks(const oracle_problem* p) {
+  return (p->seq_kv + p->block_size - 1) / p->block_size;
+}
+
+int32_t oracle_position(const oracle_problem* p, const int32_t* seq_lens, int32_t b, int32_t t) {
+  if (!problem_ok(p) || b < 0 || b >= p->batch || t < 0 || t >= p->seq_q) return -1;
+  if (p->decode) {
+    if (!seq_lens) return -1;
+    int32_t L = seq_lens[b];
+    if (L < 1 || L > p->seq_kv) return -1;
+    return L - 1;
+  }
+  return p->q_start + t;
+}
+
+/* Index score of token j against index head i of row (b, t): the raw dot
+ * product of index-query and index-key ([A] index branch: 4 query heads
+ * against one key head). */
+static double index_score(const oracle_problem* p, const uint16_t* iq, const uint16_t* ik,
+                          int32_t b, int32_t t, int32_t i, int32_t j) {
+  const int Di = p->idx_head_dim;
+  const uint16_t* qv = iq + (((int64_t)b * p->seq_q + t) * p->n_idx_heads + i) * Di;
+  const uint16_t* kv = ik + ((int64_t)b * p->seq_kv + j) * Di;
+  double s = 0.0;
+  for (int d = 0; d < Di; ++d) s += bf16_value(qv[d]) * bf16_value(kv[d]);
+  return s;
+}
+
+int oracle_block_scores_row(const oracle_problem* p, const uint16_t* iq, const uint16_t* ik,
+                            const int32_t* seq_lens, int32_t b, int32_t t, float* out) {
+  int32_t pos = oracle_position(p, seq_lens, b, t);
+  if (pos < 0 || !iq || !ik || !out) return ORACLE_EBADARG;
+  const int32_t nblk = oracle_num_blocks(p);
+  const int32_t bs = p->block_size;
+  const int32_t cur = pos / bs;
+  for (int32_t h = 0; h < p->n_kv_heads; ++h) {
+    for (int32_t c = 0; c < nblk; ++c) {
+      float value;
+      if (c < cur) {
+        /* every token of block c precedes the query's own block, so all of
+         * them are causal */
+        double best = -INFINITY;
+        for (int32_t i = 0; i < p->n_idx_heads; ++i) {
+          if (i % p->n_kv_heads != h) continue; /* index head i drives KV head i mod Hkv */
+          for (int32_t j = c * bs; j < (c + 1) * bs; ++j) {
+            double s = index_score(p, iq, ik, b, t, i, j);
+            if (isnan(s)) return ORACLE_ENAN;
+            if (s > best) best = s;
+          }
+        }
+        value = (float)best; /* round to nearest fp32: the decision precision */
+      } else if (c == cur) {
+        value = INFINITY; /* own block always kept */
+      } else {
+        value = -INFINITY; /* future block: never a candidate */
+      }
+      out[(int64_t)h * nblk + c] = value;
+    }
+  }
+  return ORACLE_OK;
+}
+
+int oracle_select_row(const oracle_problem* p, const float* scores, int32_t cur, int32_t* sel) {
+  if (!p || !scores || !sel || cur < 0 || p->top_k <= 0) return ORACLE_EBADARG;
+  const int32_t n = cur + 1;
+  const int32_t m = p->top_k < n ? p->top_k : n;
+  char* chosen = (char*)calloc((size_t)n, 1);
+  if (!chosen) return ORACLE_ENOMEM;
+  for (int32_t c = 0; c < n; ++c)
+    if (isnan(scores[c])) { free(chosen); return ORACLE_ENAN; }
+  /* m rounds of "take the best remaining candidate": best = highest score,
+   * and among equal scores the lowest block index (the ascending scan with a
+   * strict comparison keeps the first, i.e. lowest, index).  -0 and +0 compare
+   * equal as reals. */
+  for (int32_t r = 0; r < m; ++r) {
+    int32_t best = -1;
+    for (int32_t c = 0; c < n; ++c) {
+      if (chosen[c]) continue;
+      if (best < 0 || scores[c] > scores[best]) best = c;
+    }
+    chosen[best] = 1;
+  }
+  int32_t w = 0;
+  for (int32_t c = 0; c < n; ++c)
+    if (chosen[c]) sel[w++] = c;
+  for (; w < p->top_k; ++w) sel[w] = -1;
+  free(chosen);
+  return ORACLE_OK;
+}
+
+int oracle_attend_row(const oracle_problem* p, const uint16_t* q, const uint16_t* k,
+                      const uint16_t* v, const int32_t* seq_lens, const int32_t* sel,
+                      int32_t b, int32_t t, double* out, double* lse) {
+  int32_t pos = oracle_position(p, seq_lens, b, t);
+  if (pos < 0 || !q || !k || !v || !sel || !out || !lse) return ORACLE_EBADARG;
+  const int32_t D = p->head_dim, bs = p->block_size, K = p->top_k;
+  const int32_t G = p->n_q_heads / p->n_kv_heads;
+  const int32_t nblk = oracle_num_blocks(p);
+  int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * (size_t)K * bs);
+  double* z = (double*)malloc(sizeof(double) * (size_t)K * bs);
+  if (!tok || !z) { free(tok); free(z); return ORACLE_ENOMEM; }
+  int rc = ORACLE_OK;
+  for (int32_t hq = 0; hq < p->n_q_heads && rc == ORACLE_OK; ++hq) {
+    const int32_t h = hq / G; /* contiguous query-head groups per KV head */
+    /* T: the tokens of the blocks KV head h selected, causal (j <= pos) */
+    int32_t n = 0;
+    for (int32_t r = 0; r < K; ++r) {
+      int32_t c = sel[(int64_t)h * K + r];
+      if (c < 0) continue;
+      if (c >= nblk) { rc = ORACLE_EBADARG; break; }
+      for (int32_t j = c * bs; j < (c + 1) * bs && j <= pos; ++j) tok[n++] = j;
+    }
+    if (rc != ORACLE_OK) break;
+    double* o = out + (int64_t)hq * D;
+    if (n == 0) { /* nothing to attend: defined as zero output, lse -inf */
+      for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+      lse[hq] = -INFINITY;
+      continue;
+    }
+    const uint16_t* qv = q + (((int64_t)b * p->seq_q + t) * p->n_q_heads + hq) * D;
+    double zmax = -INFINITY;
+    for (int32_t a = 0; a < n; ++a) {
+      const uint16_t* kv = k + (((int64_t)b * p->n_kv_heads + h) * p->seq_kv + tok[a]) * D;
+      double s = 0.0;
+      for (int32_t d = 0; d < D; ++d) s += bf16_value(qv[d]) * bf16_value(kv[d]);
+      z[a] = p->softmax_scale * s;
+      if (z[a] > zmax) zmax = z[a];
+    }
+    double l = 0.0;
+    for (int32_t a = 0; a < n; ++a) { z[a] = exp(z[a] - zmax); l += z[a]; }
+    for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+    for (int32_t a = 0; a < n; ++a) {
+      const uint16_t* vv = v + (((int64_t)b * p->n_kv_heads + h) * p->seq_kv + tok[a]) * D;
+      for (int32_t d = 0; d < D; ++d) o[d] += z[a] * bf16_value(vv[d]);
+    }
+    for (int32_t d = 0; d < D; ++d) o[d] /= l;
+    lse[hq] = zmax + log(l);
+  }
+  free(tok);
+  free(z);
+  return rc;
+}
+
+int oracle_dense_row(const oracle_problem* p, const uint16_t* q, const uint16_t* k,
+                     const uint16_t* v, const int32_t* seq_lens, int32_t b, int32_t t,
+                     double* out, double* lse) {
+  int32_t pos = oracle_position(p, seq_lens, b, t);
+  if (pos < 0 || !q || !k || !v || !out || !lse) return ORACLE_EBADARG;
+  const int32_t D = p->head_dim;
+  const int32_t nkeys = pos + 1;
+  double* w = (double*)malloc(sizeof(double) * (size_t)nkeys);
+  if (!w) return ORACLE_ENOMEM;
+  for (int32_t hq = 0; hq < p->n_q_heads; ++hq) {
+    const int32_t kvh = hq / (p->n_q_heads / p->n_kv_heads);
+    const uint16_t* qrow = q + ((int64_t)(b * p->seq_q + t) * p->n_q_heads + hq) * D;
+    const uint16_t* kbase = k + ((int64_t)b * p->n_kv_heads + kvh) * p->seq_kv * D;
+    const uint16_t* vbase = v + ((int64_t)b * p->n_kv_heads + kvh) * p->seq_kv * D;
+    /* pass 1: logits and their maximum */
+    double top = -INFINITY;
+    for (int32_t j = 0; j < nkeys; ++j) {
+      double acc = 0.0;
+      for (int32_t d = 0; d < D; ++d)
+        acc += bf16_value(qrow[d]) * bf16_value(kbase[(int64_t)j * D + d]);
+      w[j] = acc * p->softmax_scale;
+      if (w[j] > top) top = w[j];
+    }
+    /* pass 2: normaliser */
+    double denom = 0.0;
+    for (int32_t j = 0; j < nkeys; ++j) denom += exp(w[j] - top);
+    /* pass 3: probabilities */
+    for (int32_t j = 0; j < nkeys; ++j) w[j] = exp(w[j] - top) / denom;
+    /* pass 4: probability-weighted values, one output element at a time */
+    for (int32_t d = 0; d < D; ++d) {
+      double acc = 0.0;
+      for (int32_t j = 0; j < nkeys; ++j) acc += w[j] * bf16_value(vbase[(int64_t)j * D + d]);
+      out[(int64_t)hq * D + d] = acc;
+    }
+    lse[hq] = top + log(denom);
+  }
+  free(w);
+  return ORACLE_OK;
+}
+
+int oracle_forward_rows(const oracle_problem* p, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const uint16_t* iq, const uint16_t* ik,
+                        const int32_t* seq_lens, int64_t n_rows, const int64_t* rows,
+                        int32_t* sel_out, double* out, double* lse, float* scores_out) {
+  if (!problem_ok(p) || n_rows < 0 || (n_rows > 0 && !rows) || !sel_out || !out || !lse)
+    return ORACLE_EBADARG;
+  const int32_t nblk = oracle_num_blocks(p);
+  const int32_t Hkv = p->n_kv_heads, K = p->top_k;
+  float* bsrow = (float*)malloc(sizeof(float) * (size_t)Hkv * nblk);
+  if (!bsrow) return ORACLE_ENOMEM;
+  int rc = ORACLE_OK;
+  for (int64_t r = 0; r < n_rows && rc == ORACLE_OK; ++r) {
+    const int64_t row = rows[r];
+    if (row < 0 || row >= (int64_t)p->batch * p->seq_q) { rc = ORACLE_EBADARG; break; }
+    const int32_t b = (int32_t)(row / p->seq_q), t = (int32_t)(row % p->seq_q);
+    const int32_t cur = oracle_position(p, seq_lens, b, t) / p->block_size;
+    rc = oracle_block_scores_row(p, iq, ik, seq_lens, b, t, bsrow);
+    if (rc != ORACLE_OK) break;
+    if (scores_out) memcpy(scores_out + r * Hkv * nblk, bsrow, sizeof(float) * (size_t)Hkv * nblk);
+    int32_t* sel = sel_out + r * Hkv * K;
+    for (int32_t h = 0; h < Hkv && rc == ORACLE_OK; ++h)
+      rc = oracle_select_row(p, bsrow + (int64_t)h * nblk, cur, sel + (int64_t)h * K);
+    if (rc != ORACLE_OK) break;
+    rc = oracle_attend_row(p, q, k, v, seq_lens, sel, b, t, out + r * p->n_q_heads * p->head_dim,
+                           lse + r * p->n_q_heads);
+  }
+  free(bsrow);
+  return rc;
+}
