@@ -1,7 +1,12 @@
 """MI355X-native (gfx950) forward hot path of MiniMax Sparse Attention (MSA).
 
-The compute lives in the HIP/C-ABI library ``libmsa.so`` built from ``csrc/``;
-this package only marshals arguments to it (see ``binding``), describes the
-workloads (``configs``) and draws seeded synthetic inputs (``inputs``).
+The compute lives in the HIP/C-ABI library ``libmsa.so`` built from ``csrc/``
+(``python -m block_sparse_gqa_02_amd.build``); ``binding`` marshals arguments
+to it under the C names, ``configs`` describes the workloads and ``inputs``
+draws seeded synthetic inputs.  The library is loaded on first use.
 """
 from . import configs, inputs  # noqa: F401
+from .binding import (Problem, MsaError, abi_version, msa_dense_attn_decode,  # noqa: F401
+                      msa_dense_attn_prefill, msa_index_block_scores, msa_index_topk_fused,
+                      msa_sparse_attn_decode, msa_sparse_attn_prefill, msa_topk_blocks,
+                      msa_workspace_bytes)

@@ -1,0 +1,230 @@
+"""Thin ctypes binding of libmsa.so: the C entry points under the same names.
+
+Argument marshalling only: every step of the hot path runs in the HIP kernels
+of the library.  Tensors are torch tensors on the GPU (torch provides device
+memory and the stream); outputs and workspaces are caller-provided, or
+allocated here with torch when passed as None.  If the library is missing the
+import of any entry point fails loudly; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, fields
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmsa.so")
+
+MSA_OK = 0
+STATUS = {0: "MSA_OK", 1: "MSA_ERR_INVALID_ARGUMENT", 2: "MSA_ERR_UNSUPPORTED",
+          3: "MSA_ERR_WORKSPACE_TOO_SMALL", 4: "MSA_ERR_HIP"}
+OPS = {"index_block_scores": 0, "topk_blocks": 1, "index_topk_fused": 2,
+       "sparse_attn_prefill": 3, "sparse_attn_decode": 4, "dense_attn_prefill": 5,
+       "dense_attn_decode": 6}
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class _CProblem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "seq_q", "seq_kv", "q_start", "n_q_heads", "n_kv_heads", "head_dim",
+        "n_idx_heads", "idx_head_dim", "block_size", "top_k")] + [("softmax_scale", ctypes.c_float)]
+
+
+@dataclass
+class Problem:
+    """Mirror of msa_problem."""
+    batch: int
+    seq_q: int
+    seq_kv: int
+    q_start: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    n_idx_heads: int
+    idx_head_dim: int
+    block_size: int
+    top_k: int
+    softmax_scale: float
+
+    @classmethod
+    def from_workload(cls, w, **override) -> "Problem":
+        kw = {f.name: getattr(w, f.name) for f in fields(cls) if f.name != "softmax_scale"}
+        kw["softmax_scale"] = w.softmax_scale
+        kw.update(override)
+        return cls(**kw)
+
+    def c(self) -> _CProblem:
+        return _CProblem(*(int(getattr(self, f.name)) for f in fields(self)
+                           if f.name != "softmax_scale"), float(self.softmax_scale))
+
+    @property
+    def nblk(self) -> int:
+        return (self.seq_kv + self.block_size - 1) // self.block_size
+
+
+_lib = None
+
+
+def lib():
+    """Load libmsa.so (built by block_sparse_gqa_02_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_gqa_02_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, vp, sz = ctypes.POINTER, ctypes.c_void_p, ctypes.c_size_t
+        pr = P(_CProblem)
+        sig = {
+            "msa_index_block_scores": [pr, vp, vp, vp, vp, vp],
+            "msa_topk_blocks": [pr, vp, vp, vp, vp],
+            "msa_index_topk_fused": [pr, vp, vp, vp, vp, vp, sz, vp],
+            "msa_sparse_attn_prefill": [pr, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "msa_sparse_attn_decode": [pr, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "msa_dense_attn_prefill": [pr, vp, vp, vp, vp, vp, vp, sz, vp],
+            "msa_dense_attn_decode": [pr, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "msa_workspace_bytes": [pr, ctypes.c_int, P(sz)],
+        }
+        for name, args in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.msa_status_string.argtypes = [ctypes.c_int]
+        L.msa_status_string.restype = ctypes.c_char_p
+        L.msa_last_error.argtypes = []
+        L.msa_last_error.restype = ctypes.c_char_p
+        L.msa_abi_version.argtypes = []
+        L.msa_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != MSA_OK:
+        raise MsaError(status, lib().msa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None):
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError("tensors must live on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def abi_version() -> int:
+    return lib().msa_abi_version()
+
+
+def msa_workspace_bytes(p: Problem, op: str) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().msa_workspace_bytes(ctypes.byref(p.c()), OPS[op], ctypes.byref(out)))
+    return out.value
+
+
+def _workspace(p: Problem, op: str, ws, device):
+    need = msa_workspace_bytes(p, op)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def msa_index_block_scores(p: Problem, iq, ik, seq_lens=None, block_scores=None, stream=None):
+    if block_scores is None:
+        block_scores = torch.empty((p.batch, p.n_kv_heads, p.seq_q, p.nblk), dtype=torch.float32,
+                                   device=iq.device)
+    _check(lib().msa_index_block_scores(ctypes.byref(p.c()), _ptr(iq, torch.bfloat16),
+                                        _ptr(ik, torch.bfloat16), _ptr(seq_lens, torch.int32),
+                                        _ptr(block_scores, torch.float32), _stream(stream)))
+    return block_scores
+
+
+def msa_topk_blocks(p: Problem, block_scores, seq_lens=None, sel=None, stream=None):
+    if sel is None:
+        sel = torch.empty((p.batch, p.n_kv_heads, p.seq_q, p.top_k), dtype=torch.int32,
+                          device=block_scores.device)
+    _check(lib().msa_topk_blocks(ctypes.byref(p.c()), _ptr(block_scores, torch.float32),
+                                 _ptr(seq_lens, torch.int32), _ptr(sel, torch.int32),
+                                 _stream(stream)))
+    return sel
+
+
+def msa_index_topk_fused(p: Problem, iq, ik, seq_lens=None, sel=None, workspace=None,
+                         stream=None):
+    if sel is None:
+        sel = torch.empty((p.batch, p.n_kv_heads, p.seq_q, p.top_k), dtype=torch.int32,
+                          device=iq.device)
+    ws, nbytes = _workspace(p, "index_topk_fused", workspace, iq.device)
+    _check(lib().msa_index_topk_fused(ctypes.byref(p.c()), _ptr(iq, torch.bfloat16),
+                                      _ptr(ik, torch.bfloat16), _ptr(seq_lens, torch.int32),
+                                      _ptr(sel, torch.int32), _ptr(ws), nbytes, _stream(stream)))
+    return sel
+
+
+def msa_sparse_attn_prefill(p: Problem, q, k, v, sel, out=None, lse=None, workspace=None,
+                            stream=None):
+    if out is None:
+        out = torch.empty_like(q)
+    ws, nbytes = _workspace(p, "sparse_attn_prefill", workspace, q.device)
+    _check(lib().msa_sparse_attn_prefill(ctypes.byref(p.c()), _ptr(q, torch.bfloat16),
+                                         _ptr(k, torch.bfloat16), _ptr(v, torch.bfloat16),
+                                         _ptr(sel, torch.int32), _ptr(out, torch.bfloat16),
+                                         _ptr(lse, torch.float32), _ptr(ws), nbytes,
+                                         _stream(stream)))
+    return out
+
+
+def msa_sparse_attn_decode(p: Problem, q, k_cache, v_cache, seq_lens, sel, out=None, lse=None,
+                           workspace=None, stream=None):
+    if out is None:
+        out = torch.empty_like(q)
+    ws, nbytes = _workspace(p, "sparse_attn_decode", workspace, q.device)
+    _check(lib().msa_sparse_attn_decode(ctypes.byref(p.c()), _ptr(q, torch.bfloat16),
+                                        _ptr(k_cache, torch.bfloat16),
+                                        _ptr(v_cache, torch.bfloat16), _ptr(seq_lens, torch.int32),
+                                        _ptr(sel, torch.int32), _ptr(out, torch.bfloat16),
+                                        _ptr(lse, torch.float32), _ptr(ws), nbytes,
+                                        _stream(stream)))
+    return out
+
+
+def msa_dense_attn_prefill(p: Problem, q, k, v, out=None, lse=None, workspace=None, stream=None):
+    if out is None:
+        out = torch.empty_like(q)
+    ws, nbytes = _workspace(p, "dense_attn_prefill", workspace, q.device)
+    _check(lib().msa_dense_attn_prefill(ctypes.byref(p.c()), _ptr(q, torch.bfloat16),
+                                        _ptr(k, torch.bfloat16), _ptr(v, torch.bfloat16),
+                                        _ptr(out, torch.bfloat16), _ptr(lse, torch.float32),
+                                        _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def msa_dense_attn_decode(p: Problem, q, k_cache, v_cache, seq_lens, out=None, lse=None,
+                          workspace=None, stream=None):
+    if out is None:
+        out = torch.empty_like(q)
+    ws, nbytes = _workspace(p, "dense_attn_decode", workspace, q.device)
+    _check(lib().msa_dense_attn_decode(ctypes.byref(p.c()), _ptr(q, torch.bfloat16),
+                                       _ptr(k_cache, torch.bfloat16),
+                                       _ptr(v_cache, torch.bfloat16), _ptr(seq_lens, torch.int32),
+                                       _ptr(out, torch.bfloat16), _ptr(lse, torch.float32),
+                                       _ptr(ws), nbytes, _stream(stream)))
+    return out

@@ -1,0 +1,212 @@
+// attn_sparse.hip — main branch of MSA: exact GQA attention over each KV
+// head's selected 64-token blocks (topic page "MiniMax稀疏注意力", summary
+// paragraph), prefill and split-K decode, plus the dense causal decode used as
+// the full-attention baseline.
+//
+// Prefill: one wave per (sequence, KV head, query row); the wave's 16 MFMA
+// columns are the row's G query heads (WaveAttn in attn_block.h).  Waves are
+// ordered KV-head-major, so the K/V working set of the whole GPU at any moment
+// is one head's cache.
+//
+// Decode: one wave per (sequence, KV head, split) attends a contiguous run of
+// the selection (or of all causal blocks for the dense baseline) and writes an
+// unnormalised partial (m, l, O); a merge kernel combines the splits by
+// log-sum-exp.  Splits keep enough waves in flight to stream K/V at HBM rate
+// when only B * Hkv = 128 (sequence, head) pairs exist.
+#include "attn_block.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace msa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kAttnWaves = 4;
+
+struct PrefillArgs {
+  const uint16_t* q;    // [B][Sq][Hq][128]
+  const uint16_t* k;    // [B][Hkv][Skv][128]
+  const uint16_t* v;
+  const int32_t* sel;   // [B][Hkv][Sq][k]
+  uint16_t* out;        // [B][Sq][Hq][128]
+  float* lse;           // [B][Hq][Sq] or null
+  int Sq, Skv, q_start, Hq, Hkv, G, top_k;
+  float scale_log2;
+  long long units;      // B * Hkv * Sq
+};
+
+__global__ void __launch_bounds__(256) sparse_prefill_kernel(PrefillArgs a) {
+  __shared__ u32x4 vtile[kAttnWaves][kBlock * 16];
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const long long u = (long long)blockIdx.x * kAttnWaves + wave;
+  if (u >= a.units) return;
+  const int t = (int)(u % a.Sq);
+  const int bh = (int)(u / a.Sq);
+  const int h = bh % a.Hkv, b = bh / a.Hkv;
+  const int pos = a.q_start + t;
+  const int cur = pos / kBlock;
+  const int hq0 = h * a.G;
+
+  WaveAttn st;
+  st.init();
+  st.load_q(a.q + (((size_t)b * a.Sq + t) * a.Hq + hq0) * kHeadDim, a.G);
+  const uint16_t* kh = a.k + ((size_t)b * a.Hkv + h) * a.Skv * kHeadDim;
+  const uint16_t* vh = a.v + ((size_t)b * a.Hkv + h) * a.Skv * kHeadDim;
+  // sel == null: dense causal attention over every block 0..cur
+  const int32_t* list = a.sel ? a.sel + u * a.top_k : nullptr;
+  const int nlist = list ? a.top_k : cur + 1;
+  for (int r = 0; r < nlist; ++r) {
+    const int c = list ? list[r] : r;
+    if (c < 0 || c > cur) continue;  // padding (or an invalid entry): never read
+    st.block(kh, vh, c, pos, a.scale_log2, vtile[wave]);
+  }
+  const float L = st.total_l();
+  const int n = lane % 16, g = lane / 16;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  if (n < a.G) {
+    st.store_bf16(a.out + (((size_t)b * a.Sq + t) * a.Hq + hq0 + n) * kHeadDim, inv);
+    if (a.lse && g == 0)
+      a.lse[((size_t)b * a.Hq + hq0 + n) * a.Sq + t] =
+          L > 0.f ? (st.m + __log2f(L)) * kLn2 : -__builtin_huge_valf();
+  }
+}
+
+struct DecodeArgs {
+  const uint16_t* q;     // [B][1][Hq][128]
+  const uint16_t* k;     // [B][Hkv][Skv][128]
+  const uint16_t* v;
+  const int32_t* seq_lens;
+  const int32_t* sel;    // [B][Hkv][1][k] or null (dense: every causal block)
+  float* part_o;         // [B][Hkv][nsplit][G][128]
+  float* part_ml;        // [B][Hkv][nsplit][G][2]
+  uint16_t* out;         // [B][1][Hq][128]
+  float* lse;            // [B][Hq][1] or null
+  int Skv, Hq, Hkv, G, top_k, nsplit, per_split;
+  float scale_log2;
+};
+
+__global__ void __launch_bounds__(256) decode_partial_kernel(DecodeArgs a) {
+  __shared__ u32x4 vtile[kAttnWaves][kBlock * 16];
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int split = blockIdx.x * kAttnWaves + wave;
+  const int h = blockIdx.y, b = blockIdx.z;
+  if (split >= a.nsplit) return;
+  const int pos = min(max(a.seq_lens[b], 1), a.Skv) - 1;
+  const int cur = pos / kBlock;
+  const int hq0 = h * a.G;
+  WaveAttn st;
+  st.init();
+  st.load_q(a.q + ((size_t)b * a.Hq + hq0) * kHeadDim, a.G);
+  const uint16_t* kh = a.k + ((size_t)b * a.Hkv + h) * a.Skv * kHeadDim;
+  const uint16_t* vh = a.v + ((size_t)b * a.Hkv + h) * a.Skv * kHeadDim;
+  const int rbeg = split * a.per_split;
+  const int rend = a.sel ? min(rbeg + a.per_split, a.top_k) : min(rbeg + a.per_split, cur + 1);
+  const int32_t* list = a.sel ? a.sel + ((size_t)b * a.Hkv + h) * a.top_k : nullptr;
+  for (int r = rbeg; r < rend; ++r) {
+    const int c = list ? list[r] : r;
+    if (c < 0 || c > cur) continue;
+    st.block(kh, vh, c, pos, a.scale_log2, vtile[wave]);
+  }
+  const float L = st.total_l();
+  const int n = lane % 16, g = lane / 16;
+  if (n < a.G) {
+    const size_t col = (((size_t)b * a.Hkv + h) * a.nsplit + split) * a.G + n;
+    st.store_f32(a.part_o + col * kHeadDim);
+    if (g == 0) {
+      a.part_ml[2 * col] = st.m;  // -inf when the split attended nothing
+      a.part_ml[2 * col + 1] = L;
+    }
+  }
+}
+
+// One wave per (sequence, query head): log-sum-exp merge of the splits.
+__global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int hq = blockIdx.x * kAttnWaves + wave;
+  const int b = blockIdx.y;
+  if (hq >= a.Hq) return;
+  const int h = hq / a.G, n = hq % a.G;
+  const size_t col0 = ((size_t)b * a.Hkv + h) * a.nsplit * a.G + n;
+  float M = -__builtin_huge_valf();
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[2 * (col0 + (size_t)s * a.G)]);
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  if (M > -__builtin_huge_valf()) {
+    for (int s = 0; s < a.nsplit; ++s) {
+      const size_t col = col0 + (size_t)s * a.G;
+      const float ms = a.part_ml[2 * col];
+      if (ms == -__builtin_huge_valf()) continue;
+      const float w = exp2f(ms - M);
+      L += w * a.part_ml[2 * col + 1];
+      const f32x2 ov = reinterpret_cast<const f32x2*>(a.part_o + col * kHeadDim)[lane];
+      o0 += w * ov[0];
+      o1 += w * ov[1];
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  reinterpret_cast<uint32_t*>(a.out + ((size_t)b * a.Hq + hq) * kHeadDim)[lane] =
+      pack_bf16x2(o0 * inv, o1 * inv);
+  if (a.lse && lane == 0)
+    a.lse[(size_t)b * a.Hq + hq] = L > 0.f ? (M + __log2f(L)) * kLn2 : -__builtin_huge_valf();
+}
+
+int decode_per_split(const Shape& s, bool dense) {
+  // sparse: ~4 blocks per wave keeps >= 2K waves in flight for 128 (b, h) pairs;
+  // dense: 64 blocks per wave.
+  return dense ? 64 : 4;
+}
+int decode_nsplit(const Shape& s, bool dense) {
+  const int n = dense ? s.nblk : s.top_k;
+  return ceil_div(n, decode_per_split(s, dense));
+}
+
+}  // namespace
+
+hipError_t launch_sparse_attn_prefill(const Shape& s, const void* q, const void* k, const void* v,
+                                      const int32_t* sel, void* out, float* lse, hipStream_t st) {
+  PrefillArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                static_cast<const uint16_t*>(v), sel, static_cast<uint16_t*>(out), lse,
+                s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.G, s.top_k, s.scale * kLog2e,
+                (long long)s.B * s.Hkv * s.Sq};
+  const long long grid = (a.units + kAttnWaves - 1) / kAttnWaves;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  sparse_prefill_kernel<<<(unsigned)grid, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_attn_prefill_rowwise(const Shape& s, const void* q, const void* k,
+                                             const void* v, void* out, float* lse,
+                                             hipStream_t st) {
+  return launch_sparse_attn_prefill(s, q, k, v, nullptr, out, lse, st);
+}
+
+size_t decode_workspace_bytes(const Shape& s, bool dense) {
+  const size_t cols = (size_t)s.B * s.Hkv * decode_nsplit(s, dense) * s.G;
+  return cols * (kHeadDim + 2) * sizeof(float);
+}
+
+hipError_t launch_attn_decode(const Shape& s, const void* q, const void* k, const void* v,
+                              const int32_t* seq_lens, const int32_t* sel, void* out, float* lse,
+                              void* ws, hipStream_t st) {
+  const bool dense = sel == nullptr;
+  const int nsplit = decode_nsplit(s, dense);
+  const size_t cols = (size_t)s.B * s.Hkv * nsplit * s.G;
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = part_o + cols * kHeadDim;
+  DecodeArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+               static_cast<const uint16_t*>(v), seq_lens, sel, part_o, part_ml,
+               static_cast<uint16_t*>(out), lse, s.Skv, s.Hq, s.Hkv, s.G, s.top_k, nsplit,
+               decode_per_split(s, dense), s.scale * kLog2e};
+  dim3 g1(ceil_div(nsplit, kAttnWaves), s.Hkv, s.B);
+  decode_partial_kernel<<<g1, 256, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 g2(ceil_div(s.Hq, kAttnWaves), s.B);
+  decode_merge_kernel<<<g2, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,95 @@
+// common.h — device-side building blocks shared by the gfx950 kernels of
+// libmsa: vector types, the two bf16 MFMA shapes used, order-preserving key
+// encodings for exact top-k, and small wave-level helpers.
+//
+// Wave64 MFMA operand layouts (checked on the device):
+//   v_mfma_f32_16x16x32_bf16: lane l holds A[m = l%16][k = 8*(l/16) + i] and
+//     B[k = 8*(l/16) + i][n = l%16] (i = 0..7); result reg r of lane l is
+//     C[m = 4*(l/16) + r][n = l%16].
+//   v_mfma_f32_32x32x16_bf16: lane l holds A[m = l%32][k = 8*(l/32) + i] and
+//     B[k = 8*(l/32) + i][n = l%32]; result reg r of lane l is
+//     C[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32].
+// Because a contraction sums over k, A and B may use any common permutation
+// of k; the kernels pick permutations that make every operand load a single
+// contiguous 16-byte read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kBlock = 64;       // tokens per selection block
+constexpr int kHeadDim = 128;    // main-branch head dim
+constexpr int kIdxDim = 64;      // index-branch head dim
+constexpr int kIdxHeads = 4;     // index-query heads
+constexpr int kMaxTopK = 256;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
+
+// Two fp32 -> packed bf16x2 (round to nearest even; one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Order-preserving map of an fp32 score to uint32: a < b as reals <=>
+// key(a) < key(b); -0 and +0 map to the same key.  -inf maps to 0x007fffff,
+// so the key 0 lies below every real score.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) == 0) u = 0;  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Number of set bits of `mask` held by lanes below the calling lane.
+__device__ __forceinline__ int prefix_count(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ float wave_max_xor16_32(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_xor16_32(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Lane l < 32 receives max(a[l], a[l+32]); lane l >= 32 receives
+// max(b[l-32], b[l]) (one v_permlane32_swap).
+__device__ __forceinline__ float halves_max(float a, float b) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace msa

@@ -1,0 +1,250 @@
+// index_scores.hip — index branch of MSA: block scores on gfx950.
+//
+// The index branch is a lightweight attention of 4 index-query heads against
+// one index-key head (talk summary "How MiniMax M3 Was Built: Sparse Attention
+// and Native Multimodality", section "MSA uses a lightweight index branch
+// before sparse attention"); its scores are reduced to one score per 64-token
+// block (section "Block-level retrieval makes sparse attention easier to run
+// on GPUs"), the max over the block's tokens and over the index heads
+// attributed to a KV head.  The token-level score matrix never leaves
+// registers.
+//
+// Prefill kernel: one work-group per (sequence, 64-row query tile), one wave
+// per index head.  The tile's index queries sit in registers as the B operand
+// of v_mfma_f32_32x32x16_bf16 for the whole sweep; each 64-key index-K block
+// (8 KiB) is staged once in LDS for the four waves; keys are on the M side so
+// that the per-block max is a register max plus one cross-half lane swap.  The
+// sweep only visits blocks strictly before a row's own block, so no causal mask
+// is applied per element.
+//
+// Decode kernel: one query per sequence; the index-K cache is streamed from
+// HBM once, each wave taking a run of blocks, with v_mfma_f32_16x16x32_bf16
+// (keys on M, the 4 index heads on N).
+#include "common.h"
+#include "kernels.h"
+
+namespace msa {
+namespace {
+
+constexpr int kTileRows = 64;   // query rows per prefill work-group
+constexpr int kStageCols = 32;  // blocks staged in LDS before a write-out
+constexpr int kStagePad = kStageCols + 1;
+
+struct IndexArgs {
+  const uint16_t* iq;  // [B][Sq][4][64]
+  const uint16_t* ik;  // [B][Skv][64]
+  const int32_t* seq_lens;
+  float* scores;       // [B][Hkv][Sq][nblk]
+  int Sq, Skv, q_start, nblk;
+};
+
+// Swizzled LDS position (in 16-byte chunks) of chunk `ch` (0..7) of key row
+// `key` of an index-K tile: spreads the 32-lane column reads over all banks.
+__device__ __forceinline__ int ktile_slot(int key, int ch) {
+  return key * 8 + (ch ^ ((key >> 1) & 7));
+}
+
+template <int HKV>
+__global__ void __launch_bounds__(256)
+index_scores_prefill_kernel(IndexArgs a) {
+  __shared__ u32x4 ktile[2][64 * 8];
+  __shared__ float stage[kIdxHeads][kTileRows][kStagePad];
+
+  const int tile = gridDim.x - 1 - blockIdx.x;  // late (long) tiles first
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;  // = index head
+  const int lane = tid % kWave;
+  const int t0 = tile * kTileRows;
+  const int rows = min(kTileRows, a.Sq - t0);
+  const int cur_last = (a.q_start + t0 + rows - 1) / kBlock;  // sweep blocks [0, cur_last)
+
+  // Index queries of this wave's head, B operand: N-tile nt holds rows
+  // t0+32nt.., lane l -> row (l%32); K-step ks covers dims 16ks..16ks+15 and
+  // lane half l/32 holds dims 16ks + 8(l/32) .. +7.
+  bf16x8 qf[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = 32 * nt + lane % 32;
+    const bool ok = r < rows;
+    const u32x4* src =
+        reinterpret_cast<const u32x4*>(a.iq + (((size_t)b * a.Sq + t0 + r) * kIdxHeads + wave) * kIdxDim);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 v = {0, 0, 0, 0};
+      if (ok) v = src[2 * ks + lane / 32];
+      qf[nt][ks] = as_bf16x8(v);
+    }
+  }
+
+  const u32x4* ikb = reinterpret_cast<const u32x4*>(a.ik + (size_t)b * a.Skv * kIdxDim);
+  // 512 chunks of 16 B per block; thread tid moves chunks tid and tid+256.
+  auto load_tile = [&](int c, u32x4& r0, u32x4& r1) {
+    const u32x4* src = ikb + (size_t)c * (kBlock * 8);
+    r0 = src[tid];
+    r1 = src[tid + 256];
+  };
+  auto store_tile = [&](int buf, u32x4 r0, u32x4 r1) {
+    int q0 = tid, q1 = tid + 256;
+    ktile[buf][ktile_slot(q0 / 8, q0 % 8)] = r0;
+    ktile[buf][ktile_slot(q1 / 8, q1 % 8)] = r1;
+  };
+
+  auto flush = [&](int c0, int cend) {
+    // lists (h, row): value = max over index heads i = h (mod HKV)
+    const int len = cend - c0;
+    for (int f = tid; f < HKV * kTileRows * kStageCols; f += 256) {
+      const int e = f % kStageCols;
+      const int list = f / kStageCols;
+      const int h = list / kTileRows, row = list % kTileRows;
+      if (e >= len || row >= rows) continue;
+      const int c = c0 + e;
+      const int cur = (a.q_start + t0 + row) / kBlock;
+      if (c >= cur) continue;
+      float v = stage[h][row][e];
+#pragma unroll
+      for (int i = h + HKV; i < kIdxHeads; i += HKV) v = fmaxf(v, stage[i][row][e]);
+      a.scores[(((size_t)b * HKV + h) * a.Sq + t0 + row) * a.nblk + c] = v;
+    }
+  };
+
+  if (cur_last > 0) {
+    u32x4 r0, r1;
+    load_tile(0, r0, r1);
+    store_tile(0, r0, r1);
+    __syncthreads();
+    int c0 = 0;
+    for (int c = 0; c < cur_last; ++c) {
+      const int buf = c & 1;
+      const bool more = c + 1 < cur_last;
+      if (more) load_tile(c + 1, r0, r1);
+
+      f32x16 acc[2][2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int ch = 2 * ks + lane / 32;
+        bf16x8 k0 = as_bf16x8(ktile[buf][ktile_slot(lane % 32, ch)]);
+        bf16x8 k1 = as_bf16x8(ktile[buf][ktile_slot(32 + lane % 32, ch)]);
+        acc[0][0] = mfma32(k0, qf[0][ks], acc[0][0]);
+        acc[0][1] = mfma32(k0, qf[1][ks], acc[0][1]);
+        acc[1][0] = mfma32(k1, qf[0][ks], acc[1][0]);
+        acc[1][1] = mfma32(k1, qf[1][ks], acc[1][1]);
+      }
+      float m0 = acc[0][0][0], m1 = acc[0][1][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) {
+        m0 = fmaxf(m0, acc[0][0][r]);
+        m1 = fmaxf(m1, acc[0][1][r]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        m0 = fmaxf(m0, acc[1][0][r]);
+        m1 = fmaxf(m1, acc[1][1][r]);
+      }
+      // lane l now holds the block max of query row l for head `wave`
+      stage[wave][lane][c - c0] = halves_max(m0, m1);
+
+      if (more) store_tile(buf ^ 1, r0, r1);
+      __syncthreads();
+      if (c + 1 - c0 == kStageCols || !more) {
+        flush(c0, c + 1);
+        c0 = c + 1;
+        __syncthreads();
+      }
+    }
+  }
+  // own block: +inf
+  for (int list = tid; list < HKV * rows; list += 256) {
+    const int h = list / rows, row = list % rows;
+    const int cur = (a.q_start + t0 + row) / kBlock;
+    a.scores[(((size_t)b * HKV + h) * a.Sq + t0 + row) * a.nblk + cur] = __builtin_huge_valf();
+  }
+}
+
+constexpr int kDecodeBlocksPerWave = 8;
+
+template <int HKV>
+__global__ void __launch_bounds__(256)
+index_scores_decode_kernel(IndexArgs a) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  // lengths outside [1, Skv] are clamped, so no read leaves the cache
+  const int pos = min(max(a.seq_lens[b], 1), a.Skv) - 1;
+  const int cur = pos / kBlock;
+  const int cbeg = (blockIdx.x * 4 + wave) * kDecodeBlocksPerWave;
+  const int cend = min(cbeg + kDecodeBlocksPerWave, cur);
+  float* out = a.scores + (size_t)b * HKV * a.nblk;  // Sq == 1
+  if (blockIdx.x == 0 && wave == 0 && lane < HKV) out[(size_t)lane * a.nblk + cur] = __builtin_huge_valf();
+  if (cbeg >= cend) return;
+
+  // B operand: column n = index head (n < 4), lane group g = l/16 holds dims
+  // 32ks + 8g .. +7 for K-step ks.
+  const int n = lane % 16, g = lane / 16;
+  bf16x8 qf[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    u32x4 v = {0, 0, 0, 0};
+    if (n < kIdxHeads)
+      v = reinterpret_cast<const u32x4*>(a.iq + ((size_t)b * kIdxHeads + n) * kIdxDim)[4 * ks + g];
+    qf[ks] = as_bf16x8(v);
+  }
+  const u32x4* ikb = reinterpret_cast<const u32x4*>(a.ik + (size_t)b * a.Skv * kIdxDim);
+  for (int c = cbeg; c < cend; ++c) {
+    // A operand: M-tile mt holds keys 64c + 16mt + (l%16), same dim mapping.
+    u32x4 kr[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        kr[mt][ks] = ikb[((size_t)c * kBlock + 16 * mt + n) * 8 + 4 * ks + g];
+    float m = -__builtin_huge_valf();
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma16(as_bf16x8(kr[mt][0]), qf[0], acc);
+      acc = mfma16(as_bf16x8(kr[mt][1]), qf[1], acc);
+      m = fmaxf(m, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+    }
+    m = wave_max_xor16_32(m);  // block max of column n (index head n)
+    if (HKV <= 2) m = fmaxf(m, __shfl_xor(m, 2));
+    if (HKV == 1) m = fmaxf(m, __shfl_xor(m, 1));
+    if (lane < HKV) out[(size_t)lane * a.nblk + c] = m;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_index_block_scores(const Shape& s, const void* iq, const void* ik,
+                                     const int32_t* seq_lens, float* scores, hipStream_t st) {
+  IndexArgs a{static_cast<const uint16_t*>(iq), static_cast<const uint16_t*>(ik), seq_lens, scores,
+              s.Sq, s.Skv, s.q_start, s.nblk};
+  const bool dec = seq_lens != nullptr;
+  const int per_wg = 4 * kDecodeBlocksPerWave;
+  dim3 grid = dec ? dim3(ceil_div(s.nblk, per_wg), s.B) : dim3(ceil_div(s.Sq, kTileRows), s.B);
+  switch (s.Hkv) {
+    case 1:
+      if (dec) index_scores_decode_kernel<1><<<grid, 256, 0, st>>>(a);
+      else index_scores_prefill_kernel<1><<<grid, 256, 0, st>>>(a);
+      break;
+    case 2:
+      if (dec) index_scores_decode_kernel<2><<<grid, 256, 0, st>>>(a);
+      else index_scores_prefill_kernel<2><<<grid, 256, 0, st>>>(a);
+      break;
+    case 4:
+      if (dec) index_scores_decode_kernel<4><<<grid, 256, 0, st>>>(a);
+      else index_scores_prefill_kernel<4><<<grid, 256, 0, st>>>(a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace msa

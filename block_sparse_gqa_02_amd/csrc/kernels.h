@@ -1,0 +1,50 @@
+// kernels.h — host-side launchers of the gfx950 kernels.  Called by the C ABI
+// (api.cpp) after it has validated every argument; each launcher only derives
+// grid sizes and launches on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msa {
+
+struct Shape {
+  int B, Sq, Skv, q_start;
+  int Hq, Hkv, G;     // query heads, KV heads, Hq / Hkv
+  int top_k;
+  float scale;        // main-branch softmax scale
+  int nblk;           // ceil(Skv / 64)
+};
+
+// Index branch: block scores [B][Hkv][Sq][nblk] (decode when seq_lens != NULL).
+hipError_t launch_index_block_scores(const Shape& s, const void* iq, const void* ik,
+                                     const int32_t* seq_lens, float* scores, hipStream_t st);
+
+// Per-KV-head top-k over block scores -> sel [B][Hkv][Sq][k].
+hipError_t launch_topk_blocks(const Shape& s, const float* scores, const int32_t* seq_lens,
+                              int32_t* sel, hipStream_t st);
+
+// Fused index scoring + running top-k (prefill).
+size_t fused_workspace_bytes(const Shape& s);
+hipError_t launch_index_topk_fused(const Shape& s, const void* iq, const void* ik, int32_t* sel,
+                                   void* ws, hipStream_t st);
+
+// Sparse attention.
+hipError_t launch_sparse_attn_prefill(const Shape& s, const void* q, const void* k,
+                                      const void* v, const int32_t* sel, void* out, float* lse,
+                                      hipStream_t st);
+size_t decode_workspace_bytes(const Shape& s, bool dense);
+hipError_t launch_attn_decode(const Shape& s, const void* q, const void* k, const void* v,
+                              const int32_t* seq_lens, const int32_t* sel, void* out, float* lse,
+                              void* ws, hipStream_t st);  // sel == NULL: dense
+
+// Dense causal attention (baseline): row-wise (one wave per row and KV head)
+// and tiled (K/V tiles shared by a work-group of rows).
+hipError_t launch_dense_attn_prefill_rowwise(const Shape& s, const void* q, const void* k,
+                                             const void* v, void* out, float* lse,
+                                             hipStream_t st);
+hipError_t launch_dense_attn_prefill(const Shape& s, const void* q, const void* k, const void* v,
+                                     void* out, float* lse, hipStream_t st);
+
+}  // namespace msa

@@ -1,0 +1,190 @@
+/*
+ * msa.h — C ABI of libmsa.so: the forward hot path of MiniMax Sparse Attention
+ * (MSA) on AMD Instinct MI355X (gfx950).
+ *
+ * The method, as the pages describe it:
+ *   - a lightweight index branch, 4 index-query heads against a single
+ *     index-key head, scores the causal context (talk summary "How MiniMax M3
+ *     Was Built: Sparse Attention and Native Multimodality", section "MSA uses
+ *     a lightweight index branch before sparse attention");
+ *   - every KV head picks its own top-k set, the index outputs are not merged
+ *     across heads, and the unit of selection is a block of tokens, not a token
+ *     (same page, section "Block-level retrieval makes sparse attention easier
+ *     to run on GPUs"; news write-up "MiniMax Researcher Olive Song: Sparse
+ *     Attention Cannot Be Directly Ported Across Architectures; GPU Memory
+ *     Layout Dictates Design Choices", paragraph 6, paragraphs counted from the
+ *     first one after the headline);
+ *   - the main GQA branch computes exact softmax attention over the selected
+ *     blocks only (topic page "MiniMax稀疏注意力", summary paragraph).
+ * Constants the pages leave open are fixed here: block size 64; a block's
+ * score is the max of the raw index dot products over the block's tokens and
+ * over the index heads attributed to the KV head (index head i -> KV head
+ * i mod n_kv_heads); the query's own block is always kept and counts toward k;
+ * ties go to the lower block index; query head hq reads KV head
+ * hq / (n_q_heads / n_kv_heads); inside the own block only keys j <= pos are
+ * attended.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are device pointers (hipMalloc'd or equivalent), densely packed
+ *     row-major in the layouts below, 16-byte aligned.  bf16 is IEEE
+ *     bfloat16 (raw 16-bit).  The caller owns every buffer, including any
+ *     workspace; the library never allocates, frees or synchronises.
+ *   - Every call is asynchronous on `stream` (NULL = the null stream).
+ *   - Arguments are validated on the host before anything is launched; a call
+ *     that returns an error has launched nothing, except MSA_ERR_HIP, which
+ *     reports a launch failure (detail in msa_last_error()).
+ *   - Positions: prefill row t of every sequence sits at q_start + t and
+ *     q_start + seq_q <= seq_kv.  Decode (seq_lens != NULL): seq_q == 1 and the
+ *     query of sequence b sits at seq_lens[b] - 1 (the cache already holds the
+ *     new token), 1 <= seq_lens[b] <= seq_kv (values are read on the device and
+ *     are not validated on the host).  cur(t) = pos(t) / 64 is the own block.
+ *
+ * Layouts (B batch, Sq query rows, Skv = seq_kv, Hq/Hkv query/KV heads,
+ * D = 128, Hi = 4 index heads, Di = 64, nblk = ceil(Skv / 64), k = top_k):
+ *   q        [B][Sq][Hq][D]     bf16      out  [B][Sq][Hq][D] bf16
+ *   k, v     [B][Hkv][Skv][D]   bf16      lse  [B][Hq][Sq]    fp32 (natural log)
+ *   iq       [B][Sq][Hi][Di]    bf16      ik   [B][Skv][Di]   bf16 (one index-key head)
+ *   block_scores [B][Hkv][Sq][nblk] fp32  sel  [B][Hkv][Sq][k] int32
+ * K/V are head-major so that one (head, block) is one contiguous 16 KiB read:
+ * the pages note that splitting a head dimension over several KV heads breaks
+ * contiguous reads and that block retrieval restores them (talk summary,
+ * section "DeepSeek's DSA did not directly fit MiniMax's grouped-query
+ * architecture").
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_ABI_VERSION 1
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARGUMENT = 1,   /* NULL/misaligned pointer, inconsistent sizes */
+  MSA_ERR_UNSUPPORTED = 2,        /* valid problem outside what the kernels implement */
+  MSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MSA_ERR_HIP = 4                 /* a HIP launch failed; see msa_last_error() */
+} msa_status;
+
+typedef struct {
+  int32_t batch;          /* B >= 1 */
+  int32_t seq_q;          /* Sq >= 1 query rows per sequence (1 for decode) */
+  int32_t seq_kv;         /* Skv >= 1: token capacity of k, v, ik per sequence */
+  int32_t q_start;        /* prefill: position of row 0; ignored in decode */
+  int32_t n_q_heads;      /* Hq */
+  int32_t n_kv_heads;     /* Hkv; Hq / Hkv must be 4 or 8 */
+  int32_t head_dim;       /* must be 128 */
+  int32_t n_idx_heads;    /* must be 4 (the pages' index branch), multiple of Hkv */
+  int32_t idx_head_dim;   /* must be 64 */
+  int32_t block_size;     /* must be 64 */
+  int32_t top_k;          /* 1..256 blocks per KV head per query (own block included) */
+  float softmax_scale;    /* scale of q.k in the main branch, e.g. 1/sqrt(128) */
+} msa_problem;
+
+/* Operation ids for msa_workspace_bytes. */
+typedef enum {
+  MSA_OP_INDEX_BLOCK_SCORES = 0,
+  MSA_OP_TOPK_BLOCKS = 1,
+  MSA_OP_INDEX_TOPK_FUSED = 2,
+  MSA_OP_SPARSE_ATTN_PREFILL = 3,
+  MSA_OP_SPARSE_ATTN_DECODE = 4,
+  MSA_OP_DENSE_ATTN_PREFILL = 5,
+  MSA_OP_DENSE_ATTN_DECODE = 6
+} msa_op;
+
+/* Index branch: block scores.  For every sequence b, KV head h, row t and
+ * block c: c < cur(t): max over index heads i with i mod Hkv == h and tokens
+ * j in [64c, 64c+63] of sum_d iq[b][t][i][d] * ik[b][j][d] (bf16 products,
+ * fp32 accumulation); c == cur(t): +inf; entries c > cur(t) are not written.
+ * seq_lens == NULL selects prefill positions, else decode positions.
+ * Source: talk summary, section "MSA uses a lightweight index branch before
+ * sparse attention" (4 index-query heads, 1 index-key head, highest-scoring
+ * positions are kept); block granularity: section "Block-level retrieval
+ * makes sparse attention easier to run on GPUs". */
+msa_status msa_index_block_scores(const msa_problem* p, const void* iq, const void* ik,
+                                  const int32_t* seq_lens, float* block_scores,
+                                  hipStream_t stream);
+
+/* Per-KV-head causal top-k over block scores.  For every (b, h, t): the first
+ * min(k, cur+1) blocks c in [0, cur] in order of (score descending, c
+ * ascending), with the own block cur treated as +inf whatever block_scores
+ * holds there; written ascending into sel[b][h][t][0..], the rest -1.  Scores
+ * compare as reals (-0 == +0); NaN scores give an unspecified selection.
+ * Source: news write-up, paragraph 6 (each KV head selects independently, no
+ * aggregation; fewer candidates make top-k and merging cheaper). */
+msa_status msa_topk_blocks(const msa_problem* p, const float* block_scores,
+                           const int32_t* seq_lens, int32_t* sel, hipStream_t stream);
+
+/* Index scoring and top-k in one pass: the same sel as msa_index_block_scores
+ * followed by msa_topk_blocks, but block scores stream through a running
+ * top-k and are never written to memory (needed at 1M-token contexts, where
+ * they would take gigabytes).  Prefill positions only (seq_lens must be NULL).
+ * workspace: msa_workspace_bytes(p, MSA_OP_INDEX_TOPK_FUSED) bytes, any
+ * content; it holds per-split candidate lists.
+ * Source: as msa_index_block_scores and msa_topk_blocks; the 1M-token window
+ * is named in the talk summary, section "MiniMax M3 combines agentic coding,
+ * long context, and native multimodality". */
+msa_status msa_index_topk_fused(const msa_problem* p, const void* iq, const void* ik,
+                                const int32_t* seq_lens, int32_t* sel, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* Main branch, prefill: exact GQA softmax attention of every row over the
+ * tokens of the blocks its KV head selected.  For query head hq (KV head
+ * h = hq / (Hq/Hkv)): T = { j : j/64 in sel[b][h][t][:], j <= pos(t) },
+ * out = softmax(softmax_scale * q.k_j over T) . v_j, lse = log sum exp.
+ * sel entries must be -1 or in [0, cur(t)] (others give unspecified results,
+ * never out-of-range reads); a row whose list is all -1 gets out = 0,
+ * lse = -inf.  lse may be NULL.  bf16 operands, fp32 accumulation and softmax.
+ * Source: topic page "MiniMax稀疏注意力", summary paragraph (exact attention
+ * only over the selected blocks). */
+msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const void* k,
+                                   const void* v, const int32_t* sel, void* out, float* lse,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Main branch, decode: as msa_sparse_attn_prefill for the single query of
+ * each sequence at seq_lens[b] - 1, with the selected blocks split over
+ * several work-groups whose partial softmax states are merged by
+ * log-sum-exp.  workspace: msa_workspace_bytes(p, MSA_OP_SPARSE_ATTN_DECODE).
+ * Source: as msa_sparse_attn_prefill; decode speed-ups over full attention are
+ * reported in the news write-up, paragraph 7. */
+msa_status msa_sparse_attn_decode(const msa_problem* p, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* seq_lens,
+                                  const int32_t* sel, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/* Dense causal GQA attention over every key j <= pos(t) (the full-attention
+ * baseline every speed-up on the pages is quoted against).  top_k is ignored. */
+msa_status msa_dense_attn_prefill(const msa_problem* p, const void* q, const void* k,
+                                  const void* v, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/* Dense decode: every key j < seq_lens[b], split over work-groups and merged by
+ * log-sum-exp.  workspace: msa_workspace_bytes(p, MSA_OP_DENSE_ATTN_DECODE). */
+msa_status msa_dense_attn_decode(const msa_problem* p, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* seq_lens, void* out,
+                                 float* lse, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* Workspace bytes an operation needs for problem p (0 if none).  Host only. */
+msa_status msa_workspace_bytes(const msa_problem* p, msa_op op, size_t* bytes);
+
+/* Static description of a status code. */
+const char* msa_status_string(msa_status s);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* msa_last_error(void);
+
+/* MSA_ABI_VERSION of the loaded library. */
+int msa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

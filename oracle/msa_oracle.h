@@ -14,15 +14,16 @@
  *       attention easier to run on GPUs".
  *   [B] "MiniMax Researcher Olive Song: Sparse Attention Cannot Be Directly
  *       Ported Across Architectures; GPU Memory Layout Dictates Design Choices"
- *       (disconfirmai.com news write-up), paragraphs 3 and 5.
+ *       (disconfirmai.com news write-up), paragraphs 3, 5 and 6 (counted from
+ *       the first paragraph after the headline).
  *   [C] "MiniMax稀疏注意力" (disconfirmai.com topic page), summary paragraph:
  *       exact attention is computed only over the selected key/value blocks.
  *   [D] talks.tomv.uk analysis of the same talk, key_points 2 and 4.
  *
  * What the pages fix: an index branch of 4 index-query heads against one
  * index-key head scores the causal context [A §index branch, D kp2]; each KV
- * head selects its own top-k set, with no merging across heads [B ¶5, D kp4];
- * selection is over blocks of tokens, not single tokens [A §block-level, B ¶5];
+ * head selects its own top-k set, with no merging across heads [B ¶6, D kp4];
+ * selection is over blocks of tokens, not single tokens [A §block-level, B ¶6];
  * the main GQA branch then computes exact softmax attention over the selected
  * blocks only [C summary].
  *

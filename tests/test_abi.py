@@ -1,0 +1,128 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_gqa_02_amd as msa
+from block_sparse_gqa_02_amd import binding
+from block_sparse_gqa_02_amd.configs import ALL, CHUNK_1M, DECODE_32x256K, PREFILL_128K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+A = ctypes.c_void_p(0x10000)       # dummy, 16-byte aligned, never dereferenced
+A4 = ctypes.c_void_p(0x10004)      # 4-byte aligned only
+NULL = None
+
+
+def declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:msa_status|const char\s*\*|int)\s+(msa_\w+)\s*\(",
+                                 src, re.M)))
+
+
+def test_header_declares_entry_points():
+    names = declared()
+    for n in ["msa_index_block_scores", "msa_topk_blocks", "msa_index_topk_fused",
+              "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_dense_attn_prefill",
+              "msa_dense_attn_decode", "msa_workspace_bytes", "msa_status_string",
+              "msa_last_error", "msa_abi_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(binding.LIB_PATH)
+    for n in declared():
+        assert hasattr(L, n), f"libmsa.so does not export {n}"
+
+
+def test_abi_version_and_status_strings():
+    L = binding.lib()
+    assert L.msa_abi_version() == 1
+    for code, name in binding.STATUS.items():
+        assert L.msa_status_string(code).decode() == name
+
+
+def prob(w=PREFILL_128K, **kw):
+    return msa.Problem.from_workload(w, **kw).c()
+
+
+def call(name, *args):
+    L = binding.lib()
+    return getattr(L, name)(*args), L.msa_last_error().decode()
+
+
+def P(p):
+    return ctypes.byref(p)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 64, 2), ("idx_head_dim", 128, 2), ("block_size", 128, 2),
+    ("n_idx_heads", 8, 2), ("n_kv_heads", 8, 2), ("n_q_heads", 30, 1),
+    ("top_k", 0, 1), ("top_k", 257, 2), ("batch", 0, 1), ("seq_kv", 100, 1),
+    ("q_start", -1, 1), ("n_q_heads", 4 * 17, 2),
+])
+def test_topk_validation(field, value, code):
+    p = prob(**{field: value})
+    st, msg = call("msa_topk_blocks", P(p), A, NULL, A, NULL)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_null_and_misaligned_pointers():
+    p = prob()
+    assert call("msa_index_block_scores", P(p), NULL, A, NULL, A, NULL)[0] == 1
+    assert call("msa_index_block_scores", P(p), A4, A, NULL, A, NULL)[0] == 1  # bf16: 16 B
+    assert call("msa_sparse_attn_prefill", P(p), A, A, A, NULL, A, NULL, NULL, 0, NULL)[0] == 1
+    assert call("msa_sparse_attn_prefill", P(p), A, A, A, A4, A4, NULL, NULL, 0, NULL)[0] == 1
+    assert call("msa_dense_attn_prefill", P(p), A, NULL, A, A, NULL, NULL, 0, NULL)[0] == 1
+    assert call("msa_index_block_scores", None, A, A, NULL, A, NULL)[0] == 1
+
+
+def test_decode_shape_rules():
+    p = prob(DECODE_32x256K)
+    # decode needs seq_q == 1
+    bad = prob(DECODE_32x256K, seq_q=2)
+    assert call("msa_sparse_attn_decode", P(bad), A, A, A, A4, A4, A, NULL, A, 1 << 30, NULL)[0] == 1
+    # workspace too small
+    need = ctypes.c_size_t()
+    assert call("msa_workspace_bytes", P(p), 4, ctypes.byref(need))[0] == 0 and need.value > 0
+    st, msg = call("msa_sparse_attn_decode", P(p), A, A, A, A4, A4, A, NULL, A, need.value - 1, NULL)
+    assert st == 3 and "workspace" in msg
+    st, _ = call("msa_dense_attn_decode", P(p), A, A, A, NULL, A, NULL, A, 1 << 40, NULL)
+    assert st == 1  # seq_lens required
+
+
+def test_fused_rules():
+    p = prob(CHUNK_1M)
+    assert call("msa_index_topk_fused", P(p), A, A, A4, A4, A, 1 << 40, NULL)[0] == 2  # decode
+    need = ctypes.c_size_t()
+    assert call("msa_workspace_bytes", P(p), 2, ctypes.byref(need))[0] == 0
+    if need.value:
+        st, msg = call("msa_index_topk_fused", P(p), A, A, NULL, A4, A, need.value - 1, NULL)
+        assert st == 3, msg
+
+
+def test_workspace_bytes_every_op_and_workload():
+    for w in ALL:
+        p = prob(w)
+        for op in range(7):
+            is_decode_op = op in (4, 6)
+            out = ctypes.c_size_t(12345)
+            st, msg = call("msa_workspace_bytes", P(p), op, ctypes.byref(out))
+            if is_decode_op and not w.decode:
+                continue  # decode ops need seq_q == 1
+            if op == 2 and w.decode:
+                continue
+            assert st == 0, (w.name, op, msg)
+    assert call("msa_workspace_bytes", P(prob()), 99, ctypes.byref(ctypes.c_size_t()))[0] == 1
+    assert call("msa_workspace_bytes", P(prob()), 0, None)[0] == 1
+
+
+def test_binding_raises_with_detail():
+    p = msa.Problem.from_workload(PREFILL_128K, head_dim=64)
+    with pytest.raises(msa.MsaError, match="UNSUPPORTED"):
+        msa.msa_workspace_bytes(p, "sparse_attn_prefill")

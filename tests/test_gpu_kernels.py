@@ -1,0 +1,215 @@
+"""Per-kernel parity of the HIP path against the CPU oracle at small sizes that
+still span several tiles and ragged tails (every row checked)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_gqa_02_amd as msa
+from block_sparse_gqa_02_amd.configs import TINY_PREFILL_2K, DECODE_32x256K, PREFILL_32K
+from block_sparse_gqa_02_amd.inputs import bf16_bits, generate
+import oracle.oracle as O
+import parity as PAR
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def oprob(w):
+    return O.Problem(w.batch, w.seq_q, w.seq_kv, w.q_start, w.n_q_heads, w.n_kv_heads,
+                     w.head_dim, w.n_idx_heads, w.idx_head_dim, w.block_size, w.top_k, w.decode,
+                     w.softmax_scale)
+
+
+def host(inp):
+    return dict(q=bf16_bits(inp.q), k=bf16_bits(inp.k), v=bf16_bits(inp.v),
+                iq=bf16_bits(inp.iq), ik=bf16_bits(inp.ik),
+                seq_lens=None if inp.seq_lens is None else inp.seq_lens.cpu().numpy())
+
+
+def positions(w, seq_lens):
+    if w.decode:
+        return np.array(seq_lens) - 1
+    return w.q_start + np.arange(w.seq_q)
+
+
+def oracle_all(w, h, rows=None):
+    p = oprob(w)
+    if rows is None:
+        rows = np.arange(w.batch * w.seq_q)
+    return O.forward_rows_parallel(p, h["q"], h["k"], h["v"], h["iq"], h["ik"], h["seq_lens"],
+                                   rows, PAR.host_threads(), want_scores=True)
+
+
+PREFILL_SMALL = [
+    # name, overrides (seq_q, seq_kv, q_start, heads, k)
+    ("g4_hkv2_ragged", dict(seq_q=1000, seq_kv=1000, q_start=0, n_q_heads=8, n_kv_heads=2, top_k=5)),
+    ("g8_hkv4_offset", dict(seq_q=333, seq_kv=1500, q_start=1100, n_q_heads=32, n_kv_heads=4, top_k=7)),
+    ("g4_hkv1", dict(seq_q=700, seq_kv=700, q_start=0, n_q_heads=4, n_kv_heads=1, top_k=3)),
+    ("batch2_k_all", dict(batch=2, seq_q=300, seq_kv=300, q_start=0, n_q_heads=8, n_kv_heads=2, top_k=64)),
+]
+
+
+@pytest.mark.parametrize("integer", [True, False], ids=["integer", "normal"])
+@pytest.mark.parametrize("name,ov", PREFILL_SMALL, ids=[x[0] for x in PREFILL_SMALL])
+def test_prefill_pipeline_small(name, ov, integer):
+    need_gpu()
+    w = TINY_PREFILL_2K.shrink(**ov)
+    inp = generate(w, DEV, seed=1234, integer=integer)
+    p = msa.Problem.from_workload(w)
+    bs = msa.msa_index_block_scores(p, inp.iq, inp.ik)
+    sel = msa.msa_topk_blocks(p, bs)
+    lse = torch.empty((w.batch, w.n_q_heads, w.seq_q), dtype=torch.float32, device=DEV)
+    out = msa.msa_sparse_attn_prefill(p, inp.q, inp.k, inp.v, sel, lse=lse)
+    torch.cuda.synchronize()
+    h = host(inp)
+    o_sel, o_out, o_lse, o_sc = oracle_all(w, h)
+    bs_h, sel_h = bs.cpu().numpy(), sel.cpu().numpy()
+    out_h = out.float().cpu().numpy()
+    lse_h = lse.cpu().numpy()
+    pos = positions(w, None)
+    ties = 0
+    for b in range(w.batch):
+        for t in range(w.seq_q):
+            r = b * w.seq_q + t
+            cur = int(pos[t]) // 64
+            for hh in range(w.n_kv_heads):
+                ref = o_sc[r, hh, : cur + 1]
+                got = bs_h[b, hh, t, : cur + 1]
+                assert got[cur] == np.inf
+                if integer:
+                    assert np.array_equal(got[:cur], ref[:cur]), (b, t, hh)
+                else:
+                    err = np.abs(got[:cur].astype(np.float64) - ref[:cur])
+                    assert np.all(err <= 1e-5 * np.maximum(1.0, np.abs(ref[:cur]))), (b, t, hh)
+                ties += PAR.check_selection_row(sel_h[b, hh, t], ref, cur, w.top_k, integer,
+                                                f"row {t} head {hh}")
+    # attention on the GPU's own selection
+    p_o = oprob(w)
+    ref_out = np.empty_like(out_h, dtype=np.float64)
+    ref_lse = np.empty_like(lse_h, dtype=np.float64)
+    for b in range(w.batch):
+        for t in range(w.seq_q):
+            o, l = O.attend_row(p_o, h["q"], h["k"], h["v"], None, sel_h[b, :, t], b, t)
+            ref_out[b, t] = o
+            ref_lse[b, :, t] = l
+    PAR.assert_attention_close(out_h, ref_out, name)
+    assert np.allclose(lse_h, ref_lse, atol=1e-3, rtol=1e-4)
+    print(f"{name}: tie-band mismatches {ties}")
+
+
+@pytest.mark.parametrize("k,nblk,seed", [(1, 40, 0), (5, 130, 1), (64, 700, 2), (200, 513, 3),
+                                         (256, 256, 4), (8, 32, 5)])
+def test_topk_exact_against_oracle_on_same_scores(k, nblk, seed):
+    """Top-k alone on synthetic scores full of exact ties (integers, -0/+0):
+    the decision is taken on identical fp32 values, so it must be bit-exact."""
+    need_gpu()
+    g = torch.Generator().manual_seed(seed)
+    Sq, Hkv = 2 * 64 * 3 + 17, 2
+    seq_kv = nblk * 64
+    q_start = seq_kv - Sq
+    sc = torch.randint(-3, 4, (1, Hkv, Sq, nblk), generator=g).float()
+    sc[sc == 0] = torch.where(torch.rand(sc[sc == 0].shape, generator=g) < 0.5,
+                              torch.tensor(-0.0), torch.tensor(0.0))
+    sc[0, 1] = torch.randn((Sq, nblk), generator=g)  # one head without ties
+    w = TINY_PREFILL_2K.shrink(seq_q=Sq, seq_kv=seq_kv, q_start=q_start, n_kv_heads=Hkv,
+                               n_q_heads=8, top_k=k)
+    p = msa.Problem.from_workload(w)
+    sel = msa.msa_topk_blocks(p, sc.to(DEV)).cpu().numpy()
+    po = oprob(w)
+    for hh in range(Hkv):
+        for t in range(Sq):
+            cur = (q_start + t) // 64
+            row = sc[0, hh, t].numpy().copy()
+            row[cur] = np.inf  # the oracle's scores carry the own block at +inf
+            ref = O.select_row(po, row, cur)
+            assert np.array_equal(sel[0, hh, t], ref), (hh, t, sel[0, hh, t], ref)
+
+
+def test_index_scores_decode_and_topk_ragged():
+    need_gpu()
+    w = DECODE_32x256K.shrink(batch=5, seq_kv=5000, top_k=9)
+    lens = [5000, 1, 4097, 64, 65]
+    inp = generate(w, DEV, seed=77, seq_lens=lens)
+    p = msa.Problem.from_workload(w)
+    bs = msa.msa_index_block_scores(p, inp.iq, inp.ik, inp.seq_lens)
+    sel = msa.msa_topk_blocks(p, bs, inp.seq_lens)
+    torch.cuda.synchronize()
+    h = host(inp)
+    o_sel, _, _, o_sc = oracle_all(w, h)
+    bs_h, sel_h = bs.cpu().numpy(), sel.cpu().numpy()
+    for b, L in enumerate(lens):
+        cur = (L - 1) // 64
+        for hh in range(w.n_kv_heads):
+            got = bs_h[b, hh, 0, : cur + 1]
+            ref = o_sc[b, hh, : cur + 1]
+            assert got[cur] == np.inf
+            assert np.all(np.abs(got[:cur] - ref[:cur]) <= 1e-5 * np.maximum(1, np.abs(ref[:cur])))
+            PAR.check_selection_row(sel_h[b, hh, 0], ref, cur, w.top_k, False, f"seq {b}")
+
+
+@pytest.mark.parametrize("dense", [False, True], ids=["sparse", "dense"])
+def test_decode_attention_ragged(dense):
+    need_gpu()
+    w = DECODE_32x256K.shrink(batch=4, seq_kv=3000, top_k=11)
+    lens = [3000, 65, 1, 2048]
+    inp = generate(w, DEV, seed=5, seq_lens=lens)
+    p = msa.Problem.from_workload(w)
+    lse = torch.empty((w.batch, w.n_q_heads, 1), dtype=torch.float32, device=DEV)
+    if dense:
+        out = msa.msa_dense_attn_decode(p, inp.q, inp.k, inp.v, inp.seq_lens, lse=lse)
+    else:
+        bs = msa.msa_index_block_scores(p, inp.iq, inp.ik, inp.seq_lens)
+        sel = msa.msa_topk_blocks(p, bs, inp.seq_lens)
+        out = msa.msa_sparse_attn_decode(p, inp.q, inp.k, inp.v, inp.seq_lens, sel, lse=lse)
+        sel_h = sel.cpu().numpy()
+    torch.cuda.synchronize()
+    h = host(inp)
+    po = oprob(w)
+    out_h, lse_h = out.float().cpu().numpy(), lse.cpu().numpy()
+    for b in range(w.batch):
+        if dense:
+            o, l = O.dense_row(po, h["q"], h["k"], h["v"], h["seq_lens"], b, 0)
+        else:
+            o, l = O.attend_row(po, h["q"], h["k"], h["v"], h["seq_lens"], sel_h[b, :, 0], b, 0)
+        PAR.assert_attention_close(out_h[b, 0], o, f"seq {b}")
+        assert np.allclose(lse_h[b, :, 0], l, atol=1e-3, rtol=1e-4)
+
+
+def test_dense_prefill_small():
+    need_gpu()
+    w = PREFILL_32K.shrink(seq_q=300, seq_kv=400, q_start=100, top_k=1, block_offset_std=0.0)
+    inp = generate(w, DEV, seed=9)
+    p = msa.Problem.from_workload(w)
+    lse = torch.empty((1, w.n_q_heads, w.seq_q), dtype=torch.float32, device=DEV)
+    out = msa.msa_dense_attn_prefill(p, inp.q, inp.k, inp.v, lse=lse)
+    torch.cuda.synchronize()
+    h = host(inp)
+    po = oprob(w)
+    out_h, lse_h = out.float().cpu().numpy(), lse.cpu().numpy()
+    ref = np.empty_like(out_h, dtype=np.float64)
+    for t in range(w.seq_q):
+        o, l = O.dense_row(po, h["q"], h["k"], h["v"], None, 0, t)
+        ref[0, t] = o
+        assert np.allclose(lse_h[0, :, t], l, atol=1e-3, rtol=1e-4)
+    PAR.assert_attention_close(out_h, ref, "dense prefill")
+
+
+def test_sparse_equals_dense_when_every_block_is_kept():
+    """k >= nblk: the sparse kernels attend every causal block, so they must
+    reproduce the dense kernel (both in the library)."""
+    need_gpu()
+    w = PREFILL_32K.shrink(seq_q=520, seq_kv=520, q_start=0, top_k=9, block_offset_std=0.0)
+    inp = generate(w, DEV, seed=3)
+    p = msa.Problem.from_workload(w)
+    sel = msa.msa_topk_blocks(p, msa.msa_index_block_scores(p, inp.iq, inp.ik))
+    a = msa.msa_sparse_attn_prefill(p, inp.q, inp.k, inp.v, sel).float()
+    d = msa.msa_dense_attn_prefill(p, inp.q, inp.k, inp.v).float()
+    assert torch.max(torch.abs(a - d)).item() <= 1e-2
