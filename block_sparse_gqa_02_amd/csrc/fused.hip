@@ -1,15 +1,242 @@
-// fused.hip — index scoring with a streaming per-(row, KV head) top-k.
+// fused.hip — index scoring with a streaming per-(row, KV head) top-k: block
+// scores never leave the chip.
+//
+// At a 1M-token context (the window named in the talk summary "How MiniMax M3
+// Was Built", section "MiniMax M3 combines agentic coding, long context, and
+// native multimodality") a chunk of 8192 rows has 4 x 8192 x 16384 block
+// scores, 2 GiB in fp32; here they stream through a running top-k instead.
+// Each KV head keeps its own list (news write-up "MiniMax Researcher Olive
+// Song: Sparse Attention Cannot Be Directly Ported…", paragraph 6).
+//
+// Pass 1 (fused_sweep_kernel): one work-group per (64-row tile, key split).
+// The index sweep (index_sweep.h) stages 32 blocks of maxima at a time; each
+// (row, KV head) list then appends the candidates above its threshold to a
+// per-split candidate list in the workspace and compacts it to the best k-1
+// when it fills (select.h).  Splits of the key range fill the GPU when there
+// are few tiles; split s of every tile runs on the same XCD (work-group ids are
+// dealt round-robin over the 8 XCDs), so that XCD's L2 serves one key range.
+// Pass 2 (fused_merge_kernel): one wave per list merges the splits' lists
+// (each ascending, ranges ascending) with the same compaction, appends the
+// own block and writes the ascending selection.
 #include "common.h"
+#include "index_sweep.h"
 #include "kernels.h"
+#include "select.h"
 
 namespace msa {
+namespace {
 
-size_t fused_workspace_bytes(const Shape& s) { (void)s; return 0; }
+struct FusedArgs {
+  const uint16_t* iq;
+  const uint16_t* ik;
+  int32_t* sel;       // [B][Hkv][Sq][k]
+  uint32_t* wkeys;    // [S][B*Hkv*Sq][cap]
+  int32_t* widx;      // [S][B*Hkv*Sq][cap]
+  int32_t* wcnt;      // [S][B*Hkv*Sq]
+  int B, Sq, Skv, q_start, Hkv, nsplit, ntiles, k, cap;
+};
+
+// Candidate-list capacity: keep k-1 (the own block is added at the end) plus
+// room for at least two 32-wide staging chunks between compactions.
+__host__ __device__ inline int fused_cap(int k) { return 64 * ((k - 1 + 128 + 63) / 64); }
+
+template <int HKV, int MAXE>
+__global__ void __launch_bounds__(256) fused_sweep_kernel(FusedArgs a) {
+  __shared__ IndexLds lds;
+  __shared__ uint32_t lthr[HKV * kTileRows];
+  __shared__ int32_t lcnt[HKV * kTileRows];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int s = blockIdx.x % a.nsplit;
+  const int tile = a.ntiles - 1 - blockIdx.x / a.nsplit;  // late (long) tiles first
+  const int b = blockIdx.y;
+  const int t0 = tile * kTileRows;
+  const int rows = min(kTileRows, a.Sq - t0);
+  const int cur_last = (a.q_start + t0 + rows - 1) / kBlock;
+  const int cbeg = (int)((long long)s * cur_last / a.nsplit);
+  const int cend = (int)((long long)(s + 1) * cur_last / a.nsplit);
+  const int m = a.k - 1;  // candidates kept per list (own block excluded)
+  const long long nlist = (long long)a.B * HKV * a.Sq;
+  for (int L = tid; L < HKV * kTileRows; L += 256) {
+    lthr[L] = 0;
+    lcnt[L] = 0;
+  }
+  __syncthreads();
+  auto base_of = [&](int L) -> long long {  // list L = h * 64 + row of this tile
+    const int h = L / kTileRows, row = L % kTileRows;
+    return ((long long)s * nlist + ((long long)b * HKV + h) * a.Sq + t0 + row) * a.cap;
+  };
+
+  if (m > 0) {
+    index_sweep(IndexTile{a.iq, a.ik, b, t0, rows, a.Sq, a.Skv}, cbeg, cend, lds,
+                [&](int c0, int len) {
+      // lists 2p (lanes 0..31) and 2p+1 (lanes 32..63), one 32-block chunk each
+      for (int p = wave; p < HKV * kTileRows / 2; p += 4) {
+        const int half = lane / 32, e = lane % 32;
+        const int L = 2 * p + half;
+        const int h = L / kTileRows, row = L % kTileRows;
+        const int c = c0 + e;
+        const bool ok = row < rows && e < len && c < (a.q_start + t0 + row) / kBlock;
+        uint32_t key = 0;
+        if (ok) {
+          float v = lds.stage[h][row][e];
+#pragma unroll
+          for (int i = h + HKV; i < kIdxHeads; i += HKV) v = fmaxf(v, lds.stage[i][row][e]);
+          key = score_key(v);
+        }
+        int cnt = lcnt[L];
+        const bool pass = ok && key > lthr[L];
+        const uint64_t mask = ballot(pass);
+        const uint32_t hm = half ? (uint32_t)(mask >> 32) : (uint32_t)mask;
+        if (pass) {
+          const int d = cnt + __popc(hm & ((1u << e) - 1u));
+          const long long base = base_of(L);
+          a.wkeys[base + d] = key;
+          a.widx[base + d] = c;
+        }
+        cnt += __popc(hm);
+        if (e == 0) lcnt[L] = cnt;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int LL = 2 * p + hh;
+          const int n = __shfl(cnt, 32 * hh);
+          if (n > a.cap - 32) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            const long long base = base_of(LL);
+            const uint32_t thr = wave_compact_topm<MAXE>(a.wkeys + base, a.widx + base, n, m);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            if (lane == 0) {
+              lthr[LL] = thr;
+              lcnt[LL] = m;
+            }
+            __builtin_amdgcn_wave_barrier();
+          }
+        }
+      }
+    });
+  }
+  __syncthreads();
+  // final compaction of this split's lists to at most m entries
+  for (int p = wave; p < HKV * kTileRows / 2; p += 4) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int L = 2 * p + hh;
+      if (L % kTileRows >= rows) continue;
+      int n = lcnt[L];
+      if (n > m) {
+        const long long base = base_of(L);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        wave_compact_topm<MAXE>(a.wkeys + base, a.widx + base, n, m);
+        n = m;
+      }
+      if (lane == 0) {
+        const int h = L / kTileRows, row = L % kTileRows;
+        a.wcnt[(long long)s * nlist + ((long long)b * HKV + h) * a.Sq + t0 + row] = n;
+      }
+    }
+  }
+}
+
+template <int MAXE>
+__global__ void __launch_bounds__(256) fused_merge_kernel(FusedArgs a) {
+  constexpr int CAP = MAXE * kWave;
+  __shared__ uint32_t skeys[4][CAP];
+  __shared__ int32_t sidx[4][CAP];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  uint32_t* keys = skeys[wave];
+  int32_t* idxs = sidx[wave];
+  const long long nlist = (long long)a.B * a.Hkv * a.Sq;
+  const int m = a.k - 1;
+  for (long long L = (long long)blockIdx.x * 4 + wave; L < nlist; L += (long long)gridDim.x * 4) {
+    const int t = (int)(L % a.Sq);
+    const int cur = (a.q_start + t) / kBlock;
+    int cnt = 0;
+    uint32_t thr = 0;
+    if (m > 0) {
+      for (int s = 0; s < a.nsplit; ++s) {
+        const int n = a.wcnt[(long long)s * nlist + L];
+        const long long base = ((long long)s * nlist + L) * a.cap;
+        for (int off = 0; off < n; off += kWave) {
+          const int i = off + lane;
+          const bool ok = i < n;
+          const uint32_t key = ok ? a.wkeys[base + i] : 0u;
+          const int32_t idx = ok ? a.widx[base + i] : 0;
+          cnt = wave_append(keys, idxs, cnt, ok && key > thr, key, idx);
+          if (cnt > CAP - kWave) {
+            thr = wave_compact_topm<MAXE>(keys, idxs, cnt, m);
+            cnt = m;
+          }
+        }
+      }
+      if (cnt > m) {
+        wave_compact_topm<MAXE>(keys, idxs, cnt, m);
+        cnt = m;
+      }
+    }
+    int32_t* dst = a.sel + L * a.k;
+    for (int i = lane; i < a.k; i += kWave) dst[i] = i < cnt ? idxs[i] : (i == cnt ? cur : -1);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+int fused_nsplit(const Shape& s) {
+  const int ntiles = ceil_div(s.Sq, kTileRows);
+  const int cur_max = (s.q_start + s.Sq - 1) / kBlock;
+  int n = ceil_div(1024, s.B * ntiles);
+  n = std::min(n, 16);
+  n = std::min(n, std::max(1, cur_max / 64));
+  return std::max(n, 1);
+}
+
+template <int HKV>
+hipError_t launch_hkv(const Shape& s, const FusedArgs& a, hipStream_t st) {
+  dim3 g1(a.ntiles * a.nsplit, s.B);
+  const long long nlist = (long long)s.B * s.Hkv * s.Sq;
+  const int g2 = (int)std::min<long long>((nlist + 3) / 4, 16384);
+  const int cap = a.cap;
+  if (cap <= 192) {
+    fused_sweep_kernel<HKV, 3><<<g1, 256, 0, st>>>(a);
+    fused_merge_kernel<3><<<g2, 256, 0, st>>>(a);
+  } else if (cap <= 256) {
+    fused_sweep_kernel<HKV, 4><<<g1, 256, 0, st>>>(a);
+    fused_merge_kernel<4><<<g2, 256, 0, st>>>(a);
+  } else if (cap <= 320) {
+    fused_sweep_kernel<HKV, 5><<<g1, 256, 0, st>>>(a);
+    fused_merge_kernel<5><<<g2, 256, 0, st>>>(a);
+  } else {
+    fused_sweep_kernel<HKV, 6><<<g1, 256, 0, st>>>(a);
+    fused_merge_kernel<6><<<g2, 256, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t fused_workspace_bytes(const Shape& s) {
+  const size_t nlist = (size_t)s.B * s.Hkv * s.Sq;
+  const size_t ns = (size_t)fused_nsplit(s);
+  return ns * nlist * ((size_t)fused_cap(s.top_k) * 8 + 4) + 256;
+}
 
 hipError_t launch_index_topk_fused(const Shape& s, const void* iq, const void* ik, int32_t* sel,
                                    void* ws, hipStream_t st) {
-  (void)s; (void)iq; (void)ik; (void)sel; (void)ws; (void)st;
-  return hipErrorNotSupported;
+  const int nsplit = fused_nsplit(s);
+  const size_t nlist = (size_t)s.B * s.Hkv * s.Sq;
+  const int cap = fused_cap(s.top_k);
+  uint32_t* wkeys = static_cast<uint32_t*>(ws);
+  int32_t* widx = reinterpret_cast<int32_t*>(wkeys + (size_t)nsplit * nlist * cap);
+  int32_t* wcnt = widx + (size_t)nsplit * nlist * cap;
+  FusedArgs a{static_cast<const uint16_t*>(iq), static_cast<const uint16_t*>(ik), sel, wkeys, widx,
+              wcnt, s.B, s.Sq, s.Skv, s.q_start, s.Hkv, nsplit, ceil_div(s.Sq, kTileRows),
+              s.top_k, cap};
+  switch (s.Hkv) {
+    case 1: return launch_hkv<1>(s, a, st);
+    case 2: return launch_hkv<2>(s, a, st);
+    case 4: return launch_hkv<4>(s, a, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace msa

@@ -21,14 +21,11 @@
 // HBM once, each wave taking a run of blocks, with v_mfma_f32_16x16x32_bf16
 // (keys on M, the 4 index heads on N).
 #include "common.h"
+#include "index_sweep.h"
 #include "kernels.h"
 
 namespace msa {
 namespace {
-
-constexpr int kTileRows = 64;   // query rows per prefill work-group
-constexpr int kStageCols = 32;  // blocks staged in LDS before a write-out
-constexpr int kStagePad = kStageCols + 1;
 
 struct IndexArgs {
   const uint16_t* iq;  // [B][Sq][4][64]
@@ -38,127 +35,33 @@ struct IndexArgs {
   int Sq, Skv, q_start, nblk;
 };
 
-// Swizzled LDS position (in 16-byte chunks) of chunk `ch` (0..7) of key row
-// `key` of an index-K tile: spreads the 32-lane column reads over all banks.
-__device__ __forceinline__ int ktile_slot(int key, int ch) {
-  return key * 8 + (ch ^ ((key >> 1) & 7));
-}
-
 template <int HKV>
 __global__ void __launch_bounds__(256)
 index_scores_prefill_kernel(IndexArgs a) {
-  __shared__ u32x4 ktile[2][64 * 8];
-  __shared__ float stage[kIdxHeads][kTileRows][kStagePad];
-
+  __shared__ IndexLds lds;
   const int tile = gridDim.x - 1 - blockIdx.x;  // late (long) tiles first
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;  // = index head
-  const int lane = tid % kWave;
   const int t0 = tile * kTileRows;
   const int rows = min(kTileRows, a.Sq - t0);
   const int cur_last = (a.q_start + t0 + rows - 1) / kBlock;  // sweep blocks [0, cur_last)
+  const IndexTile T{a.iq, a.ik, b, t0, rows, a.Sq, a.Skv};
 
-  // Index queries of this wave's head, B operand: N-tile nt holds rows
-  // t0+32nt.., lane l -> row (l%32); K-step ks covers dims 16ks..16ks+15 and
-  // lane half l/32 holds dims 16ks + 8(l/32) .. +7.
-  bf16x8 qf[2][4];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = 32 * nt + lane % 32;
-    const bool ok = r < rows;
-    const u32x4* src =
-        reinterpret_cast<const u32x4*>(a.iq + (((size_t)b * a.Sq + t0 + r) * kIdxHeads + wave) * kIdxDim);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 v = {0, 0, 0, 0};
-      if (ok) v = src[2 * ks + lane / 32];
-      qf[nt][ks] = as_bf16x8(v);
-    }
-  }
-
-  const u32x4* ikb = reinterpret_cast<const u32x4*>(a.ik + (size_t)b * a.Skv * kIdxDim);
-  // 512 chunks of 16 B per block; thread tid moves chunks tid and tid+256.
-  auto load_tile = [&](int c, u32x4& r0, u32x4& r1) {
-    const u32x4* src = ikb + (size_t)c * (kBlock * 8);
-    r0 = src[tid];
-    r1 = src[tid + 256];
-  };
-  auto store_tile = [&](int buf, u32x4 r0, u32x4 r1) {
-    int q0 = tid, q1 = tid + 256;
-    ktile[buf][ktile_slot(q0 / 8, q0 % 8)] = r0;
-    ktile[buf][ktile_slot(q1 / 8, q1 % 8)] = r1;
-  };
-
-  auto flush = [&](int c0, int cend) {
-    // lists (h, row): value = max over index heads i = h (mod HKV)
-    const int len = cend - c0;
+  index_sweep(T, 0, cur_last, lds, [&](int c0, int len) {
+    // list (h, row): max over index heads i = h (mod HKV); written row-contiguous
     for (int f = tid; f < HKV * kTileRows * kStageCols; f += 256) {
       const int e = f % kStageCols;
       const int list = f / kStageCols;
       const int h = list / kTileRows, row = list % kTileRows;
       if (e >= len || row >= rows) continue;
       const int c = c0 + e;
-      const int cur = (a.q_start + t0 + row) / kBlock;
-      if (c >= cur) continue;
-      float v = stage[h][row][e];
+      if (c >= (a.q_start + t0 + row) / kBlock) continue;  // own or later block
+      float v = lds.stage[h][row][e];
 #pragma unroll
-      for (int i = h + HKV; i < kIdxHeads; i += HKV) v = fmaxf(v, stage[i][row][e]);
+      for (int i = h + HKV; i < kIdxHeads; i += HKV) v = fmaxf(v, lds.stage[i][row][e]);
       a.scores[(((size_t)b * HKV + h) * a.Sq + t0 + row) * a.nblk + c] = v;
     }
-  };
-
-  if (cur_last > 0) {
-    u32x4 r0, r1;
-    load_tile(0, r0, r1);
-    store_tile(0, r0, r1);
-    __syncthreads();
-    int c0 = 0;
-    for (int c = 0; c < cur_last; ++c) {
-      const int buf = c & 1;
-      const bool more = c + 1 < cur_last;
-      if (more) load_tile(c + 1, r0, r1);
-
-      f32x16 acc[2][2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int ch = 2 * ks + lane / 32;
-        bf16x8 k0 = as_bf16x8(ktile[buf][ktile_slot(lane % 32, ch)]);
-        bf16x8 k1 = as_bf16x8(ktile[buf][ktile_slot(32 + lane % 32, ch)]);
-        acc[0][0] = mfma32(k0, qf[0][ks], acc[0][0]);
-        acc[0][1] = mfma32(k0, qf[1][ks], acc[0][1]);
-        acc[1][0] = mfma32(k1, qf[0][ks], acc[1][0]);
-        acc[1][1] = mfma32(k1, qf[1][ks], acc[1][1]);
-      }
-      float m0 = acc[0][0][0], m1 = acc[0][1][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) {
-        m0 = fmaxf(m0, acc[0][0][r]);
-        m1 = fmaxf(m1, acc[0][1][r]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        m0 = fmaxf(m0, acc[1][0][r]);
-        m1 = fmaxf(m1, acc[1][1][r]);
-      }
-      // lane l now holds the block max of query row l for head `wave`
-      stage[wave][lane][c - c0] = halves_max(m0, m1);
-
-      if (more) store_tile(buf ^ 1, r0, r1);
-      __syncthreads();
-      if (c + 1 - c0 == kStageCols || !more) {
-        flush(c0, c + 1);
-        c0 = c + 1;
-        __syncthreads();
-      }
-    }
-  }
+  });
   // own block: +inf
   for (int list = tid; list < HKV * rows; list += 256) {
     const int h = list / rows, row = list % rows;

@@ -1,0 +1,123 @@
+// index_sweep.h — the index branch's inner loop, shared by the block-score
+// kernel and the fused block-score + top-k kernel.
+//
+// A work-group of four waves owns 64 consecutive query rows of one sequence;
+// wave w is index head w.  The rows' index queries stay in registers as the B
+// operand of v_mfma_f32_32x32x16_bf16; each 64-key index-K block (8 KiB) is
+// staged once in LDS (double-buffered, swizzled) for the four waves; keys are
+// on the M side, so a block's max per query is a max over the lane's result
+// registers plus one v_permlane32_swap.  Block maxima are staged in LDS,
+// kStageCols blocks at a time, and handed to a consumer.
+#pragma once
+
+#include "common.h"
+
+namespace msa {
+
+constexpr int kTileRows = 64;   // query rows per work-group
+constexpr int kStageCols = 32;  // blocks staged before the consumer runs
+constexpr int kStagePad = kStageCols + 1;
+
+struct IndexLds {
+  u32x4 ktile[2][64 * 8];                          // 2 x 8 KiB index-K tiles
+  float stage[kIdxHeads][kTileRows][kStagePad];    // block maxima per (head, row, block)
+};
+
+// Swizzled 16-byte slot of chunk `ch` (0..7) of key row `key`: the 32-lane
+// column reads of a K-step then spread over all LDS banks.
+__device__ __forceinline__ int ktile_slot(int key, int ch) { return key * 8 + (ch ^ ((key >> 1) & 7)); }
+
+struct IndexTile {
+  const uint16_t* iq;  // [B][Sq][4][64]
+  const uint16_t* ik;  // [B][Skv][64]
+  int b, t0, rows, Sq, Skv;
+};
+
+// Sweeps blocks [cbeg, cend) for the tile.  After every kStageCols blocks (and
+// at the end) all threads call flush(c0, len) with stage[i][row][e] holding
+// the max over block c0+e's keys of head i's scores for row t0+row.  Must be
+// called by all 256 threads; contains barriers.
+template <typename Flush>
+__device__ __forceinline__ void index_sweep(const IndexTile& T, int cbeg, int cend, IndexLds& L,
+                                            Flush&& flush) {
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;  // index head
+  const int lane = tid % kWave;
+  if (cbeg >= cend) return;
+
+  // B operand: N-tile nt holds rows 32nt + l%32; K-step ks covers dims
+  // 16ks..16ks+15, lane half l/32 holds dims 16ks + 8(l/32) .. +7.
+  bf16x8 qf[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = 32 * nt + lane % 32;
+    const bool ok = r < T.rows;
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        T.iq + (((size_t)T.b * T.Sq + T.t0 + (ok ? r : 0)) * kIdxHeads + wave) * kIdxDim);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 v = {0, 0, 0, 0};
+      if (ok) v = src[2 * ks + lane / 32];
+      qf[nt][ks] = as_bf16x8(v);
+    }
+  }
+
+  const u32x4* ikb = reinterpret_cast<const u32x4*>(T.ik + (size_t)T.b * T.Skv * kIdxDim);
+  u32x4 r0, r1;
+  auto load_tile = [&](int c) {
+    const u32x4* src = ikb + (size_t)c * (kBlock * 8);
+    r0 = src[tid];
+    r1 = src[tid + 256];
+  };
+  auto store_tile = [&](int buf) {
+    const int q0 = tid, q1 = tid + 256;
+    L.ktile[buf][ktile_slot(q0 / 8, q0 % 8)] = r0;
+    L.ktile[buf][ktile_slot(q1 / 8, q1 % 8)] = r1;
+  };
+
+  load_tile(cbeg);
+  store_tile(0);
+  __syncthreads();
+  int c0 = cbeg;
+  for (int c = cbeg; c < cend; ++c) {
+    const int buf = (c - cbeg) & 1;
+    const bool more = c + 1 < cend;
+    if (more) load_tile(c + 1);
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ch = 2 * ks + lane / 32;
+      const bf16x8 k0 = as_bf16x8(L.ktile[buf][ktile_slot(lane % 32, ch)]);
+      const bf16x8 k1 = as_bf16x8(L.ktile[buf][ktile_slot(32 + lane % 32, ch)]);
+      acc[0][0] = mfma32(k0, qf[0][ks], acc[0][0]);
+      acc[0][1] = mfma32(k0, qf[1][ks], acc[0][1]);
+      acc[1][0] = mfma32(k1, qf[0][ks], acc[1][0]);
+      acc[1][1] = mfma32(k1, qf[1][ks], acc[1][1]);
+    }
+    float m0 = fmaxf(acc[0][0][0], acc[1][0][0]), m1 = fmaxf(acc[0][1][0], acc[1][1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      m0 = fmaxf(m0, fmaxf(acc[0][0][r], acc[1][0][r]));
+      m1 = fmaxf(m1, fmaxf(acc[0][1][r], acc[1][1][r]));
+    }
+    // lane l now holds the block max of row l for head `wave`
+    L.stage[wave][lane][c - c0] = halves_max(m0, m1);
+
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+    if (c + 1 - c0 == kStageCols || !more) {
+      flush(c0, c + 1 - c0);
+      c0 = c + 1;
+      __syncthreads();
+    }
+  }
+}
+
+}  // namespace msa

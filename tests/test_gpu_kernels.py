@@ -213,3 +213,40 @@ def test_sparse_equals_dense_when_every_block_is_kept():
     a = msa.msa_sparse_attn_prefill(p, inp.q, inp.k, inp.v, sel).float()
     d = msa.msa_dense_attn_prefill(p, inp.q, inp.k, inp.v).float()
     assert torch.max(torch.abs(a - d)).item() <= 1e-2
+
+
+FUSED_CASES = [
+    # seq_q, seq_kv, q_start, Hq, Hkv, k
+    ("multi_split_k128", dict(seq_q=256, seq_kv=16384, q_start=16128, n_q_heads=32, n_kv_heads=4, top_k=128)),
+    ("multi_split_unaligned", dict(seq_q=300, seq_kv=12000, q_start=11650, n_q_heads=8, n_kv_heads=2, top_k=37)),
+    ("k1", dict(seq_q=200, seq_kv=9000, q_start=8700, n_q_heads=4, n_kv_heads=1, top_k=1)),
+    ("k256", dict(seq_q=130, seq_kv=20000, q_start=19800, n_q_heads=8, n_kv_heads=2, top_k=256)),
+    ("short_rows", dict(seq_q=700, seq_kv=700, q_start=0, n_q_heads=8, n_kv_heads=2, top_k=6)),
+]
+
+
+@pytest.mark.parametrize("integer", [True, False], ids=["integer", "normal"])
+@pytest.mark.parametrize("name,ov", FUSED_CASES, ids=[x[0] for x in FUSED_CASES])
+def test_fused_equals_separate_and_oracle(name, ov, integer):
+    """The fused kernel computes the same fp32 block maxima as the block-score
+    kernel, so its selection must equal block scores + top-k exactly; both are
+    also held to the oracle protocol on every row."""
+    need_gpu()
+    w = TINY_PREFILL_2K.shrink(**ov)
+    inp = generate(w, DEV, seed=4321, integer=integer)
+    p = msa.Problem.from_workload(w)
+    sel_f = msa.msa_index_topk_fused(p, inp.iq, inp.ik)
+    bs = msa.msa_index_block_scores(p, inp.iq, inp.ik)
+    sel_s = msa.msa_topk_blocks(p, bs)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_f, sel_s), "fused selection differs from block scores + top-k"
+    h = host(inp)
+    rows = np.arange(w.seq_q)
+    _, _, _, o_sc = O.forward_rows_parallel(oprob(w), h["q"], h["k"], h["v"], h["iq"], h["ik"],
+                                            None, rows, PAR.host_threads(), want_scores=True)
+    sel_h = sel_f.cpu().numpy()
+    for t in rows:
+        cur = (w.q_start + t) // 64
+        for hh in range(w.n_kv_heads):
+            PAR.check_selection_row(sel_h[0, hh, t], o_sc[t, hh], cur, w.top_k, integer,
+                                    f"{name} row {t} head {hh}")
