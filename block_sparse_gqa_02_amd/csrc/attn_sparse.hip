@@ -171,6 +171,7 @@ hipError_t launch_sparse_attn_prefill(const Shape& s, const void* q, const void*
                 static_cast<const uint16_t*>(v), sel, static_cast<uint16_t*>(out), lse,
                 s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.G, s.top_k, s.scale * kLog2e,
                 (long long)s.B * s.Hkv * s.Sq};
+  if (sel && union_prefill_supported(s)) return launch_union_prefill(s, q, k, v, sel, out, lse, st);
   const long long grid = (a.units + kAttnWaves - 1) / kAttnWaves;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   sparse_prefill_kernel<<<(unsigned)grid, 256, 0, st>>>(a);

@@ -34,6 +34,10 @@ hipError_t launch_index_topk_fused(const Shape& s, const void* iq, const void* i
 hipError_t launch_sparse_attn_prefill(const Shape& s, const void* q, const void* k,
                                       const void* v, const int32_t* sel, void* out, float* lse,
                                       hipStream_t st);
+// Tile-union schedule of the sparse prefill (used for G = 4 and 8).
+bool union_prefill_supported(const Shape& s);
+hipError_t launch_union_prefill(const Shape& s, const void* q, const void* k, const void* v,
+                                const int32_t* sel, void* out, float* lse, hipStream_t st);
 size_t decode_workspace_bytes(const Shape& s, bool dense);
 hipError_t launch_attn_decode(const Shape& s, const void* q, const void* k, const void* v,
                               const int32_t* seq_lens, const int32_t* sel, void* out, float* lse,

@@ -54,6 +54,9 @@ PREFILL_SMALL = [
     ("g8_hkv4_offset", dict(seq_q=333, seq_kv=1500, q_start=1100, n_q_heads=32, n_kv_heads=4, top_k=7)),
     ("g4_hkv1", dict(seq_q=700, seq_kv=700, q_start=0, n_q_heads=4, n_kv_heads=1, top_k=3)),
     ("batch2_k_all", dict(batch=2, seq_q=300, seq_kv=300, q_start=0, n_q_heads=8, n_kv_heads=2, top_k=64)),
+    ("g16_rowwise", dict(seq_q=400, seq_kv=900, q_start=500, n_q_heads=32, n_kv_heads=2, top_k=6)),
+    ("g2_rowwise", dict(seq_q=300, seq_kv=300, q_start=0, n_q_heads=8, n_kv_heads=4, top_k=3)),
+    ("g8_many_tiles", dict(seq_q=1500, seq_kv=4000, q_start=2500, n_q_heads=16, n_kv_heads=2, top_k=20)),
 ]
 
 
