@@ -7,7 +7,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/msa.h"
+#include "msa.h"
 #include "kernels.h"
 
 namespace {
