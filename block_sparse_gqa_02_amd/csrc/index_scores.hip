@@ -99,14 +99,16 @@ index_scores_decode_kernel(IndexArgs a) {
     qf[ks] = as_bf16x8(v);
   }
   const u32x4* ikb = reinterpret_cast<const u32x4*>(a.ik + (size_t)b * a.Skv * kIdxDim);
-  for (int c = cbeg; c < cend; ++c) {
-    // A operand: M-tile mt holds keys 64c + 16mt + (l%16), same dim mapping.
-    u32x4 kr[4][2];
+  // two blocks per step: 16 independent 16-byte loads in flight per lane
+  auto load = [&](int c, u32x4 (&kr)[4][2]) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
         kr[mt][ks] = ikb[((size_t)c * kBlock + 16 * mt + n) * 8 + 4 * ks + g];
+  };
+  auto score = [&](int c, const u32x4 (&kr)[4][2]) {
+    // A operand: M-tile mt holds keys 64c + 16mt + (l%16), same dim mapping.
     float m = -__builtin_huge_valf();
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -119,6 +121,14 @@ index_scores_decode_kernel(IndexArgs a) {
     if (HKV <= 2) m = fmaxf(m, __shfl_xor(m, 2));
     if (HKV == 1) m = fmaxf(m, __shfl_xor(m, 1));
     if (lane < HKV) out[(size_t)lane * a.nblk + c] = m;
+  };
+  for (int c = cbeg; c < cend; c += 2) {
+    u32x4 k0[4][2], k1[4][2];
+    load(c, k0);
+    const bool two = c + 1 < cend;
+    if (two) load(c + 1, k1);
+    score(c, k0);
+    if (two) score(c + 1, k1);
   }
 }
 

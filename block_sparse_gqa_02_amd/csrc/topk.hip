@@ -61,15 +61,94 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
   }
 }
 
+// Few long rows (decode): one work-group of eight waves per row.  Wave w
+// keeps the running list of candidate segment w; wave 0 then streams the eight
+// lists, which are ascending and cover ascending ranges, through the same
+// compaction.
+template <int MAXE>
+__global__ void __launch_bounds__(512) topk_wide_kernel(TopkArgs a) {
+  constexpr int CAP = MAXE * kWave;
+  __shared__ uint32_t skeys[8][CAP];
+  __shared__ int32_t sidx[8][CAP];
+  __shared__ int32_t scnt[8];
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  for (long long row = blockIdx.x; row < a.nrows; row += gridDim.x) {
+    const int t = (int)(row % a.Sq);
+    const int b = (int)(row / ((long long)a.Sq * a.Hkv));
+    const int pos = a.seq_lens ? min(max(a.seq_lens[b], 1), a.Skv) - 1 : a.q_start + t;
+    const int cur = pos / kBlock;
+    const int m = min(a.k, cur + 1);
+    const float* src = a.scores + row * a.nblk;
+    // segment of wave w: whole 64-candidate chunks, ascending
+    const int nchunk = cur / kWave + 1;
+    const int c_beg = (int)((long long)nchunk * wave / 8) * kWave;
+    const int c_end = min((int)((long long)nchunk * (wave + 1) / 8) * kWave, cur + 1);
+    uint32_t* keys = skeys[wave];
+    int32_t* idxs = sidx[wave];
+    int cnt = 0;
+    uint32_t thr = 0;
+    for (int c0 = c_beg; c0 < c_end; c0 += kWave) {
+      const int c = c0 + lane;
+      const bool ok = c < c_end;
+      uint32_t key = 0;
+      if (ok) key = (c == cur) ? 0xffffffffu : score_key(src[c]);
+      cnt = wave_append(keys, idxs, cnt, ok && key > thr, key, c);
+      if (cnt > CAP - kWave) {
+        thr = wave_compact_topm<MAXE>(keys, idxs, cnt, m);
+        cnt = m;
+      }
+    }
+    if (cnt > m) {
+      wave_compact_topm<MAXE>(keys, idxs, cnt, m);
+      cnt = m;
+    }
+    if (lane == 0) scnt[wave] = cnt;
+    __syncthreads();
+    if (wave == 0) {
+      // merge: stream the other waves' lists after wave 0's own
+      cnt = scnt[0];
+      thr = 0;
+      for (int w = 1; w < 8; ++w) {
+        const int nw = scnt[w];
+        for (int off = 0; off < nw; off += kWave) {
+          const int i = off + lane;
+          const bool ok = i < nw;
+          const uint32_t key = ok ? skeys[w][i] : 0u;
+          const int32_t idx = ok ? sidx[w][i] : 0;
+          cnt = wave_append(keys, idxs, cnt, ok && key > thr, key, idx);
+          if (cnt > CAP - kWave) {
+            thr = wave_compact_topm<MAXE>(keys, idxs, cnt, m);
+            cnt = m;
+          }
+        }
+      }
+      if (cnt > m) wave_compact_topm<MAXE>(keys, idxs, cnt, m);
+      int32_t* dst = a.sel + row * a.k;
+      for (int i = lane; i < a.k; i += kWave) dst[i] = i < m ? idxs[i] : -1;
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk_blocks(const Shape& s, const float* scores, const int32_t* seq_lens,
                               int32_t* sel, hipStream_t st) {
   TopkArgs a{scores, seq_lens, sel, s.Sq, s.Skv, s.q_start, s.Hkv, s.nblk, s.top_k,
              (long long)s.B * s.Hkv * s.Sq};
+  // list capacity >= k + 128 so that a full chunk always fits after a compaction
+  if (a.nrows < 2048 && s.nblk >= 1024) {
+    // few long rows: a work-group per row
+    const int grid = (int)a.nrows;
+    if (s.top_k <= 64) topk_wide_kernel<3><<<grid, 512, 0, st>>>(a);
+    else if (s.top_k <= 128) topk_wide_kernel<4><<<grid, 512, 0, st>>>(a);
+    else if (s.top_k <= 192) topk_wide_kernel<5><<<grid, 512, 0, st>>>(a);
+    else topk_wide_kernel<6><<<grid, 512, 0, st>>>(a);
+    return hipGetLastError();
+  }
   const long long wgs_needed = (a.nrows + kWavesPerWG - 1) / kWavesPerWG;
   const int grid = (int)std::min<long long>(wgs_needed, 16384);
-  // list capacity >= k + 128 so that a full chunk always fits after a compaction
   if (s.top_k <= 64) topk_kernel<3><<<grid, 256, 0, st>>>(a);
   else if (s.top_k <= 128) topk_kernel<4><<<grid, 256, 0, st>>>(a);
   else if (s.top_k <= 192) topk_kernel<5><<<grid, 256, 0, st>>>(a);
