@@ -2,13 +2,13 @@
 //
 // The main branch attends only to the blocks each KV head selected (topic page
 // "MiniMax稀疏注意力", summary paragraph).  With independent selections per
-// row, a tile of rows of one KV head touches nearly every causal block, but any
-// one block is wanted by only a few of its rows.  Loading each block once per
-// tile and reusing it across the rows that picked it cuts K/V traffic several
-// times against one gather per (row, block); the pages make the same point
-// about contiguous reads and the compute-to-memory ratio (talk summary "How
-// MiniMax M3 Was Built", section "Block-level retrieval makes sparse attention
-// easier to run on GPUs").
+// row, a tile of rows of one KV head touches most causal blocks, but any one
+// block is wanted by only a few of its rows.  Loading each block once per tile
+// and reusing it across the rows that picked it cuts K/V traffic several times
+// against one gather per (row, block); the pages make the same point about
+// contiguous reads and the compute-to-memory ratio (talk summary "How MiniMax
+// M3 Was Built", section "Block-level retrieval makes sparse attention easier
+// to run on GPUs").
 //
 // Work-group: eight waves on one (sequence, KV head, tile of 24 row groups); a
 // row group is 16/G rows x G query heads, the 16 columns of
@@ -17,17 +17,23 @@
 // blocks the tile builds, in LDS, the row and row-group bitmasks of every block
 // from the rows' selections and walks the union of the blocks in ascending
 // order; each block's K and V (32 KiB) are fetched once into a ring of LDS
-// slots by direct global->LDS loads.
+// slots by buffer loads that write LDS directly.
 //
-// The waves do not meet at a barrier per block: any one block is wanted by a
-// few rows only, so per-block work is very uneven across waves, and a barrier
-// would make every block cost its busiest wave.  Instead each slot carries a
-// ready tag (which union entry it holds) and a done count: a wave spins on the
-// tag of the block it needs, runs its own active groups, and counts itself
-// done; the last wave done with a slot refills it with the block kRing entries
-// ahead and publishes the new tag two blocks before anyone can need it.  Every
-// wait is bounded: past the bound the kernel stops waiting and raises a flag
-// in the output (a caller-visible failure, never a hang).
+// Only the waves that own a row group wanting a block take part in it: they
+// wait for the block's slot to carry its ready tag, run their groups, and count
+// themselves done.  The last of them refills the slot with the block kRing
+// entries ahead and publishes its tag once the loads have landed (at the latest
+// before it waits on anything itself, so no wave ever waits while holding an
+// unpublished refill).  Waves that want none of a block skip it without
+// touching the ring.  Every wait is bounded: past the bound the kernel stops
+// waiting and stores NaN outputs (a caller-visible failure, never a hang).
+//
+// LDS layouts (256-byte rows, 16-byte chunks).  K: chunk c of row r sits at
+// chunk c ^ (r & 15), so the 16 rows of an S-tile read at one chunk hit 16
+// distinct chunks.  V: chunk c of row r sits at chunk c ^ ((r & 7) << 1); the V
+// operand of O^T += V^T P^T is read with ds_read_b64_tr_b16, which hands each
+// lane of a 16-lane group one dim of four consecutive keys, and the swizzle
+// spreads the 16 rows of one such read evenly over the banks.
 #include "common.h"
 #include "kernels.h"
 
@@ -43,6 +49,8 @@ constexpr int kGPW = 3;            // row groups owned per wave
 constexpr int kNG = kWaves * kGPW; // row groups per tile
 constexpr int kRing = 4;           // K/V slots in the LDS ring
 constexpr int kSpinLimit = 1 << 22;
+constexpr int kBlockBytes = kBlock * kHeadDim * 2;  // one K or V block
+constexpr int kRsrcFlags = 0x00020000;              // raw buffer descriptor word 3
 
 struct UnionArgs {
   const uint16_t* q;    // [B][Sq][Hq][128]
@@ -56,22 +64,21 @@ struct UnionArgs {
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
-// 16-byte chunk swizzles of a 256-byte K or V row.  K: the 16 rows 16mt+n read
-// at one chunk hit 16 distinct chunks.  V: the keys a lane group reads share
-// bit 2, which picks the half of the row, so the four groups of an 8-byte
-// column read hit disjoint bank halves.
 __device__ __forceinline__ int kswz(int row) { return row & 15; }
-__device__ __forceinline__ int vswz(int row) { return ((row >> 2) & 1) << 3; }
+__device__ __forceinline__ int vswz(int row) { return (row & 7) << 1; }
 
 __device__ __forceinline__ void cbarrier() { asm volatile("" ::: "memory"); }
 
-// Ring-tag accesses as plain LDS instructions.  The compiler would otherwise
-// put a wait for every outstanding global->LDS load in front of them; the
-// kernel orders them against those loads with its own vmcnt waits.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
+
+// Ring-tag accesses as plain LDS instructions.  The compiler would otherwise
+// put a wait for every outstanding LDS-bound buffer load in front of them; the
+// kernel orders them against those loads with its own vmcnt waits.
 __device__ __forceinline__ int lds_load_tag(const int32_t* p) {
   int v;
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
@@ -96,6 +103,14 @@ __device__ __forceinline__ void wait_vm(int n) {
   cbarrier();
 }
 
+// One 16-byte LDS-bound buffer load per lane: LDS bytes dst + 16 * lane
+// receive bytes voff + soff of the descriptor's range (reads past the range
+// return zero).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, const void* dst, int voff,
+                                           int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)dst, 16, voff, soff, 0, 0);
+}
+
 template <int G>
 __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionArgs a) {
   constexpr int RPG = 16 / G;               // rows per group
@@ -105,7 +120,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
   __shared__ u32x4 vtile[kRing][1024];
   __shared__ uint32_t rmask[kWin][NWR];     // per block: tile rows that picked it
   __shared__ uint32_t gmask[kWin];          // per block: row groups that picked it
-  __shared__ int32_t ulist[kWin];
+  __shared__ int32_t ulist[kWin];           // union entries: block | (waves wanting it) << 24
   __shared__ int32_t wcount[kWaves];
   __shared__ int32_t ready[kRing];          // union entry held by each slot
   __shared__ int32_t done[kRing];           // waves finished with the slot's entry
@@ -113,21 +128,21 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n = lane % 16, g = lane / 16;
-  // work-groups: (b, h) major, tiles late-first; within every full run of 256
-  // tiles, XCD x (ids are dealt round-robin to the 8 XCDs) takes 32 adjacent
-  // tiles, which share most of their K/V blocks through that XCD's L2
-  const int i = (int)(blockIdx.x % a.ntiles);
-  const int order = (i / 256 < a.ntiles / 256) ? (i / 256) * 256 + (i % 8) * 32 + (i / 8) % 32 : i;
-  const int tile = a.ntiles - 1 - order;
+  // work-groups: (b, h) major, tiles late-first (longest sweeps start first)
+  const int tile = a.ntiles - 1 - (int)(blockIdx.x % a.ntiles);
   const int bh = (int)(blockIdx.x / a.ntiles);
   const int h = bh % a.Hkv, b = bh / a.Hkv;
   const int t0 = tile * TR;
   const int rows = min(TR, a.Sq - t0);
-  const int pos_last = a.q_start + t0 + rows - 1;
+  const int pos0 = a.q_start + t0;
+  const int pos_last = pos0 + rows - 1;
   const int cur_last = pos_last / kBlock;
-  const uint16_t* kh = a.k + ((size_t)b * a.Hkv + h) * a.Skv * kHeadDim;
-  const uint16_t* vh = a.v + ((size_t)b * a.Hkv + h) * a.Skv * kHeadDim;
-  const int32_t* selh = a.sel + (((size_t)b * a.Hkv + h) * a.Sq + t0) * a.top_k;
+  const size_t head = (size_t)b * a.Hkv + h;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.k + head * a.Skv * kHeadDim), (short)0, a.Skv * kHeadDim * 2, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.v + head * a.Skv * kHeadDim), (short)0, a.Skv * kHeadDim * 2, kRsrcFlags);
+  const int32_t* selh = a.sel + (head * a.Sq + t0) * a.top_k;
   const int rr = n / G, hh = n % G;  // this lane's column: row in group, head
 
   // owned groups gi = wave + 8j
@@ -153,43 +168,66 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
   }
   if (tid == 0) failed = 0;
 
-  // direct global->LDS copy of instructions [j0, j1) (64 lanes x 16 B each) of
-  // block c into slot sl; instruction j covers rows 4j..4j+3
-  auto fetch = [&](int c, int sl, int j0, int j1) {
+  // Ring fill.  Instruction j of a block (64 lanes x 16 B) covers rows 4j..4j+3:
+  // lane -> row 4j + lane/16, LDS chunk lane%16, which holds the row's chunk
+  // (lane%16) ^ swz(row).  Blocks wholly at or before every tile row's position
+  // take precomputed per-lane offsets (the swizzles depend on j mod 4 / mod 2);
+  // the diagonal block re-reads its last used row in place of later ones.
+  int koff[4], voff[2];
+#pragma unroll
+  for (int jm = 0; jm < 4; ++jm) {
+    const int row = 4 * jm + lane / 16;
+    koff[jm] = (lane / 16) * 256 + 16 * ((lane % 16) ^ kswz(row));
+    if (jm < 2) voff[jm] = (lane / 16) * 256 + 16 * ((lane % 16) ^ vswz(row));
+  }
+  auto fetch_full = [&](int c, int sl) {
+    const int sb = c * kBlockBytes;
+    if (c * kBlock + kBlock - 1 <= pos_last) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        load_lds16(rk, &ktile[sl][j * kWave], koff[j & 3], sb + j * 1024);
+        load_lds16(rv, &vtile[sl][j * kWave], voff[j & 1], sb + j * 1024);
+      }
+    } else {
+      const int last = pos_last - c * kBlock;
+      for (int j = 0; j < 16; ++j) {
+        const int row = 4 * j + lane / 16, srow = min(row, last);
+        load_lds16(rk, &ktile[sl][j * kWave], srow * 256 + 16 * ((lane % 16) ^ kswz(row)), sb);
+        load_lds16(rv, &vtile[sl][j * kWave], srow * 256 + 16 * ((lane % 16) ^ vswz(row)), sb);
+      }
+    }
+  };
+  auto fetch_part = [&](int c, int sl, int j0, int j1) {
+    const int sb = c * kBlockBytes;
     const int last = min(pos_last - c * kBlock, kBlock - 1);
-    const uint16_t* kb = kh + (size_t)c * kBlock * kHeadDim;
-    const uint16_t* vb = vh + (size_t)c * kBlock * kHeadDim;
     for (int j = j0; j < j1; ++j) {
-      const int row = 4 * j + lane / 16, ph = lane % 16;
-      const int srow = min(row, last);  // rows past every tile row's position are never used
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(kb + srow * kHeadDim + 8 * (ph ^ kswz(row))),
-          (lds_ptr)(&ktile[sl][j * kWave]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(vb + srow * kHeadDim + 8 * (ph ^ vswz(row))),
-          (lds_ptr)(&vtile[sl][j * kWave]), 16, 0, 0);
+      const int row = 4 * j + lane / 16, srow = min(row, last);
+      load_lds16(rk, &ktile[sl][j * kWave], srow * 256 + 16 * ((lane % 16) ^ kswz(row)), sb);
+      load_lds16(rv, &vtile[sl][j * kWave], srow * 256 + 16 * ((lane % 16) ^ vswz(row)), sb);
     }
   };
 
-  // per-lane LDS byte offsets (plus immediates inside the loops)
+  // K operand: lane reads row 16mt + n, dims 32ks + 8g .. +7
   int kbyte[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) kbyte[ks] = n * 256 + (((4 * ks + g) ^ n) << 4);
-  // V: 8-byte read at key 32kv + 16(i/4) + 4g + i%4, dims 64hf + 4n .. +3
-  const int vbyte0 = 4 * g * 256 + (((n / 2) ^ ((g & 1) << 3)) << 4) + 8 * (n & 1);
-  const int vbyte1 = 4 * g * 256 + (((8 + n / 2) ^ ((g & 1) << 3)) << 4) + 8 * (n & 1);
+  // V operand (transposed read): lane (g, n) of the read for M-tile mt, K-step
+  // kv and half hf loads dims 16mt + 4(n%4) .. +3 of key 32kv + 16hf + 4g + n/4,
+  // and the read returns to lane (g, n) dim 16mt + n of keys 32kv + 16hf + 4g +
+  // 0..3.  With that key's swizzle the byte offset in the tile is
+  //   (32kv + 16hf) * 256 + (vlane ^ 32mt).
+  const int r7 = (4 * g + n / 4) & 7;
+  const int vlane = (4 * g + n / 4) * 256 + 32 * r7 + 16 * ((n >> 1) & 1) + 8 * (n & 1);
 
-  auto compute = [&](int sl, int c, int wb) {
+  auto compute = [&](int sl, int c, uint32_t gm, const uint32_t* rm) {
     const char* kt = reinterpret_cast<const char*>(&ktile[sl][0]);
-    const char* vt0 = reinterpret_cast<const char*>(&vtile[sl][0]) + vbyte0;
-    const char* vt1 = reinterpret_cast<const char*>(&vtile[sl][0]) + vbyte1;
-    const uint32_t gm = gmask[c - wb];
+    const uint32_t vt = lds_addr(&vtile[sl][0]);
     const int key0 = c * kBlock + 4 * g;
 #pragma unroll
     for (int j = 0; j < kGPW; ++j) {
       const int gi = wave + kWaves * j;
       if (!((gm >> gi) & 1u)) continue;
-      // S^T = K Q^T
+      // S^T = K Q^T: sc[mt][r] is the score of key 16mt + 4g + r for this column
       f32x4 sc[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -201,29 +239,33 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
         }
       }
       const int row = gi * RPG + rr;
-      const bool active = (rmask[c - wb][row / 32] >> (row % 32)) & 1u;
-      const int pc = a.q_start + t0 + row;
-      float bmax = -__builtin_huge_valf();
+      const bool act = (rm[row / 32] >> (row % 32)) & 1u;
+      if (c * kBlock + kBlock - 1 > pos0 + gi * RPG) {
+        // the block reaches past the group's first row: mask keys after each row
+        const int pc = pos0 + row;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float z = sc[mt][r] * a.scale_log2;
-          if (!active || key0 + 16 * mt + r > pc) z = -__builtin_huge_valf();
-          sc[mt][r] = z;
-          bmax = fmaxf(bmax, z);
-        }
-      bmax = wave_max_xor16_32(bmax);
+          for (int r = 0; r < 4; ++r)
+            if (key0 + 16 * mt + r > pc) sc[mt][r] = -__builtin_huge_valf();
+      }
+      float bm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+      bm = fmaxf(bm, fmaxf(fmaxf(fmaxf(sc[2][0], sc[2][1]), fmaxf(sc[2][2], sc[2][3])),
+                           fmaxf(fmaxf(sc[3][0], sc[3][1]), fmaxf(sc[3][2], sc[3][3]))));
+      bm = act ? bm : -__builtin_huge_valf();
+      bm = wave_max_xor16_32(bm) * a.scale_log2;
       // lazy rescale: move the reference max only when a block exceeds it by > 2^8
-      const bool grow = bmax > mref[j] + kRescale;
+      const bool grow = bm > mref[j] + kRescale;
       if (ballot(grow) != 0ull) {
-        const float alpha = grow ? exp2f(mref[j] - bmax) : 1.f;  // 0 when mref was -inf
+        const float alpha = grow ? __builtin_amdgcn_exp2f(mref[j] - bm) : 1.f;  // 0 from -inf
 #pragma unroll
         for (int x = 0; x < 8; ++x) o[j][x] *= alpha;
         lsum[j] *= alpha;
-        mref[j] = grow ? bmax : mref[j];
+        mref[j] = grow ? bm : mref[j];
       }
-      const float mr = mref[j];
+      // rows that did not pick the block get P = 0 (exp2 of -inf)
+      const float msub = act ? mref[j] : __builtin_huge_valf();
       float ps = 0.f;
       bf16x8 pb[2];
 #pragma unroll
@@ -231,8 +273,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float z = sc[2 * kv + e / 4][e % 4];
-          p[e] = z == -__builtin_huge_valf() ? 0.f : exp2f(z - mr);
+          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * kv + e / 4][e % 4], a.scale_log2, -msub));
           ps += p[e];
         }
         u32x4 pw;
@@ -241,36 +282,39 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
         pb[kv] = as_bf16x8(pw);
       }
       lsum[j] += ps;
-      // O^T += V^T P^T: k-slot e of K-step kv is key 32kv + 16(e/4) + 4g + e%4
-      // (the lane's own S^T registers); a 4-byte read at dims 64hf + 4n + 2jp
-      // feeds M-tiles (hf, 2jp) and (hf, 2jp+1)
+      // O^T += V^T P^T over two K-steps of 32 keys; k-slot e of K-step kv is key
+      // 32kv + 16(e/4) + 4g + e%4, matching this lane's own P registers
 #pragma unroll
-      for (int kv = 0; kv < 2; ++kv)
+      for (int mt = 0; mt < 8; ++mt) {
+        const uint32_t va = vt + (uint32_t)(vlane ^ (32 * mt));
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int jp = 0; jp < 2; ++jp) {
-            uint32_t rd[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int koff = (32 * kv + 16 * (e / 4) + (e % 4)) * 256 + 4 * jp;
-              rd[e] = *reinterpret_cast<const uint32_t*>((hf ? vt1 : vt0) + koff);
-            }
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-              u32x4 av;
-#pragma unroll
-              for (int w2 = 0; w2 < 4; ++w2) {
-                const uint32_t x = rd[2 * w2], y = rd[2 * w2 + 1];
-                av[w2] = jj ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-              }
-              o[j][4 * hf + 2 * jp + jj] = mfma16(as_bf16x8(av), pb[kv], o[j][4 * hf + 2 * jp + jj]);
-            }
-          }
+        for (int kv = 0; kv < 2; ++kv) {
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_ptr)(uintptr_t)(va + (32 * kv) * 256));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_ptr)(uintptr_t)(va + (32 * kv + 16) * 256));
+          const bf16x8 av =
+              __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[j][mt] = mfma16(av, pb[kv], o[j][mt]);
+        }
+      }
     }
   };
 
   bool ok_run = true;
+  int pend0 = -1, pend1 = -1, pend_n = 0;  // this wave's refills not yet published
+  // publish own refills of entries <= lim: wait for their loads, then tag
+  auto publish_upto = [&](int lim) {
+    while (pend_n > 0 && pend0 <= lim) {
+      wait_vm(pend_n > 1 ? 32 : 0);
+      if (lane == 0) lds_store_tag(&ready[pend0 % kRing], pend0);
+      cbarrier();
+      pend0 = pend1;
+      pend1 = -1;
+      --pend_n;
+    }
+  };
+
   for (int wb = 0; wb <= cur_last && ok_run; wb += kWin) {
     const int we = min(wb + kWin, cur_last + 1);
     // 1. row and group bitmasks of the window's blocks
@@ -285,7 +329,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
       constexpr int parts = kWaves * kWave / TR;
       const int row = tid % TR, part = tid / TR;
       if (row < rows && part < parts) {
-        const int cur = (a.q_start + t0 + row) / kBlock;
+        const int cur = (pos0 + row) / kBlock;
         const int32_t* lst = selh + (size_t)row * a.top_k;
         for (int x = part; x < a.top_k; x += parts) {
           const int c = lst[x];
@@ -297,80 +341,90 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
       }
     }
     __syncthreads();
-    // 2. union list of the window, ascending
+    // 2. union list of the window, ascending, with the waves that want each entry
     int nu = 0;
     for (int j = 0; j < kWin; j += kWaves * kWave) {
       const int pidx = j + tid;
-      const bool nz = pidx < we - wb && gmask[pidx] != 0u;
+      const uint32_t gmv = pidx < we - wb ? gmask[pidx] : 0u;
+      const bool nz = gmv != 0u;
       const uint64_t bal = ballot(nz);
       if (lane == 0) wcount[wave] = __popcll(bal);
       __syncthreads();
       int before = nu;
       for (int w = 0; w < wave; ++w) before += wcount[w];
-      if (nz) ulist[before + prefix_count(bal)] = wb + pidx;
+      if (nz) {
+        const uint32_t wbits = (gmv | (gmv >> 8) | (gmv >> 16)) & 0xffu;
+        ulist[before + prefix_count(bal)] = (wb + pidx) | (int)(wbits << 24);
+      }
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) nu += wcount[w];
       __syncthreads();
     }
     // 3. first kRing entries: every wave moves 2 of the 16 instructions of each
-    for (int s = 0; s < kRing && s < nu; ++s) fetch(ulist[s], s, 2 * wave, 2 * wave + 2);
+    for (int s = 0; s < kRing && s < nu; ++s)
+      fetch_part(ulist[s] & 0xffffff, s, 2 * wave, 2 * wave + 2);
     wait_vm(0);
     __syncthreads();
     if (tid < kRing && tid < nu) ready[tid] = tid;
     __syncthreads();
-    // 4. decoupled sweep
-    int pend_u[2] = {-1, -1}, pend_n = 0;  // this wave's refills not yet published
-    for (int u = 0; u < nu; ++u) {
-      const int sl = u % kRing;
-      // publish own refills due by u + 2 (entry x is published once u >= x - 2)
-      while (pend_n > 0 && pend_u[0] <= u + 2) {
-        wait_vm(pend_n > 1 ? 32 : 0);
-        // the wait above retired the slot's global->LDS loads (vmcnt), so the
-        // data is in LDS before the tag is written
-        if (lane == 0) lds_store_tag(&ready[pend_u[0] % kRing], pend_u[0]);
-        cbarrier();
-        pend_u[0] = pend_u[1];
-        pend_u[1] = -1;
-        --pend_n;
-      }
-      // wait for entry u
-      int spins = 0;
-      // a wave's LDS operations complete in order, so once the tag reads u the
-      // slot's data reads below see the published block
-      while (lds_load_tag(&ready[sl]) != u) {
-        if (++spins > kSpinLimit) {
-          ok_run = false;
-          break;
+    // 4. decoupled sweep over the entries this wave wants
+    for (int u0 = 0; u0 < nu && ok_run; u0 += kWave) {
+      const int ue = u0 + lane < nu ? ulist[u0 + lane] : 0;
+      uint64_t mine = ballot(u0 + lane < nu && ((ue >> (24 + wave)) & 1));
+      while (mine != 0ull) {
+        const int bit = __builtin_ctzll(mine);
+        mine &= mine - 1;
+        const int u = u0 + bit;
+        const int e = __builtin_amdgcn_readlane(ue, bit);
+        const int c = e & 0xffffff;
+        const int need = __builtin_popcount((uint32_t)e >> 24);
+        const int sl = u % kRing;
+        publish_upto(u + 2);
+        // a wave's LDS operations complete in order, so once the tag reads u the
+        // slot's data reads below see the published block
+        if (lds_load_tag(&ready[sl]) != u) {
+          publish_upto(0x7fffffff);
+          int spins = 0;
+          while (lds_load_tag(&ready[sl]) != u) {
+            if (++spins > kSpinLimit) {
+              ok_run = false;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+          }
+          if (!ok_run) {
+            if (lane == 0) failed = 1;
+            break;
+          }
         }
-        __builtin_amdgcn_s_sleep(2);
-      }
-      if (!ok_run) {
-        if (lane == 0) failed = 1;
-        break;
-      }
-      cbarrier();
-      compute(sl, ulist[u], wb);
-      cbarrier();
-      // count this wave done (its slot reads precede the increment in the
-      // wave's in-order LDS stream); the last one refills the slot with entry
-      // u + kRing
-      int prev = 0;
-      if (lane == 0) prev = lds_fetch_add_tag(&done[sl], 1);
-      prev = __shfl(prev, 0);
-      if (prev == kWaves - 1) {
-        if (lane == 0) lds_store_tag(&done[sl], 0);
-        if (u + kRing < nu) {
-          fetch(ulist[u + kRing], sl, 0, 16);
-          pend_u[pend_n++] = u + kRing;
+        cbarrier();
+        compute(sl, c, gmask[c - wb], rmask[c - wb]);
+        cbarrier();
+        // count this wave done (its slot reads precede the increment in the
+        // wave's in-order LDS stream); the last wanting wave refills the slot
+        // with entry u + kRing
+        int prev = 0;
+        if (lane == 0) prev = lds_fetch_add_tag(&done[sl], 1);
+        prev = __builtin_amdgcn_readfirstlane(prev);
+        if (prev == need - 1) {
+          if (lane == 0) lds_store_tag(&done[sl], 0);
+          if (u + kRing < nu) {
+            fetch_full(ulist[u + kRing] & 0xffffff, sl);
+            if (pend_n == 0) pend0 = u + kRing;
+            else pend1 = u + kRing;
+            ++pend_n;
+          }
         }
       }
     }
+    publish_upto(0x7fffffff);
     wait_vm(0);
     __syncthreads();
     if (failed) ok_run = false;
   }
 
-  // epilogue: normalise and store this wave's groups
+  // epilogue: normalise and store this wave's groups; register r of o[j][mt] is
+  // dim 16mt + 4g + r of this lane's column
 #pragma unroll
   for (int j = 0; j < kGPW; ++j) {
     const int row = (wave + kWaves * j) * RPG + rr;
@@ -380,18 +434,11 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
       const float inv = !ok_run ? __builtin_nanf("") : (L > 0.f ? 1.f / L : 0.f);
       uint16_t* dst = a.out + (((size_t)b * a.Sq + t0 + row) * a.Hq + h * G + hh) * kHeadDim;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        u32x4 w0, w1;
-#pragma unroll
-        for (int qd = 0; qd < 8; ++qd) {
-          const int e0 = 2 * qd, e1 = 2 * qd + 1;  // element e = 4r + jx of run 64hf + 16g
-          const uint32_t v = pack_bf16x2(o[j][4 * hf + (e0 & 3)][e0 >> 2] * inv,
-                                         o[j][4 * hf + (e1 & 3)][e1 >> 2] * inv);
-          if (qd < 4) w0[qd] = v; else w1[qd - 4] = v;
-        }
-        u32x4* d = reinterpret_cast<u32x4*>(dst + 64 * hf + 16 * g);
-        d[0] = w0;
-        d[1] = w1;
+      for (int mt = 0; mt < 8; ++mt) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[j][mt][0] * inv, o[j][mt][1] * inv);
+        w[1] = pack_bf16x2(o[j][mt][2] * inv, o[j][mt][3] * inv);
+        *reinterpret_cast<u32x2*>(dst + 16 * mt + 4 * g) = w;
       }
       if (a.lse && g == 0)
         a.lse[((size_t)b * a.Hq + h * G + hh) * a.Sq + t0 + row] =
@@ -408,6 +455,8 @@ hipError_t launch_union_prefill(const Shape& s, const void* q, const void* k, co
                                 const int32_t* sel, void* out, float* lse, hipStream_t st) {
   const int TR = kNG * 16 / s.G;
   const int ntiles = ceil_div(s.Sq, TR);
+  // the buffer descriptors address one head's K or V with 32-bit byte offsets
+  if ((long long)s.Skv * kHeadDim * 2 > 0x7fffffffLL) return hipErrorInvalidValue;
   UnionArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
               static_cast<const uint16_t*>(v), sel, static_cast<uint16_t*>(out), lse,
               s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.top_k, ntiles, s.scale * kLog2e};
