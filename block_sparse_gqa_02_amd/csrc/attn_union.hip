@@ -22,11 +22,14 @@
 // Only the waves that own a row group wanting a block take part in it: they
 // wait for the block's slot to carry its ready tag, run their groups, and count
 // themselves done.  The last of them refills the slot with the block kRing
-// entries ahead and publishes its tag once the loads have landed (at the latest
-// before it waits on anything itself, so no wave ever waits while holding an
-// unpublished refill).  Waves that want none of a block skip it without
-// touching the ring.  Every wait is bounded: past the bound the kernel stops
-// waiting and stores NaN outputs (a caller-visible failure, never a hang).
+// entries ahead.  The new tag is published by the memory system, not by the
+// wave: after the 32 data loads the refiller issues one more LDS-bound load
+// that copies the entry number from a device table into the slot's tag, and a
+// wave's loads return in issue order, so the tag lands after the data.  The
+// refiller never waits for its own fetch.  Waves that want none of a block
+// skip it without touching the ring.  Every wait is bounded: past the bound
+// the kernel stops waiting and stores NaN outputs (a caller-visible failure,
+// never a hang).
 //
 // LDS layouts (256-byte rows, 16-byte chunks).  K: chunk c of row r sits at
 // chunk c ^ (r & 15), so the 16 rows of an S-tile read at one chunk hit 16
@@ -111,6 +114,15 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, const void
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)dst, 16, voff, soff, 0, 0);
 }
 
+// Entry numbers 0..kWin-1, the source of the ring tags written by LDS-bound loads.
+struct EntryIds {
+  int32_t v[kWin];
+  constexpr EntryIds() : v() {
+    for (int i = 0; i < kWin; ++i) v[i] = i;
+  }
+};
+__device__ const EntryIds kEntryIds{};
+
 template <int G>
 __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionArgs a) {
   constexpr int RPG = 16 / G;               // rows per group
@@ -142,6 +154,8 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
       (void*)(a.k + head * a.Skv * kHeadDim), (short)0, a.Skv * kHeadDim * 2, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.v + head * a.Skv * kHeadDim), (short)0, a.Skv * kHeadDim * 2, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rtag = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)&kEntryIds, (short)0, (int)sizeof(kEntryIds), kRsrcFlags);
   const int32_t* selh = a.sel + (head * a.Sq + t0) * a.top_k;
   const int rr = n / G, hh = n % G;  // this lane's column: row in group, head
 
@@ -302,19 +316,6 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
   };
 
   bool ok_run = true;
-  int pend0 = -1, pend1 = -1, pend_n = 0;  // this wave's refills not yet published
-  // publish own refills of entries <= lim: wait for their loads, then tag
-  auto publish_upto = [&](int lim) {
-    while (pend_n > 0 && pend0 <= lim) {
-      wait_vm(pend_n > 1 ? 32 : 0);
-      if (lane == 0) lds_store_tag(&ready[pend0 % kRing], pend0);
-      cbarrier();
-      pend0 = pend1;
-      pend1 = -1;
-      --pend_n;
-    }
-  };
-
   for (int wb = 0; wb <= cur_last && ok_run; wb += kWin) {
     const int we = min(wb + kWin, cur_last + 1);
     // 1. row and group bitmasks of the window's blocks
@@ -379,11 +380,9 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
         const int c = e & 0xffffff;
         const int need = __builtin_popcount((uint32_t)e >> 24);
         const int sl = u % kRing;
-        publish_upto(u + 2);
         // a wave's LDS operations complete in order, so once the tag reads u the
-        // slot's data reads below see the published block
+        // slot's data reads below see the block
         if (lds_load_tag(&ready[sl]) != u) {
-          publish_upto(0x7fffffff);
           int spins = 0;
           while (lds_load_tag(&ready[sl]) != u) {
             if (++spins > kSpinLimit) {
@@ -407,17 +406,19 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
         if (lane == 0) prev = lds_fetch_add_tag(&done[sl], 1);
         prev = __builtin_amdgcn_readfirstlane(prev);
         if (prev == need - 1) {
+          // the count is reset before the loads are issued; the tag that lets
+          // the next entry's waves in is written after the block's data
           if (lane == 0) lds_store_tag(&done[sl], 0);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           if (u + kRing < nu) {
             fetch_full(ulist[u + kRing] & 0xffffff, sl);
-            if (pend_n == 0) pend0 = u + kRing;
-            else pend1 = u + kRing;
-            ++pend_n;
+            if (lane == 0)
+              __builtin_amdgcn_raw_ptr_buffer_load_lds(rtag, (lds_ptr)&ready[sl], 4, 0,
+                                                       (u + kRing) * 4, 0, 0);
           }
         }
       }
     }
-    publish_upto(0x7fffffff);
     wait_vm(0);
     __syncthreads();
     if (failed) ok_run = false;
