@@ -241,16 +241,26 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
     for (int j = 0; j < kGPW; ++j) {
       const int gi = wave + kWaves * j;
       if (!((gm >> gi) & 1u)) continue;
-      // S^T = K Q^T: sc[mt][r] is the score of key 16mt + 4g + r for this column
+      // S^T = K Q^T: sc[mt][r] is the score of key 16mt + 4g + r for this column.
+      // K-step outer, M-tile inner: the four accumulators are independent, and
+      // the fragments of K-step ks + 1 are read while K-step ks multiplies.
       f32x4 sc[4];
+      bf16x8 kf[2][4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         sc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        kf[0][mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + kbyte[0] + mt * 4096));
+      }
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + kbyte[ks] + mt * 4096));
-          sc[mt] = mfma16(kf, qf[j][ks], sc[mt]);
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks < 3) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            kf[(ks + 1) & 1][mt] =
+                as_bf16x8(*reinterpret_cast<const u32x4*>(kt + kbyte[ks + 1] + mt * 4096));
         }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) sc[mt] = mfma16(kf[ks & 1][mt], qf[j][ks], sc[mt]);
       }
       const int row = gi * RPG + rr;
       const bool act = (rm[row / 32] >> (row % 32)) & 1u;
@@ -297,20 +307,23 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
       }
       lsum[j] += ps;
       // O^T += V^T P^T over two K-steps of 32 keys; k-slot e of K-step kv is key
-      // 32kv + 16(e/4) + 4g + e%4, matching this lane's own P registers
+      // 32kv + 16(e/4) + 4g + e%4, matching this lane's own P registers.  V
+      // fragments are read three (K-step, M-tile) steps ahead of their multiply.
+      auto vfrag = [&](int kv, int mt) {
+        const uint32_t va = vt + (uint32_t)(vlane ^ (32 * mt)) + (32 * kv) * 256;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)va);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)(va + 16 * 256));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 vf[4];
+      vf[0] = vfrag(0, 0);
+      vf[1] = vfrag(0, 1);
+      vf[2] = vfrag(0, 2);
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const uint32_t va = vt + (uint32_t)(vlane ^ (32 * mt));
-#pragma unroll
-        for (int kv = 0; kv < 2; ++kv) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_ptr)(uintptr_t)(va + (32 * kv) * 256));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4_ptr)(uintptr_t)(va + (32 * kv + 16) * 256));
-          const bf16x8 av =
-              __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[j][mt] = mfma16(av, pb[kv], o[j][mt]);
-        }
+      for (int st = 0; st < 16; ++st) {
+        const int kv = st / 8, mt = st % 8;
+        if (st < 13) vf[(st + 3) & 3] = vfrag((st + 3) / 8, (st + 3) % 8);
+        o[j][mt] = mfma16(vf[st & 3], pb[kv], o[j][mt]);
       }
     }
   };
