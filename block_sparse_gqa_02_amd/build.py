@@ -21,10 +21,17 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU ops.
+# -packed-fp32-ops keeps the compiler from emitting packed fp32 VALU ops;
+# -amdgpu-mfma-vgpr-form keeps MFMA accumulators in ordinary VGPRs, so the
+# VALU reads them without a copy out of the accumulation registers.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include")]
+# The index kernels reduce MFMA results with max only; without NaN semantics
+# those maxima need no canonicalising copies (a third of the VALU work per
+# block).  Their inputs must be finite (stated in include/msa.h).
+FILE_FLAGS = {"index_scores.hip": ["-fno-honor-nans"], "fused.hip": ["-fno-honor-nans"]}
 
 
 def sources() -> list[str]:
@@ -33,7 +40,7 @@ def sources() -> list[str]:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass warns that it does not know the packed-fp32 feature: harmless
     noise = "is not a recognized feature for this target"

@@ -103,7 +103,8 @@ typedef enum {
  * block c: c < cur(t): max over index heads i with i mod Hkv == h and tokens
  * j in [64c, 64c+63] of sum_d iq[b][t][i][d] * ik[b][j][d] (bf16 products,
  * fp32 accumulation); c == cur(t): +inf; entries c > cur(t) are not written.
- * seq_lens == NULL selects prefill positions, else decode positions.
+ * seq_lens == NULL selects prefill positions, else decode positions.  iq and
+ * ik must be finite: NaN or infinite inputs give unspecified block scores.
  * Source: talk summary, section "MSA uses a lightweight index branch before
  * sparse attention" (4 index-query heads, 1 index-key head, highest-scoring
  * positions are kept); block granularity: section "Block-level retrieval
@@ -125,7 +126,8 @@ msa_status msa_topk_blocks(const msa_problem* p, const float* block_scores,
 /* Index scoring and top-k in one pass: the same sel as msa_index_block_scores
  * followed by msa_topk_blocks, but block scores stream through a running
  * top-k and are never written to memory (needed at 1M-token contexts, where
- * they would take gigabytes).  Prefill positions only (seq_lens must be NULL).
+ * they would take gigabytes).  Prefill positions only (seq_lens must be NULL);
+ * iq and ik must be finite, as for msa_index_block_scores.
  * workspace: msa_workspace_bytes(p, MSA_OP_INDEX_TOPK_FUSED) bytes, any
  * content; it holds per-split candidate lists.
  * Source: as msa_index_block_scores and msa_topk_blocks; the 1M-token window
