@@ -10,7 +10,9 @@
 // ring by direct global->LDS loads, each wave moving 1/8 of every block, three
 // blocks ahead of the compute; all waves use every block, so one barrier per
 // block keeps them in step.  Online softmax in the log2 domain with a lazily
-// rescaled reference max; P rounded to bf16 for PV.
+// rescaled reference max; P rounded to bf16 for PV.  The V operand of
+// O^T += V^T P^T comes from ds_read_b64_tr_b16 (each lane receives one dim of
+// four consecutive keys), read three MFMA steps ahead.
 #include "common.h"
 #include "kernels.h"
 #include "lds_ring.h"
@@ -24,6 +26,13 @@ constexpr float kRescale = 8.0f;
 constexpr int kWaves = 8;
 constexpr int kNT = 2;       // MFMA column groups per wave
 constexpr int kRing = 4;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
 
 struct DenseArgs {
   const uint16_t* q;
@@ -101,8 +110,11 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) dense_prefill_kernel(DenseA
   int kbyte[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) kbyte[ks] = n * 256 + (((4 * ks + g) ^ n) << 4);
-  const int vbyte0 = 4 * g * 256 + (((n / 2) ^ ((g & 1) << 3)) << 4) + 8 * (n & 1);
-  const int vbyte1 = 4 * g * 256 + (((8 + n / 2) ^ ((g & 1) << 3)) << 4) + 8 * (n & 1);
+  // V operand: lane (g, n) of the transposed read for M-tile mt, K-step kv and
+  // half hf loads dims 16mt + 4(n%4) .. +3 of key 32kv + 16hf + 4g + n/4; with
+  // that key's swizzle the byte offset is (32kv + 16hf) * 256 + (vlane ^ 32mt)
+  const int r7 = (4 * g + n / 4) & 7;
+  const int vlane = (4 * g + n / 4) * 256 + 32 * r7 + 16 * ((n >> 1) & 1) + 8 * (n & 1);
 
 #pragma unroll
   for (int s = 0; s < kRing - 1; ++s)
@@ -113,54 +125,62 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) dense_prefill_kernel(DenseA
     raw_barrier();  // block c landed for every wave; every wave is done with c-1
     if (c + kRing - 1 < nblk) fetch(c + kRing - 1, (c + kRing - 1) % kRing);
     const char* kt = reinterpret_cast<const char*>(&ktile[sl][0]);
-    const char* vt0 = reinterpret_cast<const char*>(&vtile[sl][0]) + vbyte0;
-    const char* vt1 = reinterpret_cast<const char*>(&vtile[sl][0]) + vbyte1;
-    // S^T = K Q^T for both groups, one K operand read per pair of MFMAs
+    const uint32_t vt = lds_addr(&vtile[sl][0]);
+    // S^T = K Q^T for both groups, one K operand read per pair of MFMAs; K-step
+    // outer so consecutive MFMAs use independent accumulators, K fragments read
+    // three steps ahead
     f32x4 sc[kNT][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int gq = 0; gq < kNT; ++gq) sc[gq][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 kf[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + kbyte[ks] + mt * 4096));
+    for (int st = 0; st < 3; ++st)
+      kf[st] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + kbyte[st / 4] + (st % 4) * 4096));
 #pragma unroll
-        for (int gq = 0; gq < kNT; ++gq) sc[gq][mt] = mfma16(kf, qf[gq][ks], sc[gq][mt]);
-      }
+    for (int st = 0; st < 16; ++st) {
+      const int ks = st / 4, mt = st % 4;
+      if (st < 13)
+        kf[(st + 3) & 3] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + kbyte[(st + 3) / 4] + ((st + 3) % 4) * 4096));
+#pragma unroll
+      for (int gq = 0; gq < kNT; ++gq) sc[gq][mt] = mfma16(kf[st & 3], qf[gq][ks], sc[gq][mt]);
     }
     const bool diag = c * kBlock + kBlock - 1 > pos_first;  // some key may follow some row
     const int key0 = c * kBlock + 4 * g;
     bf16x8 pb[kNT][2];
 #pragma unroll
     for (int gq = 0; gq < kNT; ++gq) {
-      float bmax = -__builtin_huge_valf();
+      if (diag) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (key0 + 16 * mt + r > pos_col[gq]) sc[gq][mt][r] = -__builtin_huge_valf();
+      }
+      float bm = -__builtin_huge_valf();
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float z = sc[gq][mt][r] * a.scale_log2;
-          if (diag && key0 + 16 * mt + r > pos_col[gq]) z = -__builtin_huge_valf();
-          sc[gq][mt][r] = z;
-          bmax = fmaxf(bmax, z);
-        }
-      bmax = wave_max_xor16_32(bmax);
-      const bool grow = bmax > mref[gq] + kRescale;
+        bm = fmaxf(bm, fmaxf(fmaxf(sc[gq][mt][0], sc[gq][mt][1]), fmaxf(sc[gq][mt][2], sc[gq][mt][3])));
+      bm = wave_max_xor16_32(bm) * a.scale_log2;
+      const bool grow = bm > mref[gq] + kRescale;
       if (ballot(grow) != 0ull) {
-        const float alpha = grow ? exp2f(mref[gq] - bmax) : 1.f;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(mref[gq] - bm) : 1.f;  // 0 from -inf
 #pragma unroll
         for (int x = 0; x < 8; ++x) o[gq][x] *= alpha;
         lsum[gq] *= alpha;
-        mref[gq] = grow ? bmax : mref[gq];
+        mref[gq] = grow ? bm : mref[gq];
       }
-      const float mr = mref[gq];
+      // columns past the tile get P = 0 (exp2 of -inf)
+      const float msub = pos_col[gq] >= 0 ? mref[gq] : __builtin_huge_valf();
       float ps = 0.f;
 #pragma unroll
       for (int kv = 0; kv < 2; ++kv) {
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float z = sc[gq][2 * kv + e / 4][e % 4];
-          p[e] = z == -__builtin_huge_valf() ? 0.f : exp2f(z - mr);
+          p[e] = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(sc[gq][2 * kv + e / 4][e % 4], a.scale_log2, -msub));
           ps += p[e];
         }
         u32x4 pw;
@@ -170,33 +190,25 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) dense_prefill_kernel(DenseA
       }
       lsum[gq] += ps;
     }
-    // O^T += V^T P^T, one V operand per pair of MFMAs
+    // O^T += V^T P^T, one V operand per pair of MFMAs; k-slot e of K-step kv is
+    // key 32kv + 16(e/4) + 4g + e%4, matching the lane's own P registers
+    auto vfrag = [&](int kv, int mt) {
+      const uint32_t va = vt + (uint32_t)(vlane ^ (32 * mt)) + (32 * kv) * 256;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)va);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)(va + 16 * 256));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 vf[4];
+    vf[0] = vfrag(0, 0);
+    vf[1] = vfrag(0, 1);
+    vf[2] = vfrag(0, 2);
 #pragma unroll
-    for (int kv = 0; kv < 2; ++kv)
+    for (int st = 0; st < 16; ++st) {
+      const int kv = st / 8, mt = st % 8;
+      if (st < 13) vf[(st + 3) & 3] = vfrag((st + 3) / 8, (st + 3) % 8);
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int jp = 0; jp < 2; ++jp) {
-          uint32_t rd[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int koff = (32 * kv + 16 * (e / 4) + (e % 4)) * 256 + 4 * jp;
-            rd[e] = *reinterpret_cast<const uint32_t*>((hf ? vt1 : vt0) + koff);
-          }
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            u32x4 av;
-#pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2) {
-              const uint32_t x = rd[2 * w2], y = rd[2 * w2 + 1];
-              av[w2] = jj ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-            }
-            const bf16x8 avb = as_bf16x8(av);
-#pragma unroll
-            for (int gq = 0; gq < kNT; ++gq)
-              o[gq][4 * hf + 2 * jp + jj] = mfma16(avb, pb[gq][kv], o[gq][4 * hf + 2 * jp + jj]);
-          }
-        }
+      for (int gq = 0; gq < kNT; ++gq) o[gq][mt] = mfma16(vf[st & 3], pb[gq][kv], o[gq][mt]);
+    }
   }
 
 #pragma unroll
@@ -206,19 +218,13 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) dense_prefill_kernel(DenseA
     if (row < rows) {
       const float inv = L > 0.f ? 1.f / L : 0.f;
       uint16_t* dst = a.out + (((size_t)b * a.Sq + t0 + row) * a.Hq + h * G + hh) * kHeadDim;
+      // register r of o[gq][mt] is dim 16mt + 4g + r of this lane's column
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        u32x4 w0, w1;
-#pragma unroll
-        for (int qd = 0; qd < 8; ++qd) {
-          const int e0 = 2 * qd, e1 = 2 * qd + 1;
-          const uint32_t v = pack_bf16x2(o[gq][4 * hf + (e0 & 3)][e0 >> 2] * inv,
-                                         o[gq][4 * hf + (e1 & 3)][e1 >> 2] * inv);
-          if (qd < 4) w0[qd] = v; else w1[qd - 4] = v;
-        }
-        u32x4* d = reinterpret_cast<u32x4*>(dst + 64 * hf + 16 * g);
-        d[0] = w0;
-        d[1] = w1;
+      for (int mt = 0; mt < 8; ++mt) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[gq][mt][0] * inv, o[gq][mt][1] * inv);
+        w[1] = pack_bf16x2(o[gq][mt][2] * inv, o[gq][mt][3] * inv);
+        *reinterpret_cast<u32x2*>(dst + 16 * mt + 4 * g) = w;
       }
       if (a.lse && g == 0)
         a.lse[((size_t)b * a.Hq + h * G + hh) * a.Sq + t0 + row] =

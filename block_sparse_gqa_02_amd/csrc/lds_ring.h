@@ -9,11 +9,11 @@ namespace msa {
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // 16-byte chunk swizzles of a 256-byte K or V row in LDS.  K: the 16 rows
-// 16mt+n read at one chunk hit 16 distinct chunks.  V: the keys a 16-lane group
-// reads in one 8-byte column read share bit 2, which picks the half of the row,
-// so the four groups hit disjoint bank halves.
+// 16mt+n read at one chunk hit 16 distinct chunks.  V: the 16 rows of one
+// transposed read (ds_read_b64_tr_b16, rows 16hf + 4g + n/4 of a K-step) hit
+// each 32-byte pair of chunks exactly twice.
 __device__ __forceinline__ int kswz(int row) { return row & 15; }
-__device__ __forceinline__ int vswz(int row) { return ((row >> 2) & 1) << 3; }
+__device__ __forceinline__ int vswz(int row) { return (row & 7) << 1; }
 
 // Compiler-only memory barrier (no instruction).
 __device__ __forceinline__ void cbarrier() { asm volatile("" ::: "memory"); }
