@@ -31,6 +31,7 @@ class Workload:
     block_offset_std: float  # std of the per-block key offset (0 = none)
     fused_topk: bool         # block scores must stream through a running top-k
     seed: int
+    iq_shared_rows: int = 1  # rows per run that share one index query (1 = independent)
 
     @property
     def softmax_scale(self) -> float:
@@ -67,4 +68,14 @@ CHUNK_1M = Workload("chunk_prefill_1m", batch=1, seq_q=8192, seq_kv=1048576, q_s
                     block_offset_std=0.0, fused_topk=True, seed=20260005, **_COMMON)
 
 ALL = [TINY_PREFILL_2K, PREFILL_32K, PREFILL_128K, DECODE_32x256K, CHUNK_1M]
-BY_NAME = {w.name: w for w in ALL}
+
+# Diagnostic workloads (not among the five above): every 64-row query block
+# shares one index query, so its rows select the same blocks.  Real index
+# queries of neighbouring tokens are correlated to some degree; these show the
+# sparse prefill where a tile's rows agree, the regime opposite to the
+# independent draws above.
+PREFILL_128K_SHARED_IQ = PREFILL_128K.shrink(name="prefill_128k_shared_iq", iq_shared_rows=64)
+PREFILL_32K_SHARED_IQ = PREFILL_32K.shrink(name="prefill_32k_shared_iq", iq_shared_rows=64)
+DIAGNOSTIC = [PREFILL_32K_SHARED_IQ, PREFILL_128K_SHARED_IQ]
+
+BY_NAME = {w.name: w for w in ALL + DIAGNOSTIC}

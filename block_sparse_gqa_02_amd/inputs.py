@@ -12,7 +12,9 @@ target device, in the order Q, K, V, iQ, iK, and rounded to bf16
 tensors are drawn in fixed-size chunks so that generation needs little scratch
 memory; the result depends only on the seed, the device type and the shapes.
 Integer mode draws every entry uniformly from {-2, ..., 2} instead, so that
-every index score is an integer that fp32 represents exactly.
+every index score is an integer that fp32 represents exactly.  With
+iq_shared_rows = r > 1 (diagnostic workloads), iQ is drawn for ceil(Sq / r)
+rows and each draw is repeated for r consecutive rows.
 """
 from __future__ import annotations
 
@@ -86,7 +88,14 @@ def generate(w: Workload, device, *, seed: Optional[int] = None, integer: bool =
     else:
         _fill(k, gen, integer)
     _fill(v, gen, integer)
-    _fill(iq, gen, integer)
+    r = w.iq_shared_rows
+    if r > 1:
+        runs = torch.empty((B, (Sq + r - 1) // r, w.n_idx_heads, w.idx_head_dim), **bf)
+        _fill(runs, gen, integer)
+        iq.copy_(runs.repeat_interleave(r, dim=1)[:, :Sq])
+        del runs
+    else:
+        _fill(iq, gen, integer)
     if offset:
         _fill_with_block_offset(ik, gen, w.block_offset_std, w.block_size)
     else:

@@ -8,7 +8,8 @@ import pytest
 import torch
 
 from block_sparse_gqa_02_amd.configs import (CHUNK_1M, DECODE_32x256K, PREFILL_128K,
-                                             PREFILL_32K, TINY_PREFILL_2K)
+                                             PREFILL_32K, PREFILL_32K_SHARED_IQ,
+                                             TINY_PREFILL_2K)
 import block_sparse_gqa_02_amd as msa
 from block_sparse_gqa_02_amd.inputs import generate
 import parity as PAR
@@ -71,3 +72,13 @@ def test_fused_equals_separate_full_size(w):
     torch.cuda.synchronize()
     diff = int((sel_f != sel_s).sum().item())
     assert diff == 0, f"{w.name}: {diff} selection entries differ"
+
+
+def test_prefill_32k_shared_index_queries_sampled():
+    """Diagnostic recipe: a 64-row query block shares one index query, so a
+    tile's rows select the same blocks and every row group of the sparse
+    prefill is active for most ring entries."""
+    need_gpu()
+    w = PREFILL_32K_SHARED_IQ
+    rows = PAR.sample_rows(w.seq_q, w.q_start, w.block_size, seed=33, n_uniform=1024)
+    WC.check(w, False, rows, log=log)
