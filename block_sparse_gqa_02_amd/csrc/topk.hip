@@ -144,6 +144,131 @@ __global__ void __launch_bounds__(512) topk_wide_kernel(TopkArgs a) {
   }
 }
 
+// Few long rows, second form: an exact radix select per row.  A work-group of
+// 512 threads holds the row's candidate keys in registers (thread t owns
+// candidates [E t, E t + E)); four 8-bit passes over an LDS histogram find T,
+// the m-th largest key, and how many keys equal to T are taken; two
+// block-wide scans then place every key above T and the lowest-indexed keys
+// equal to T at their ranks in ascending block order.  Same selection as the
+// running-list kernels: score descending, ties to the lower block.
+constexpr int kRadixThreads = 512;
+
+// Exclusive prefix sum of v over the work-group (512 threads); total in *sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* sum) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kRadixThreads / kWave; ++w) {
+    const int x = wsum[w];
+    before += w < wave ? x : 0;
+    total += x;
+  }
+  __syncthreads();
+  *sum = total;
+  return before + incl - v;
+}
+
+template <int E>
+__global__ void __launch_bounds__(kRadixThreads) topk_radix_kernel(TopkArgs a) {
+  __shared__ int hist[256];
+  __shared__ int wsum[kRadixThreads / kWave];
+  __shared__ int pick[2];  // digit, remaining count
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  for (long long row = blockIdx.x; row < a.nrows; row += gridDim.x) {
+    const int t = (int)(row % a.Sq);
+    const int b = (int)(row / ((long long)a.Sq * a.Hkv));
+    const int pos = a.seq_lens ? min(max(a.seq_lens[b], 1), a.Skv) - 1 : a.q_start + t;
+    const int cur = pos / kBlock;
+    const int n = cur + 1;
+    const int m = min(a.k, n);
+    const float* src = a.scores + row * a.nblk;
+    const int c0 = tid * E;
+    uint32_t key[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int c = c0 + e;
+      key[e] = c < n ? (c == cur ? 0xffffffffu : score_key(src[c])) : 0u;  // 0: below every real key
+    }
+    // radix select of the m-th largest key, most significant digit first
+    uint32_t prefix = 0, pmask = 0;
+    int rem = m;
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (c0 + e < n && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255], 1);
+      __syncthreads();
+      if (wave == 0) {
+        // lane l holds digits 4l..4l+3; count of matching keys with a higher digit
+        int h[4], own = 0;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          h[x] = hist[4 * lane + x];
+          own += h[x];
+        }
+        int suffix = own;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int y = __shfl_down(suffix, off);
+          if (lane + off < kWave) suffix += y;
+        }
+        int above = suffix - own;
+#pragma unroll
+        for (int x = 3; x >= 0; --x) {
+          if (above < rem && above + h[x] >= rem) {
+            pick[0] = 4 * lane + x;
+            pick[1] = rem - above;
+          }
+          above += h[x];
+        }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)pick[0] << shift;
+      pmask |= 0xffu << shift;
+      rem = pick[1];
+      __syncthreads();
+    }
+    // prefix is T; take every key above T and the first `rem` keys equal to T
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool ok = c0 + e < n;
+      gt += ok && key[e] > prefix;
+      eq += ok && key[e] == prefix;
+    }
+    int ties_total;
+    const int tie_rank = block_exclusive_scan(eq, wsum, &ties_total);
+    const int take = min(max(rem - tie_rank, 0), eq);
+    int selected;
+    int at = block_exclusive_scan(gt + take, wsum, &selected);
+    int32_t* dst = a.sel + row * a.k;
+    int took = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int c = c0 + e;
+      if (c >= n) continue;
+      const bool tie = key[e] == prefix;
+      if (key[e] > prefix || (tie && took < take)) {
+        dst[at++] = c;
+        took += tie;
+      }
+    }
+    for (int i = m + tid; i < a.k; i += kRadixThreads) dst[i] = -1;
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk_blocks(const Shape& s, const float* scores, const int32_t* seq_lens,
@@ -151,8 +276,16 @@ hipError_t launch_topk_blocks(const Shape& s, const float* scores, const int32_t
   TopkArgs a{scores, seq_lens, sel, s.Sq, s.Skv, s.q_start, s.Hkv, s.nblk, s.top_k,
              (long long)s.B * s.Hkv * s.Sq};
   // list capacity >= k + 128 so that a full chunk always fits after a compaction
+  if (a.nrows < 2048 && s.nblk >= 1024 && s.nblk <= 32 * kRadixThreads) {
+    // few long rows: a work-group per row, radix select
+    const int grid = (int)a.nrows;
+    if (s.nblk <= 8 * kRadixThreads) topk_radix_kernel<8><<<grid, kRadixThreads, 0, st>>>(a);
+    else if (s.nblk <= 16 * kRadixThreads) topk_radix_kernel<16><<<grid, kRadixThreads, 0, st>>>(a);
+    else topk_radix_kernel<32><<<grid, kRadixThreads, 0, st>>>(a);
+    return hipGetLastError();
+  }
   if (a.nrows < 2048 && s.nblk >= 1024) {
-    // few long rows: a work-group per row
+    // few longer rows: a work-group per row, eight running lists
     const int grid = (int)a.nrows;
     if (s.top_k <= 64) topk_wide_kernel<3><<<grid, 512, 0, st>>>(a);
     else if (s.top_k <= 128) topk_wide_kernel<4><<<grid, 512, 0, st>>>(a);
