@@ -92,6 +92,9 @@ def lib():
             "msa_dense_attn_prefill": [pr, vp, vp, vp, vp, vp, vp, sz, vp],
             "msa_dense_attn_decode": [pr, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "msa_workspace_bytes": [pr, ctypes.c_int, P(sz)],
+            "msa_index_block_scores_paged": [pr, vp, vp, vp, ctypes.c_int32, vp, vp, vp],
+            "msa_sparse_attn_decode_paged": [pr, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, vp,
+                                             vp, sz, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -203,6 +206,33 @@ def msa_sparse_attn_decode(p: Problem, q, k_cache, v_cache, seq_lens, sel, out=N
                                         _ptr(sel, torch.int32), _ptr(out, torch.bfloat16),
                                         _ptr(lse, torch.float32), _ptr(ws), nbytes,
                                         _stream(stream)))
+    return out
+
+
+def msa_index_block_scores_paged(p: Problem, iq, ik_pages, page_table, num_pages: int, seq_lens,
+                                 block_scores=None, stream=None):
+    """Decode block scores with the index-K cache in pages [num_pages][64][64]."""
+    if block_scores is None:
+        block_scores = torch.empty((p.batch, p.n_kv_heads, 1, p.nblk), dtype=torch.float32,
+                                   device=iq.device)
+    _check(lib().msa_index_block_scores_paged(
+        ctypes.byref(p.c()), _ptr(iq, torch.bfloat16), _ptr(ik_pages, torch.bfloat16),
+        _ptr(page_table, torch.int32), int(num_pages), _ptr(seq_lens, torch.int32),
+        _ptr(block_scores, torch.float32), _stream(stream)))
+    return block_scores
+
+
+def msa_sparse_attn_decode_paged(p: Problem, q, k_pages, v_pages, page_table, num_pages: int,
+                                 seq_lens, sel, out=None, lse=None, workspace=None, stream=None):
+    """Sparse decode with K and V in pages [num_pages][Hkv][64][128]."""
+    if out is None:
+        out = torch.empty_like(q)
+    ws, nbytes = _workspace(p, "sparse_attn_decode", workspace, q.device)
+    _check(lib().msa_sparse_attn_decode_paged(
+        ctypes.byref(p.c()), _ptr(q, torch.bfloat16), _ptr(k_pages, torch.bfloat16),
+        _ptr(v_pages, torch.bfloat16), _ptr(page_table, torch.int32), int(num_pages),
+        _ptr(seq_lens, torch.int32), _ptr(sel, torch.int32), _ptr(out, torch.bfloat16),
+        _ptr(lse, torch.float32), _ptr(ws), nbytes, _stream(stream)))
     return out
 
 

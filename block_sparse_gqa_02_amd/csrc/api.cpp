@@ -212,6 +212,53 @@ msa_status msa_dense_attn_decode(const msa_problem* p, const void* q, const void
                        workspace_bytes, stream, "msa_dense_attn_decode");
 }
 
+msa_status msa_index_block_scores_paged(const msa_problem* p, const void* iq,
+                                        const void* ik_pages, const int32_t* page_table,
+                                        int32_t num_pages, const int32_t* seq_lens,
+                                        float* block_scores, hipStream_t stream) {
+  msa::Shape s;
+  msa_status st = check_problem(p, Mode::kDecode, false, &s);
+  if (st != MSA_OK) return st;
+  NEED_PTR(iq);
+  NEED_PTR(ik_pages);
+  NEED_PTR4(page_table);
+  NEED_PTR4(seq_lens);
+  NEED_PTR4(block_scores);
+  if (num_pages < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+  const msa::Paging pg{page_table, num_pages};
+  return launched(msa::launch_index_block_scores(s, iq, ik_pages, seq_lens, block_scores, stream,
+                                                 &pg),
+                  "msa_index_block_scores_paged");
+}
+
+msa_status msa_sparse_attn_decode_paged(const msa_problem* p, const void* q,
+                                        const void* k_pages, const void* v_pages,
+                                        const int32_t* page_table, int32_t num_pages,
+                                        const int32_t* seq_lens, const int32_t* sel, void* out,
+                                        float* lse, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  msa::Shape s;
+  msa_status st = check_problem(p, Mode::kDecode, true, &s);
+  if (st != MSA_OK) return st;
+  NEED_PTR(q);
+  NEED_PTR(k_pages);
+  NEED_PTR(v_pages);
+  NEED_PTR4(page_table);
+  NEED_PTR4(seq_lens);
+  NEED_PTR4(sel);
+  NEED_PTR(out);
+  NEED_PTR(workspace);
+  if (num_pages < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+  if (lse && !aligned(lse, 4)) return fail(MSA_ERR_INVALID_ARGUMENT, "lse is not 4-byte aligned");
+  const size_t need = msa::decode_workspace_bytes(s, false);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  const msa::Paging pg{page_table, num_pages};
+  return launched(msa::launch_attn_decode(s, q, k_pages, v_pages, seq_lens, sel, out, lse,
+                                          workspace, stream, &pg),
+                  "msa_sparse_attn_decode_paged");
+}
+
 msa_status msa_workspace_bytes(const msa_problem* p, msa_op op, size_t* bytes) {
   if (!bytes) return fail(MSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
   msa::Shape s;

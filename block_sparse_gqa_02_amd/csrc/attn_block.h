@@ -62,9 +62,16 @@ struct WaveAttn {
   // j > pos masked.  vlds: this wave's 16 KiB V staging area.
   __device__ __forceinline__ void block(const uint16_t* k_head, const uint16_t* v_head, int c,
                                         int pos, float scale_log2, u32x4* vlds) {
+    block_at(k_head + (size_t)c * kBlock * kHeadDim, v_head + (size_t)c * kBlock * kHeadDim, c,
+             pos, scale_log2, vlds);
+  }
+
+  // The same with the block's 64 K and V rows at k_blk / v_blk (a cache page).
+  __device__ __forceinline__ void block_at(const uint16_t* k_blk, const uint16_t* v_blk, int c,
+                                           int pos, float scale_log2, u32x4* vlds) {
     const int lane = lane_id(), n = lane % 16, g = lane / 16;
-    const u32x4* kb = reinterpret_cast<const u32x4*>(k_head + (size_t)c * kBlock * kHeadDim);
-    const u32x4* vb = reinterpret_cast<const u32x4*>(v_head + (size_t)c * kBlock * kHeadDim);
+    const u32x4* kb = reinterpret_cast<const u32x4*>(k_blk);
+    const u32x4* vb = reinterpret_cast<const u32x4*>(v_blk);
     // Rows past pos (only in the own block, which may also run past the end of
     // the cache) are read from row pos instead and masked below.
     const int last = min(pos - c * kBlock, kBlock - 1);

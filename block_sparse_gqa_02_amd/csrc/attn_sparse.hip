@@ -85,6 +85,8 @@ struct DecodeArgs {
   float* lse;            // [B][Hq][1] or null
   int Skv, Hq, Hkv, G, top_k, nsplit, per_split;
   float scale_log2;
+  const int32_t* pages;  // paged K/V pools: [B][nblk] page ids, else null
+  int num_pages, nblk;
 };
 
 __global__ void __launch_bounds__(256) decode_partial_kernel(DecodeArgs a) {
@@ -108,7 +110,16 @@ __global__ void __launch_bounds__(256) decode_partial_kernel(DecodeArgs a) {
   for (int r = rbeg; r < rend; ++r) {
     const int c = list ? list[r] : r;
     if (c < 0 || c > cur) continue;
-    st.block(kh, vh, c, pos, a.scale_log2, vtile[wave]);
+    if (a.pages) {
+      // block c of this sequence is page pg of the pools ([page][Hkv][64][128]);
+      // ids outside the pool are skipped, never read
+      const int pg = a.pages[(size_t)b * a.nblk + c];
+      if (pg < 0 || pg >= a.num_pages) continue;
+      const size_t off = ((size_t)pg * a.Hkv + h) * kBlock * kHeadDim;
+      st.block_at(a.k + off, a.v + off, c, pos, a.scale_log2, vtile[wave]);
+    } else {
+      st.block(kh, vh, c, pos, a.scale_log2, vtile[wave]);
+    }
   }
   const float L = st.total_l();
   const int n = lane % 16, g = lane / 16;
@@ -192,7 +203,7 @@ size_t decode_workspace_bytes(const Shape& s, bool dense) {
 
 hipError_t launch_attn_decode(const Shape& s, const void* q, const void* k, const void* v,
                               const int32_t* seq_lens, const int32_t* sel, void* out, float* lse,
-                              void* ws, hipStream_t st) {
+                              void* ws, hipStream_t st, const Paging* pg) {
   const bool dense = sel == nullptr;
   const int nsplit = decode_nsplit(s, dense);
   const size_t cols = (size_t)s.B * s.Hkv * nsplit * s.G;
@@ -201,7 +212,8 @@ hipError_t launch_attn_decode(const Shape& s, const void* q, const void* k, cons
   DecodeArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                static_cast<const uint16_t*>(v), seq_lens, sel, part_o, part_ml,
                static_cast<uint16_t*>(out), lse, s.Skv, s.Hq, s.Hkv, s.G, s.top_k, nsplit,
-               decode_per_split(s, dense), s.scale * kLog2e};
+               decode_per_split(s, dense), s.scale * kLog2e, pg ? pg->table : nullptr,
+               pg ? pg->num_pages : 0, s.nblk};
   dim3 g1(ceil_div(nsplit, kAttnWaves), s.Hkv, s.B);
   decode_partial_kernel<<<g1, 256, 0, st>>>(a);
   hipError_t e = hipGetLastError();

@@ -33,6 +33,8 @@ struct IndexArgs {
   const int32_t* seq_lens;
   float* scores;       // [B][Hkv][Sq][nblk]
   int Sq, Skv, q_start, nblk;
+  const int32_t* pages;  // decode with a paged index-K cache: [B][nblk] page ids, else null
+  int num_pages;
 };
 
 template <int HKV>
@@ -99,13 +101,26 @@ index_scores_decode_kernel(IndexArgs a) {
     qf[ks] = as_bf16x8(v);
   }
   const u32x4* ikb = reinterpret_cast<const u32x4*>(a.ik + (size_t)b * a.Skv * kIdxDim);
+  // index-K block c: contiguous cache, or its page (ids outside the pool read
+  // page 0 and score -inf)
+  auto block_base = [&](int c) -> const u32x4* {
+    if (!a.pages) return ikb + (size_t)c * kBlock * 8;
+    const int pg = a.pages[(size_t)b * a.nblk + c];
+    const bool ok = pg >= 0 && pg < a.num_pages;
+    return reinterpret_cast<const u32x4*>(a.ik) + (size_t)(ok ? pg : 0) * kBlock * 8;
+  };
+  auto page_ok = [&](int c) {
+    if (!a.pages) return true;
+    const int pg = a.pages[(size_t)b * a.nblk + c];
+    return pg >= 0 && pg < a.num_pages;
+  };
   // two blocks per step: 16 independent 16-byte loads in flight per lane
   auto load = [&](int c, u32x4 (&kr)[4][2]) {
+    const u32x4* base = block_base(c);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        kr[mt][ks] = ikb[((size_t)c * kBlock + 16 * mt + n) * 8 + 4 * ks + g];
+      for (int ks = 0; ks < 2; ++ks) kr[mt][ks] = base[(16 * mt + n) * 8 + 4 * ks + g];
   };
   auto score = [&](int c, const u32x4 (&kr)[4][2]) {
     // A operand: M-tile mt holds keys 64c + 16mt + (l%16), same dim mapping.
@@ -120,6 +135,7 @@ index_scores_decode_kernel(IndexArgs a) {
     m = wave_max_xor16_32(m);  // block max of column n (index head n)
     if (HKV <= 2) m = fmaxf(m, __shfl_xor(m, 2));
     if (HKV == 1) m = fmaxf(m, __shfl_xor(m, 1));
+    if (!page_ok(c)) m = -__builtin_huge_valf();
     if (lane < HKV) out[(size_t)lane * a.nblk + c] = m;
   };
   for (int c = cbeg; c < cend; c += 2) {
@@ -135,9 +151,11 @@ index_scores_decode_kernel(IndexArgs a) {
 }  // namespace
 
 hipError_t launch_index_block_scores(const Shape& s, const void* iq, const void* ik,
-                                     const int32_t* seq_lens, float* scores, hipStream_t st) {
+                                     const int32_t* seq_lens, float* scores, hipStream_t st,
+                                     const Paging* pg) {
+  if (pg && !seq_lens) return hipErrorInvalidValue;  // paged caches are decode caches
   IndexArgs a{static_cast<const uint16_t*>(iq), static_cast<const uint16_t*>(ik), seq_lens, scores,
-              s.Sq, s.Skv, s.q_start, s.nblk};
+              s.Sq, s.Skv, s.q_start, s.nblk, pg ? pg->table : nullptr, pg ? pg->num_pages : 0};
   const bool dec = seq_lens != nullptr;
   const int per_wg = 4 * kDecodeBlocksPerWave;
   dim3 grid = dec ? dim3(ceil_div(s.nblk, per_wg), s.B) : dim3(ceil_div(s.Sq, kTileRows), s.B);

@@ -17,9 +17,18 @@ struct Shape {
   int nblk;           // ceil(Skv / 64)
 };
 
+// Paged caches (decode): block c of sequence b lives in page table[b * nblk + c]
+// of pools of num_pages pages; ids outside [0, num_pages) are never read.
+struct Paging {
+  const int32_t* table;
+  int num_pages;
+};
+
 // Index branch: block scores [B][Hkv][Sq][nblk] (decode when seq_lens != NULL).
+// pg (decode only): ik is a pool of [num_pages][64][64] pages.
 hipError_t launch_index_block_scores(const Shape& s, const void* iq, const void* ik,
-                                     const int32_t* seq_lens, float* scores, hipStream_t st);
+                                     const int32_t* seq_lens, float* scores, hipStream_t st,
+                                     const Paging* pg = nullptr);
 
 // Per-KV-head top-k over block scores -> sel [B][Hkv][Sq][k].
 hipError_t launch_topk_blocks(const Shape& s, const float* scores, const int32_t* seq_lens,
@@ -39,9 +48,10 @@ bool union_prefill_supported(const Shape& s);
 hipError_t launch_union_prefill(const Shape& s, const void* q, const void* k, const void* v,
                                 const int32_t* sel, void* out, float* lse, hipStream_t st);
 size_t decode_workspace_bytes(const Shape& s, bool dense);
+// sel == NULL: dense; pg: k and v are pools of [num_pages][Hkv][64][128] pages.
 hipError_t launch_attn_decode(const Shape& s, const void* q, const void* k, const void* v,
                               const int32_t* seq_lens, const int32_t* sel, void* out, float* lse,
-                              void* ws, hipStream_t st);  // sel == NULL: dense
+                              void* ws, hipStream_t st, const Paging* pg = nullptr);
 
 // Dense causal attention (baseline): row-wise (one wave per row and KV head)
 // and tiled (K/V tiles shared by a work-group of rows).

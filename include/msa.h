@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 1
+#define MSA_ABI_VERSION 2
 
 typedef enum {
   MSA_OK = 0,
@@ -173,6 +173,36 @@ msa_status msa_dense_attn_decode(const msa_problem* p, const void* q, const void
                                  const void* v_cache, const int32_t* seq_lens, void* out,
                                  float* lse, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream);
+
+/* Paged decode caches.  The index-K, K and V caches of the decode functions
+ * above can instead live in page pools, one page per 64-token block:
+ *   ik_pages [num_pages][64][64] bf16,  k_pages / v_pages [num_pages][Hkv][64][128]
+ *   bf16 (one page and KV head is a contiguous 16 KiB run, as in the
+ *   contiguous cache), page_table [batch][ceil(seq_kv / 64)] int32 (device):
+ *   block c of sequence b is page page_table[b][c].
+ * p->seq_kv is the capacity per sequence (it sizes page_table rows and
+ * block_scores rows); only entries for blocks c <= (seq_lens[b] - 1) / 64 are
+ * read.  A page id outside [0, num_pages) is never read: its block scores
+ * -inf in msa_index_block_scores_paged and is skipped by
+ * msa_sparse_attn_decode_paged (a caller error with unspecified selection or
+ * output, not a fault).  Results are those of the contiguous functions on
+ * the gathered caches, bit for bit.
+ * Source: the operations are those of msa_index_block_scores and
+ * msa_sparse_attn_decode; the pages fix no cache layout beyond block-contiguous
+ * reads (talk summary, section "Block-level retrieval makes sparse attention
+ * easier to run on GPUs"), which one page per block keeps. */
+msa_status msa_index_block_scores_paged(const msa_problem* p, const void* iq,
+                                        const void* ik_pages, const int32_t* page_table,
+                                        int32_t num_pages, const int32_t* seq_lens,
+                                        float* block_scores, hipStream_t stream);
+
+/* workspace: msa_workspace_bytes(p, MSA_OP_SPARSE_ATTN_DECODE). */
+msa_status msa_sparse_attn_decode_paged(const msa_problem* p, const void* q,
+                                        const void* k_pages, const void* v_pages,
+                                        const int32_t* page_table, int32_t num_pages,
+                                        const int32_t* seq_lens, const int32_t* sel, void* out,
+                                        float* lse, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
 
 /* Workspace bytes an operation needs for problem p (0 if none).  Host only. */
 msa_status msa_workspace_bytes(const msa_problem* p, msa_op op, size_t* bytes);

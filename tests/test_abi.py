@@ -29,7 +29,8 @@ def test_header_declares_entry_points():
     for n in ["msa_index_block_scores", "msa_topk_blocks", "msa_index_topk_fused",
               "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_dense_attn_prefill",
               "msa_dense_attn_decode", "msa_workspace_bytes", "msa_status_string",
-              "msa_last_error", "msa_abi_version"]:
+              "msa_last_error", "msa_abi_version", "msa_index_block_scores_paged",
+              "msa_sparse_attn_decode_paged"]:
         assert n in names
 
 
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = binding.lib()
-    assert L.msa_abi_version() == 1
+    assert L.msa_abi_version() == 2
     for code, name in binding.STATUS.items():
         assert L.msa_status_string(code).decode() == name
 
@@ -94,6 +95,32 @@ def test_decode_shape_rules():
     assert st == 3 and "workspace" in msg
     st, _ = call("msa_dense_attn_decode", P(p), A, A, A, NULL, A, NULL, A, 1 << 40, NULL)
     assert st == 1  # seq_lens required
+
+
+def test_paged_decode_rules():
+    p = prob(DECODE_32x256K)
+    need = ctypes.c_size_t()
+    assert call("msa_workspace_bytes", P(p), 4, ctypes.byref(need))[0] == 0
+    # index scores: page table, pool size, decode shape
+    assert call("msa_index_block_scores_paged", P(p), A, A, NULL, 8, A4, A4, NULL)[0] == 1
+    st, msg = call("msa_index_block_scores_paged", P(p), A, A, A4, 0, A4, A4, NULL)
+    assert st == 1 and "num_pages" in msg
+    bad = prob(DECODE_32x256K, seq_q=2)
+    assert call("msa_index_block_scores_paged", P(bad), A, A, A4, 8, A4, A4, NULL)[0] == 1
+    assert call("msa_index_block_scores_paged", P(p), A, A4, A4, 8, A4, A4, NULL)[0] == 1  # pool: 16 B
+    # attention: every pointer, pool size, workspace
+    args = [A, A, A, A4, 8, A4, A4, A, NULL, A, need.value, NULL]
+    for i in (0, 1, 2, 3, 5, 6, 7, 9):
+        a = list(args)
+        a[i] = NULL
+        assert call("msa_sparse_attn_decode_paged", P(p), *a)[0] == 1, i
+    a = list(args)
+    a[4] = -1
+    assert call("msa_sparse_attn_decode_paged", P(p), *a)[0] == 1
+    a = list(args)
+    a[10] = need.value - 1
+    st, msg = call("msa_sparse_attn_decode_paged", P(p), *a)
+    assert st == 3 and "workspace" in msg
 
 
 def test_fused_rules():
