@@ -9,10 +9,14 @@
 // Song: Sparse Attention Cannot Be Directly Ported…", paragraph 6).
 //
 // Pass 1 (fused_sweep_kernel): one work-group per (64-row tile, key split).
-// The index sweep (index_sweep.h) stages 32 blocks of maxima at a time; each
-// (row, KV head) list then appends the candidates above its threshold to a
-// per-split candidate list in the workspace and compacts it to the best k-1
-// when it fills (select.h).  Splits of the key range fill the GPU when there
+// The index sweep (index_sweep.h) stages 32 blocks of maxima at a time.  Each
+// (row, KV head) list belongs to one lane, which keeps its count and threshold
+// in registers, walks its row's staged maxima in ascending block order and
+// appends the candidates above its threshold to its per-split list in the
+// workspace.  A list that could overflow on the next flush is compacted to
+// the best k-1 by the whole wave (select.h): copied into an idle 8 KiB index-K
+// tile buffer of LDS (2 KiB per wave, lists of up to 256 entries), compacted
+// there and the survivors written back; longer lists are compacted in place.  Splits of the key range fill the GPU when there
 // are few tiles; split s of every tile runs on the same XCD (work-group ids are
 // dealt round-robin over the 8 XCDs), so that XCD's L2 serves one key range.
 // Pass 2 (fused_merge_kernel): one wave per list merges the splits' lists
@@ -43,8 +47,6 @@ __host__ __device__ inline int fused_cap(int k) { return 64 * ((k - 1 + 128 + 63
 template <int HKV, int MAXE>
 __global__ void __launch_bounds__(256) fused_sweep_kernel(FusedArgs a) {
   __shared__ IndexLds lds;
-  __shared__ uint32_t lthr[HKV * kTileRows];
-  __shared__ int32_t lcnt[HKV * kTileRows];
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int s = blockIdx.x % a.nsplit;
   const int tile = a.ntiles - 1 - blockIdx.x / a.nsplit;  // late (long) tiles first
@@ -56,87 +58,85 @@ __global__ void __launch_bounds__(256) fused_sweep_kernel(FusedArgs a) {
   const int cend = (int)((long long)(s + 1) * cur_last / a.nsplit);
   const int m = a.k - 1;  // candidates kept per list (own block excluded)
   const long long nlist = (long long)a.B * HKV * a.Sq;
-  for (int L = tid; L < HKV * kTileRows; L += 256) {
-    lthr[L] = 0;
-    lcnt[L] = 0;
-  }
-  __syncthreads();
-  auto base_of = [&](int L) -> long long {  // list L = h * 64 + row of this tile
-    const int h = L / kTileRows, row = L % kTileRows;
-    return ((long long)s * nlist + ((long long)b * HKV + h) * a.Sq + t0 + row) * a.cap;
+  // Lane `lane` of wave h < HKV owns the list of (KV head h, row lane): its
+  // count and threshold live in registers, its entries in the workspace.
+  const int h = wave, row = lane;
+  const bool owner = wave < HKV && row < rows;
+  const int cur_row = (a.q_start + t0 + row) / kBlock;
+  auto list_base = [&](int r) {
+    return ((long long)s * nlist + ((long long)b * HKV + h) * a.Sq + t0 + r) * a.cap;
+  };
+  uint32_t thr = 0;
+  int cnt = 0;
+
+  // Compacts the list of lane l of this wave (n entries) to its best m and
+  // returns the new threshold; spare: 8 KiB of idle LDS (2 KiB per wave).
+  auto compact = [&](int l, int n, u32x4* spare) {
+    const long long lb = list_base(l);
+    // the list's entries were stored by lane l: make them visible to the wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    uint32_t t;
+    if (a.cap <= 256) {
+      uint32_t* sk = reinterpret_cast<uint32_t*>(spare) + wave * 512;
+      int32_t* si = reinterpret_cast<int32_t*>(sk + 256);
+      for (int i = lane; i < n; i += kWave) {
+        sk[i] = a.wkeys[lb + i];
+        si[i] = a.widx[lb + i];
+      }
+      __builtin_amdgcn_wave_barrier();
+      t = wave_compact_topm<MAXE>(sk, si, n, m);
+      for (int i = lane; i < m; i += kWave) {
+        a.wkeys[lb + i] = sk[i];
+        a.widx[lb + i] = si[i];
+      }
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      t = wave_compact_topm<MAXE>(a.wkeys + lb, a.widx + lb, n, m);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return t;
+  };
+  // compacts every list of this wave holding more than `limit` entries
+  auto compact_over = [&](int limit, u32x4* spare) {
+    uint64_t over = ballot(owner && cnt > limit);
+    while (over != 0ull) {
+      const int l = __builtin_ctzll(over);
+      over &= over - 1;
+      const int n = __builtin_amdgcn_readlane(cnt, l);
+      const uint32_t t = compact(l, n, spare);
+      if (lane == l) {
+        thr = t;
+        cnt = m;
+      }
+    }
   };
 
   if (m > 0) {
     index_sweep(IndexTile{a.iq, a.ik, b, t0, rows, a.Sq, a.Skv}, cbeg, cend, lds,
-                [&](int c0, int len) {
-      // lists 2p (lanes 0..31) and 2p+1 (lanes 32..63), one 32-block chunk each
-      for (int p = wave; p < HKV * kTileRows / 2; p += 4) {
-        const int half = lane / 32, e = lane % 32;
-        const int L = 2 * p + half;
-        const int h = L / kTileRows, row = L % kTileRows;
+                [&](int c0, int len, u32x4* spare) {
+      if (wave >= HKV) return;
+      // each owning lane streams the staged maxima of its row, ascending
+      for (int e = 0; e < len; ++e) {
         const int c = c0 + e;
-        const bool ok = row < rows && e < len && c < (a.q_start + t0 + row) / kBlock;
-        uint32_t key = 0;
-        if (ok) {
-          float v = lds.stage[h][row][e];
+        float v = lds.stage[h][row][e];
 #pragma unroll
-          for (int i = h + HKV; i < kIdxHeads; i += HKV) v = fmaxf(v, lds.stage[i][row][e]);
-          key = score_key(v);
-        }
-        int cnt = lcnt[L];
-        const bool pass = ok && key > lthr[L];
-        const uint64_t mask = ballot(pass);
-        const uint32_t hm = half ? (uint32_t)(mask >> 32) : (uint32_t)mask;
-        if (pass) {
-          const int d = cnt + __popc(hm & ((1u << e) - 1u));
-          const long long base = base_of(L);
-          a.wkeys[base + d] = key;
-          a.widx[base + d] = c;
-        }
-        cnt += __popc(hm);
-        if (e == 0) lcnt[L] = cnt;
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int LL = 2 * p + hh;
-          const int n = __shfl(cnt, 32 * hh);
-          if (n > a.cap - 32) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            const long long base = base_of(LL);
-            const uint32_t thr = wave_compact_topm<MAXE>(a.wkeys + base, a.widx + base, n, m);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            if (lane == 0) {
-              lthr[LL] = thr;
-              lcnt[LL] = m;
-            }
-            __builtin_amdgcn_wave_barrier();
-          }
+        for (int j = 1; j < kIdxHeads / HKV; ++j) v = fmaxf(v, lds.stage[h + j * HKV][row][e]);
+        const uint32_t key = score_key(v);
+        if (owner && c < cur_row && key > thr) {
+          const long long lb = list_base(row);
+          a.wkeys[lb + cnt] = key;
+          a.widx[lb + cnt] = c;
+          ++cnt;
         }
       }
+      // a list takes at most kStageCols entries per flush
+      compact_over(a.cap - kStageCols, spare);
     });
   }
-  __syncthreads();
-  // final compaction of this split's lists to at most m entries
-  for (int p = wave; p < HKV * kTileRows / 2; p += 4) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int L = 2 * p + hh;
-      if (L % kTileRows >= rows) continue;
-      int n = lcnt[L];
-      if (n > m) {
-        const long long base = base_of(L);
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        wave_compact_topm<MAXE>(a.wkeys + base, a.widx + base, n, m);
-        n = m;
-      }
-      if (lane == 0) {
-        const int h = L / kTileRows, row = L % kTileRows;
-        a.wcnt[(long long)s * nlist + ((long long)b * HKV + h) * a.Sq + t0 + row] = n;
-      }
-    }
-  }
+  // the list goes to the merge as it stands (up to cap entries, ascending)
+  if (owner) a.wcnt[(long long)s * nlist + ((long long)b * HKV + h) * a.Sq + t0 + row] = cnt;
 }
 
 template <int MAXE>

@@ -49,7 +49,7 @@ index_scores_prefill_kernel(IndexArgs a) {
   const int cur_last = (a.q_start + t0 + rows - 1) / kBlock;  // sweep blocks [0, cur_last)
   const IndexTile T{a.iq, a.ik, b, t0, rows, a.Sq, a.Skv};
 
-  index_sweep(T, 0, cur_last, lds, [&](int c0, int len) {
+  index_sweep(T, 0, cur_last, lds, [&](int c0, int len, u32x4*) {
     // list (h, row): max over index heads i = h (mod HKV); written row-contiguous
     for (int f = tid; f < HKV * kTileRows * kStageCols; f += 256) {
       const int e = f % kStageCols;

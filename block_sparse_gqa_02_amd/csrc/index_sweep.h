@@ -34,9 +34,11 @@ struct IndexTile {
 };
 
 // Sweeps blocks [cbeg, cend) for the tile.  After every kStageCols blocks (and
-// at the end) all threads call flush(c0, len) with stage[i][row][e] holding
-// the max over block c0+e's keys of head i's scores for row t0+row.  Must be
-// called by all 256 threads; contains barriers.
+// at the end) all threads call flush(c0, len, spare) with stage[i][row][e]
+// holding the max over block c0+e's keys of head i's scores for row t0+row;
+// `spare` is an 8 KiB index-K tile buffer that nothing reads or writes until
+// flush returns (scratch for the consumer).  Must be called by all 256
+// threads; contains barriers.
 template <typename Flush>
 __device__ __forceinline__ void index_sweep(const IndexTile& T, int cbeg, int cend, IndexLds& L,
                                             Flush&& flush) {
@@ -113,7 +115,7 @@ __device__ __forceinline__ void index_sweep(const IndexTile& T, int cbeg, int ce
     if (more) store_tile(buf ^ 1);
     __syncthreads();
     if (c + 1 - c0 == kStageCols || !more) {
-      flush(c0, c + 1 - c0);
+      flush(c0, c + 1 - c0, &L.ktile[buf][0]);
       c0 = c + 1;
       __syncthreads();
     }
