@@ -10,17 +10,19 @@
 //
 // Pass 1 (fused_sweep_kernel): one work-group per (64-row tile, key split).
 // The index sweep (index_sweep.h) stages 32 blocks of maxima at a time.  Each
-// (row, KV head) list belongs to one lane, which keeps its count and threshold
-// in registers, walks its row's staged maxima in ascending block order and
-// appends the candidates above its threshold to its per-split list in the
-// workspace.  A list that could overflow on the next flush is compacted to
-// the best k-1 by the whole wave (select.h): copied into an idle 8 KiB index-K
-// tile buffer of LDS (2 KiB per wave, lists of up to 256 entries), compacted
-// there and the survivors written back; longer lists are compacted in place.  Splits of the key range fill the GPU when there
-// are few tiles; split s of every tile runs on the same XCD (work-group ids are
-// dealt round-robin over the 8 XCDs), so that XCD's L2 serves one key range.
+// (row, KV head) list lives in the workspace as packed (key, block) words in
+// ascending block order; lane `row` of wave h keeps its count and threshold
+// in registers.  At each flush the wave takes its 64 lists two at a time, one
+// per half-wave: the 32 staged maxima of a list are tested against its
+// threshold and the survivors appended contiguously (ballot prefix counts),
+// so one store instruction writes a run of one list rather than one entry of
+// 64 lists.  A list that could overflow on the next flush is compacted in
+// place to the best k-1 by the whole wave (select.h), which also raises its
+// threshold.  Splits of the key range fill the GPU when there are few tiles;
+// split s of every tile runs on the same XCD (work-group ids are dealt
+// round-robin over the 8 XCDs), so that XCD's L2 serves one key range.
 // Pass 2 (fused_merge_kernel): one wave per list merges the splits' lists
-// (each ascending, ranges ascending) with the same compaction, appends the
+// (each ascending, ranges ascending) with the same selection, appends the
 // own block and writes the ascending selection.
 #include "common.h"
 #include "index_sweep.h"
@@ -34,8 +36,7 @@ struct FusedArgs {
   const uint16_t* iq;
   const uint16_t* ik;
   int32_t* sel;       // [B][Hkv][Sq][k]
-  uint32_t* wkeys;    // [S][B*Hkv*Sq][cap]
-  int32_t* widx;      // [S][B*Hkv*Sq][cap]
+  uint64_t* went;     // [S][B*Hkv*Sq][cap] packed candidates (pack_cand)
   int32_t* wcnt;      // [S][B*Hkv*Sq]
   int B, Sq, Skv, q_start, Hkv, nsplit, ntiles, k, cap;
 };
@@ -46,7 +47,7 @@ __host__ __device__ inline int fused_cap(int k) { return 64 * ((k - 1 + 128 + 63
 
 template <int HKV, int MAXE>
 __global__ void __launch_bounds__(256) fused_sweep_kernel(FusedArgs a) {
-  __shared__ IndexLds lds;
+  __shared__ IndexLds<> lds;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int s = blockIdx.x % a.nsplit;
   const int tile = a.ntiles - 1 - blockIdx.x / a.nsplit;  // late (long) tiles first
@@ -58,85 +59,70 @@ __global__ void __launch_bounds__(256) fused_sweep_kernel(FusedArgs a) {
   const int cend = (int)((long long)(s + 1) * cur_last / a.nsplit);
   const int m = a.k - 1;  // candidates kept per list (own block excluded)
   const long long nlist = (long long)a.B * HKV * a.Sq;
-  // Lane `lane` of wave h < HKV owns the list of (KV head h, row lane): its
-  // count and threshold live in registers, its entries in the workspace.
-  const int h = wave, row = lane;
-  const bool owner = wave < HKV && row < rows;
-  const int cur_row = (a.q_start + t0 + row) / kBlock;
-  auto list_base = [&](int r) {
-    return ((long long)s * nlist + ((long long)b * HKV + h) * a.Sq + t0 + r) * a.cap;
-  };
+  // Wave h < HKV handles the lists of KV head h; lane r holds the count and
+  // threshold of row r's list.
+  const int h = wave;
+  uint64_t* const tile_lists =
+      a.went + ((long long)s * nlist + ((long long)b * HKV + h) * a.Sq + t0) * a.cap;
   uint32_t thr = 0;
   int cnt = 0;
 
-  // Compacts the list of lane l of this wave (n entries) to its best m and
-  // returns the new threshold; spare: 8 KiB of idle LDS (2 KiB per wave).
-  auto compact = [&](int l, int n, u32x4* spare) {
-    const long long lb = list_base(l);
-    // the list's entries were stored by lane l: make them visible to the wave
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    uint32_t t;
-    if (a.cap <= 256) {
-      uint32_t* sk = reinterpret_cast<uint32_t*>(spare) + wave * 512;
-      int32_t* si = reinterpret_cast<int32_t*>(sk + 256);
-      for (int i = lane; i < n; i += kWave) {
-        sk[i] = a.wkeys[lb + i];
-        si[i] = a.widx[lb + i];
-      }
-      __builtin_amdgcn_wave_barrier();
-      t = wave_compact_topm<MAXE>(sk, si, n, m);
-      for (int i = lane; i < m; i += kWave) {
-        a.wkeys[lb + i] = sk[i];
-        a.widx[lb + i] = si[i];
-      }
-      __builtin_amdgcn_wave_barrier();
-    } else {
-      t = wave_compact_topm<MAXE>(a.wkeys + lb, a.widx + lb, n, m);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    return t;
-  };
   // compacts every list of this wave holding more than `limit` entries
-  auto compact_over = [&](int limit, u32x4* spare) {
-    uint64_t over = ballot(owner && cnt > limit);
+  auto compact_over = [&](int limit) {
+    uint64_t over = ballot(lane < rows && cnt > limit);
+    if (over == 0ull) return;
+    // the entries were stored by other lanes of this wave: make them visible
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     while (over != 0ull) {
       const int l = __builtin_ctzll(over);
       over &= over - 1;
       const int n = __builtin_amdgcn_readlane(cnt, l);
-      const uint32_t t = compact(l, n, spare);
+      const uint32_t t = wave_compact_topm_packed<MAXE>(tile_lists + (long long)l * a.cap, n, m);
       if (lane == l) {
         thr = t;
         cnt = m;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   };
 
   if (m > 0) {
+    const int half = lane / 32, e = lane % 32;
     index_sweep(IndexTile{a.iq, a.ik, b, t0, rows, a.Sq, a.Skv}, cbeg, cend, lds,
-                [&](int c0, int len, u32x4* spare) {
+                [&](int c0, int len, u32x4*) {
       if (wave >= HKV) return;
-      // each owning lane streams the staged maxima of its row, ascending
-      for (int e = 0; e < len; ++e) {
-        const int c = c0 + e;
-        float v = lds.stage[h][row][e];
+      const int c = c0 + e;
+      // rows 2p (lanes 0-31) and 2p+1 (lanes 32-63); column e of the stage
+      for (int p = 0; p < kTileRows / 2; ++p) {
+        const int r = 2 * p + half;
+        float v = lds.stage[h][r][e];
 #pragma unroll
-        for (int j = 1; j < kIdxHeads / HKV; ++j) v = fmaxf(v, lds.stage[h + j * HKV][row][e]);
+        for (int j = 1; j < kIdxHeads / HKV; ++j) v = fmaxf(v, lds.stage[h + j * HKV][r][e]);
         const uint32_t key = score_key(v);
-        if (owner && c < cur_row && key > thr) {
-          const long long lb = list_base(row);
-          a.wkeys[lb + cnt] = key;
-          a.widx[lb + cnt] = c;
-          ++cnt;
+        const int cnt0 = __builtin_amdgcn_readlane(cnt, 2 * p);
+        const int cnt1 = __builtin_amdgcn_readlane(cnt, 2 * p + 1);
+        const uint32_t thr0 = __builtin_amdgcn_readlane(thr, 2 * p);
+        const uint32_t thr1 = __builtin_amdgcn_readlane(thr, 2 * p + 1);
+        const int cur_r = (a.q_start + t0 + r) / kBlock;
+        const bool take = e < len && r < rows && c < cur_r && key > (half ? thr1 : thr0);
+        const uint64_t bal = ballot(take);
+        const int n0 = __popc((uint32_t)bal), n1 = __popc((uint32_t)(bal >> 32));
+        if (take) {
+          const int pos = (half ? cnt1 - n0 : cnt0) + prefix_count(bal);
+          tile_lists[(long long)r * a.cap + pos] = pack_cand(key, c);
         }
+        if (lane == 2 * p) cnt += n0;
+        if (lane == 2 * p + 1) cnt += n1;
       }
       // a list takes at most kStageCols entries per flush
-      compact_over(a.cap - kStageCols, spare);
+      compact_over(a.cap - kStageCols);
     });
   }
   // the list goes to the merge as it stands (up to cap entries, ascending)
-  if (owner) a.wcnt[(long long)s * nlist + ((long long)b * HKV + h) * a.Sq + t0 + row] = cnt;
+  if (wave < HKV && lane < rows)
+    a.wcnt[(long long)s * nlist + ((long long)b * HKV + h) * a.Sq + t0 + lane] = cnt;
 }
 
 template <int MAXE>
@@ -157,13 +143,13 @@ __global__ void __launch_bounds__(256) fused_merge_kernel(FusedArgs a) {
     if (m > 0) {
       for (int s = 0; s < a.nsplit; ++s) {
         const int n = a.wcnt[(long long)s * nlist + L];
-        const long long base = ((long long)s * nlist + L) * a.cap;
+        const uint64_t* src = a.went + ((long long)s * nlist + L) * a.cap;
         for (int off = 0; off < n; off += kWave) {
           const int i = off + lane;
           const bool ok = i < n;
-          const uint32_t key = ok ? a.wkeys[base + i] : 0u;
-          const int32_t idx = ok ? a.widx[base + i] : 0;
-          cnt = wave_append(keys, idxs, cnt, ok && key > thr, key, idx);
+          const uint64_t v = ok ? src[i] : 0ull;
+          const uint32_t key = (uint32_t)(v >> 32);
+          cnt = wave_append(keys, idxs, cnt, ok && key > thr, key, (int32_t)(uint32_t)v);
           if (cnt > CAP - kWave) {
             thr = wave_compact_topm<MAXE>(keys, idxs, cnt, m);
             cnt = m;
@@ -225,11 +211,9 @@ hipError_t launch_index_topk_fused(const Shape& s, const void* iq, const void* i
   const int nsplit = fused_nsplit(s);
   const size_t nlist = (size_t)s.B * s.Hkv * s.Sq;
   const int cap = fused_cap(s.top_k);
-  uint32_t* wkeys = static_cast<uint32_t*>(ws);
-  int32_t* widx = reinterpret_cast<int32_t*>(wkeys + (size_t)nsplit * nlist * cap);
-  int32_t* wcnt = widx + (size_t)nsplit * nlist * cap;
-  FusedArgs a{static_cast<const uint16_t*>(iq), static_cast<const uint16_t*>(ik), sel, wkeys, widx,
-              wcnt, s.B, s.Sq, s.Skv, s.q_start, s.Hkv, nsplit, ceil_div(s.Sq, kTileRows),
+  uint64_t* went = static_cast<uint64_t*>(ws);
+  int32_t* wcnt = reinterpret_cast<int32_t*>(went + (size_t)nsplit * nlist * cap);
+  FusedArgs a{static_cast<const uint16_t*>(iq), static_cast<const uint16_t*>(ik), sel, went, wcnt, s.B, s.Sq, s.Skv, s.q_start, s.Hkv, nsplit, ceil_div(s.Sq, kTileRows),
               s.top_k, cap};
   switch (s.Hkv) {
     case 1: return launch_hkv<1>(s, a, st);

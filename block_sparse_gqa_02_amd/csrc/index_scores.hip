@@ -40,7 +40,7 @@ struct IndexArgs {
 template <int HKV>
 __global__ void __launch_bounds__(256)
 index_scores_prefill_kernel(IndexArgs a) {
-  __shared__ IndexLds lds;
+  __shared__ IndexLds<> lds;
   const int tile = gridDim.x - 1 - blockIdx.x;  // late (long) tiles first
   const int b = blockIdx.y;
   const int tid = threadIdx.x;

@@ -15,12 +15,12 @@
 namespace msa {
 
 constexpr int kTileRows = 64;   // query rows per work-group
-constexpr int kStageCols = 32;  // blocks staged before the consumer runs
-constexpr int kStagePad = kStageCols + 1;
+constexpr int kStageCols = 32;  // blocks staged before the consumer runs (default)
 
+template <int SC = kStageCols>
 struct IndexLds {
   u32x4 ktile[2][64 * 8];                          // 2 x 8 KiB index-K tiles
-  float stage[kIdxHeads][kTileRows][kStagePad];    // block maxima per (head, row, block)
+  float stage[kIdxHeads][kTileRows][SC + 1];       // block maxima per (head, row, block)
 };
 
 // Swizzled 16-byte slot of chunk `ch` (0..7) of key row `key`: the 32-lane
@@ -33,15 +33,15 @@ struct IndexTile {
   int b, t0, rows, Sq, Skv;
 };
 
-// Sweeps blocks [cbeg, cend) for the tile.  After every kStageCols blocks (and
+// Sweeps blocks [cbeg, cend) for the tile.  After every SC blocks (and
 // at the end) all threads call flush(c0, len, spare) with stage[i][row][e]
 // holding the max over block c0+e's keys of head i's scores for row t0+row;
 // `spare` is an 8 KiB index-K tile buffer that nothing reads or writes until
 // flush returns (scratch for the consumer).  Must be called by all 256
 // threads; contains barriers.
-template <typename Flush>
-__device__ __forceinline__ void index_sweep(const IndexTile& T, int cbeg, int cend, IndexLds& L,
-                                            Flush&& flush) {
+template <int SC, typename Flush>
+__device__ __forceinline__ void index_sweep(const IndexTile& T, int cbeg, int cend,
+                                            IndexLds<SC>& L, Flush&& flush) {
   const int tid = threadIdx.x;
   const int wave = tid / kWave;  // index head
   const int lane = tid % kWave;
@@ -114,7 +114,7 @@ __device__ __forceinline__ void index_sweep(const IndexTile& T, int cbeg, int ce
 
     if (more) store_tile(buf ^ 1);
     __syncthreads();
-    if (c + 1 - c0 == kStageCols || !more) {
+    if (c + 1 - c0 == SC || !more) {
       flush(c0, c + 1 - c0, &L.ktile[buf][0]);
       c0 = c + 1;
       __syncthreads();

@@ -34,24 +34,21 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return v;
 }
 
-// Compacts entries [0, n) of (keys, idxs) (any address space, ascending idx
-// order, n > m >= 1, n <= 64 * MAXE) in place to the m entries with the
-// largest (key, -idx), preserving order.  Returns the m-th largest key: a later
-// candidate (higher idx) can only enter the top m if its key is larger.
-// Must be called by all 64 lanes of a wave with uniform arguments.
-template <int MAXE, typename KP, typename IP>
-__device__ __forceinline__ uint32_t wave_compact_topm(KP keys, IP idxs, int n, int m) {
+// Selection core on a wave's registers: entry e * 64 + lane (< n) is
+// (kr[e], ir[e]), ascending idx order, n > m >= 1, n <= 64 * MAXE.  Calls
+// put(d, key, idx) for the m entries with the largest (key, -idx), d = 0..m-1
+// in their original order, and returns the m-th largest key: a later candidate
+// (higher idx) can only enter the top m if its key is larger.  Must be called
+// by all 64 lanes of a wave with uniform n, m.
+template <int MAXE, typename Put>
+__device__ __forceinline__ uint32_t wave_topm_regs(const uint32_t (&kr)[MAXE],
+                                                   const int32_t (&ir)[MAXE], int n, int m,
+                                                   Put&& put) {
   const int lane = lane_id();
-  uint32_t kr[MAXE];
-  int32_t ir[MAXE];
   uint32_t mx = 0, mn = 0xffffffffu;
 #pragma unroll
   for (int e = 0; e < MAXE; ++e) {
-    const int i = e * kWave + lane;
-    const bool ok = i < n;
-    kr[e] = ok ? keys[i] : 0u;
-    ir[e] = ok ? idxs[i] : 0;
-    if (ok) {
+    if (e * kWave + lane < n) {
       mx = max(mx, kr[e]);
       mn = min(mn, kr[e]);
     }
@@ -89,16 +86,57 @@ __device__ __forceinline__ uint32_t wave_compact_topm(KP keys, IP idxs, int n, i
     const uint64_t eqm = ballot(eq);
     const bool keep = gt || (eq && eq_seen + prefix_count(eqm) < take_equal);
     const uint64_t km = ballot(keep);
-    if (keep) {
-      const int d = out + prefix_count(km);
-      keys[d] = kr[e];
-      idxs[d] = ir[e];
-    }
+    if (keep) put(out + prefix_count(km), kr[e], ir[e]);
     out += __popcll(km);
     eq_seen += __popcll(eqm);
   }
   __builtin_amdgcn_wave_barrier();
   return V;
+}
+
+// Compacts entries [0, n) of (keys, idxs) (any address space, ascending idx
+// order, n > m >= 1, n <= 64 * MAXE) in place to the m entries with the
+// largest (key, -idx), preserving order; returns the m-th largest key.
+template <int MAXE, typename KP, typename IP>
+__device__ __forceinline__ uint32_t wave_compact_topm(KP keys, IP idxs, int n, int m) {
+  const int lane = lane_id();
+  uint32_t kr[MAXE];
+  int32_t ir[MAXE];
+#pragma unroll
+  for (int e = 0; e < MAXE; ++e) {
+    const int i = e * kWave + lane;
+    const bool ok = i < n;
+    kr[e] = ok ? keys[i] : 0u;
+    ir[e] = ok ? idxs[i] : 0;
+  }
+  __builtin_amdgcn_wave_barrier();
+  return wave_topm_regs<MAXE>(kr, ir, n, m, [&](int d, uint32_t k, int32_t i) {
+    keys[d] = k;
+    idxs[d] = i;
+  });
+}
+
+// Packed candidate: the key in the high word, the block index in the low word.
+__device__ __forceinline__ uint64_t pack_cand(uint32_t key, int32_t idx) {
+  return ((uint64_t)key << 32) | (uint32_t)idx;
+}
+
+// wave_compact_topm over a packed list (pack_cand entries) in global memory.
+template <int MAXE>
+__device__ __forceinline__ uint32_t wave_compact_topm_packed(uint64_t* ents, int n, int m) {
+  const int lane = lane_id();
+  uint32_t kr[MAXE];
+  int32_t ir[MAXE];
+#pragma unroll
+  for (int e = 0; e < MAXE; ++e) {
+    const int i = e * kWave + lane;
+    const uint64_t v = i < n ? ents[i] : 0ull;
+    kr[e] = (uint32_t)(v >> 32);
+    ir[e] = (int32_t)(uint32_t)v;
+  }
+  return wave_topm_regs<MAXE>(kr, ir, n, m, [&](int d, uint32_t k, int32_t i) {
+    ents[d] = pack_cand(k, i);
+  });
 }
 
 // Appends this lane's candidate (if `pass`) at the end of a list of length
