@@ -41,9 +41,16 @@ struct FusedArgs {
   int B, Sq, Skv, q_start, Hkv, nsplit, ntiles, k, cap;
 };
 
-// Candidate-list capacity: keep k-1 (the own block is added at the end) plus
-// room for at least two 32-wide staging chunks between compactions.
-__host__ __device__ inline int fused_cap(int k) { return 64 * ((k - 1 + 128 + 63) / 64); }
+constexpr int kFusedMaxE = 8;  // list capacity at most 8 x 64 entries
+
+// Candidate-list capacity: k-1 (the own block is added at the end) plus at
+// least 257 more entries.  A split of n blocks streams about k (1 + ln(n / k))
+// candidates past its running threshold, so at k = 64..128 and splits of about
+// a thousand blocks a list is compacted about once, when it first fills.
+__host__ __device__ inline int fused_cap(int k) {
+  const int c = 64 * ((k - 1 + 257 + 63) / 64);
+  return c < 64 * kFusedMaxE ? c : 64 * kFusedMaxE;
+}
 
 template <int HKV, int MAXE>
 __global__ void __launch_bounds__(256) fused_sweep_kernel(FusedArgs a) {
@@ -138,6 +145,30 @@ __global__ void __launch_bounds__(256) fused_merge_kernel(FusedArgs a) {
   for (long long L = (long long)blockIdx.x * 4 + wave; L < nlist; L += (long long)gridDim.x * 4) {
     const int t = (int)(L % a.Sq);
     const int cur = (a.q_start + t) / kBlock;
+    int32_t* dst = a.sel + L * a.k;
+    if (a.nsplit == 1 && m > 0) {
+      // one split: its list (ascending, at most cap = 64 * MAXE entries) is
+      // selected straight from registers into the output
+      const int n = a.wcnt[L];
+      const uint64_t* src = a.went + L * a.cap;
+      if (n > m) {
+        uint32_t kr[MAXE];
+        int32_t ir[MAXE];
+#pragma unroll
+        for (int e = 0; e < MAXE; ++e) {
+          const int i = e * kWave + lane;
+          const uint64_t v = i < n ? src[i] : 0ull;
+          kr[e] = (uint32_t)(v >> 32);
+          ir[e] = (int32_t)(uint32_t)v;
+        }
+        wave_topm_regs<MAXE>(kr, ir, n, m, [&](int d, uint32_t, int32_t i) { dst[d] = i; });
+        if (lane == 0) dst[m] = cur;
+      } else {
+        for (int i = lane; i < a.k; i += kWave)
+          dst[i] = i < n ? (int32_t)(uint32_t)src[i] : (i == n ? cur : -1);
+      }
+      continue;
+    }
     int cnt = 0;
     uint32_t thr = 0;
     if (m > 0) {
@@ -161,7 +192,6 @@ __global__ void __launch_bounds__(256) fused_merge_kernel(FusedArgs a) {
         cnt = m;
       }
     }
-    int32_t* dst = a.sel + L * a.k;
     for (int i = lane; i < a.k; i += kWave) dst[i] = i < cnt ? idxs[i] : (i == cnt ? cur : -1);
     __builtin_amdgcn_wave_barrier();
   }
@@ -181,19 +211,23 @@ hipError_t launch_hkv(const Shape& s, const FusedArgs& a, hipStream_t st) {
   dim3 g1(a.ntiles * a.nsplit, s.B);
   const long long nlist = (long long)s.B * s.Hkv * s.Sq;
   const int g2 = (int)std::min<long long>((nlist + 3) / 4, 16384);
-  const int cap = a.cap;
-  if (cap <= 192) {
-    fused_sweep_kernel<HKV, 3><<<g1, 256, 0, st>>>(a);
-    fused_merge_kernel<3><<<g2, 256, 0, st>>>(a);
-  } else if (cap <= 256) {
-    fused_sweep_kernel<HKV, 4><<<g1, 256, 0, st>>>(a);
-    fused_merge_kernel<4><<<g2, 256, 0, st>>>(a);
-  } else if (cap <= 320) {
-    fused_sweep_kernel<HKV, 5><<<g1, 256, 0, st>>>(a);
-    fused_merge_kernel<5><<<g2, 256, 0, st>>>(a);
-  } else {
-    fused_sweep_kernel<HKV, 6><<<g1, 256, 0, st>>>(a);
-    fused_merge_kernel<6><<<g2, 256, 0, st>>>(a);
+  // cap is a multiple of 64 in [128, 64 * kFusedMaxE]
+  switch (a.cap / kWave) {
+#define MSA_FUSED_CASE(E)                                 \
+  case E:                                                 \
+    fused_sweep_kernel<HKV, E><<<g1, 256, 0, st>>>(a);    \
+    fused_merge_kernel<E><<<g2, 256, 0, st>>>(a);         \
+    break;
+    MSA_FUSED_CASE(2)
+    MSA_FUSED_CASE(3)
+    MSA_FUSED_CASE(4)
+    MSA_FUSED_CASE(5)
+    MSA_FUSED_CASE(6)
+    MSA_FUSED_CASE(7)
+    MSA_FUSED_CASE(8)
+#undef MSA_FUSED_CASE
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -23,23 +23,32 @@
 
 namespace msa {
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
+// Wave-wide max / min of a uint32, returned as a wave-uniform (scalar) value:
+// DPP steps within each 16-lane row (swap neighbours, swap pairs, mirror within
+// 8 and within 16 lanes), then v_permlane16_swap and v_permlane32_swap across
+// rows.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_uniform(uint32_t v) {
+  auto op = [](uint32_t x, uint32_t y) { return MAX ? max(x, y) : min(x, y); };
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(r[0], r[1]);
+  r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = op(r[0], r[1]);
+  return __builtin_amdgcn_readfirstlane(v);
 }
 
 // Selection core on a wave's registers: entry e * 64 + lane (< n) is
-// (kr[e], ir[e]), ascending idx order, n > m >= 1, n <= 64 * MAXE.  Calls
-// put(d, key, idx) for the m entries with the largest (key, -idx), d = 0..m-1
-// in their original order, and returns the m-th largest key: a later candidate
-// (higher idx) can only enter the top m if its key is larger.  Must be called
-// by all 64 lanes of a wave with uniform n, m.
+// (kr[e], ir[e]), ascending idx order, n > m >= 1, n <= 64 * MAXE; real keys
+// are nonzero (score_key of a non-NaN score, or the own block's all-ones key)
+// and slots at or beyond n hold key 0.  Calls put(d, key, idx) for the m
+// entries with the largest (key, -idx), d = 0..m-1 in their original order,
+// and returns the m-th largest key: a later candidate (higher idx) can only
+// enter the top m if its key is larger.  Must be called by all 64 lanes of a
+// wave with uniform n, m.
 template <int MAXE, typename Put>
 __device__ __forceinline__ uint32_t wave_topm_regs(const uint32_t (&kr)[MAXE],
                                                    const int32_t (&ir)[MAXE], int n, int m,
@@ -48,16 +57,15 @@ __device__ __forceinline__ uint32_t wave_topm_regs(const uint32_t (&kr)[MAXE],
   uint32_t mx = 0, mn = 0xffffffffu;
 #pragma unroll
   for (int e = 0; e < MAXE; ++e) {
-    if (e * kWave + lane < n) {
-      mx = max(mx, kr[e]);
-      mn = min(mn, kr[e]);
-    }
+    mx = max(mx, kr[e]);
+    if (e * kWave + lane < n) mn = min(mn, kr[e]);
   }
-  mx = wave_max_u32(mx);
-  mn = wave_min_u32(mn);
+  mx = wave_reduce_uniform<true>(mx);
+  mn = wave_reduce_uniform<false>(mn);
   uint32_t V = mx;
   if (mx != mn) {
-    // every candidate shares the bits of mx above the highest differing bit
+    // every candidate shares the bits of mx above the highest differing bit;
+    // the zero padding never reaches a threshold T >= 1
     const int top = 31 - __builtin_clz(mx ^ mn);
     const uint32_t low = (top == 31) ? 0xffffffffu : ((2u << top) - 1u);
     V = mx & ~low;
@@ -65,24 +73,22 @@ __device__ __forceinline__ uint32_t wave_topm_regs(const uint32_t (&kr)[MAXE],
       const uint32_t T = V | (1u << bit);
       int cnt = 0;
 #pragma unroll
-      for (int e = 0; e < MAXE; ++e)
-        if (e * kWave < n) cnt += __popcll(ballot(e * kWave + lane < n && kr[e] >= T));
+      for (int e = 0; e < MAXE; ++e) cnt += __popcll(ballot(kr[e] >= T));
       if (cnt >= m) V = T;
     }
   }
+  // V is a real key, so the padding is neither above nor equal to it
   int greater = 0;
 #pragma unroll
-  for (int e = 0; e < MAXE; ++e)
-    if (e * kWave < n) greater += __popcll(ballot(e * kWave + lane < n && kr[e] > V));
+  for (int e = 0; e < MAXE; ++e) greater += __popcll(ballot(kr[e] > V));
   const int take_equal = m - greater;
   __builtin_amdgcn_wave_barrier();
   int out = 0, eq_seen = 0;
 #pragma unroll
   for (int e = 0; e < MAXE; ++e) {
     if (e * kWave >= n) break;
-    const bool ok = e * kWave + lane < n;
-    const bool gt = ok && kr[e] > V;
-    const bool eq = ok && kr[e] == V;
+    const bool gt = kr[e] > V;
+    const bool eq = kr[e] == V;
     const uint64_t eqm = ballot(eq);
     const bool keep = gt || (eq && eq_seen + prefix_count(eqm) < take_equal);
     const uint64_t km = ballot(keep);
