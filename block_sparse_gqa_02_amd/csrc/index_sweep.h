@@ -65,26 +65,35 @@ __device__ __forceinline__ void index_sweep(const IndexTile& T, int cbeg, int ce
   }
 
   const u32x4* ikb = reinterpret_cast<const u32x4*>(T.ik + (size_t)T.b * T.Skv * kIdxDim);
-  u32x4 r0, r1;
-  auto load_tile = [&](int c) {
+  // Index-K blocks travel through registers two blocks ahead of the MFMAs
+  // (two register sets that swap roles every block) and through LDS one
+  // block ahead (double-buffered tiles).
+  struct Regs { u32x4 r0, r1; };
+  auto load_tile = [&](int c, Regs& R) {
     const u32x4* src = ikb + (size_t)c * (kBlock * 8);
-    r0 = src[tid];
-    r1 = src[tid + 256];
+    R.r0 = src[tid];
+    R.r1 = src[tid + 256];
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, const Regs& R) {
     const int q0 = tid, q1 = tid + 256;
-    L.ktile[buf][ktile_slot(q0 / 8, q0 % 8)] = r0;
-    L.ktile[buf][ktile_slot(q1 / 8, q1 % 8)] = r1;
+    L.ktile[buf][ktile_slot(q0 / 8, q0 % 8)] = R.r0;
+    L.ktile[buf][ktile_slot(q1 / 8, q1 % 8)] = R.r1;
   };
 
-  load_tile(cbeg);
-  store_tile(0);
+  Regs RA, RB;
+  load_tile(cbeg, RA);
+  store_tile(0, RA);
+  // the loads ahead are unconditional (clamped to the last block) so that
+  // every path has the same loads in flight and the waits stay precise
+  load_tile(min(cbeg + 1, cend - 1), RA);
   __syncthreads();
   int c0 = cbeg;
-  for (int c = cbeg; c < cend; ++c) {
+  // block c: its tile is in LDS buffer (c - cbeg) & 1, block c + 1 is in
+  // `next`, and block c + 2 is loaded into `ahead`
+  auto step = [&](int c, Regs& next, Regs& ahead) {
     const int buf = (c - cbeg) & 1;
     const bool more = c + 1 < cend;
-    if (more) load_tile(c + 1);
+    load_tile(min(c + 2, cend - 1), ahead);
 
     f32x16 acc[2][2];
 #pragma unroll
@@ -112,14 +121,20 @@ __device__ __forceinline__ void index_sweep(const IndexTile& T, int cbeg, int ce
     // lane l now holds the block max of row l for head `wave`
     L.stage[wave][lane][c - c0] = halves_max(m0, m1);
 
-    if (more) store_tile(buf ^ 1);
+    if (more) store_tile(buf ^ 1, next);
     __syncthreads();
     if (c + 1 - c0 == SC || !more) {
       flush(c0, c + 1 - c0, &L.ktile[buf][0]);
       c0 = c + 1;
       __syncthreads();
     }
+  };
+  int c = cbeg;
+  for (; c + 1 < cend; c += 2) {
+    step(c, RA, RB);
+    step(c + 1, RB, RA);
   }
+  if (c < cend) step(c, RA, RB);
 }
 
 }  // namespace msa
