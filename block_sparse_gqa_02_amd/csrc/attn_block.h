@@ -69,29 +69,73 @@ struct WaveAttn {
   // The same with the block's 64 K and V rows at k_blk / v_blk (a cache page).
   __device__ __forceinline__ void block_at(const uint16_t* k_blk, const uint16_t* v_blk, int c,
                                            int pos, float scale_log2, u32x4* vlds) {
-    const int lane = lane_id(), n = lane % 16, g = lane / 16;
-    const u32x4* kb = reinterpret_cast<const u32x4*>(k_blk);
-    const u32x4* vb = reinterpret_cast<const u32x4*>(v_blk);
-    // Rows past pos (only in the own block, which may also run past the end of
-    // the cache) are read from row pos instead and masked below.
+    u32x4 vr[16], kr[4][4];
     const int last = min(pos - c * kBlock, kBlock - 1);
-    // V block -> LDS (1024 chunks of 16 B; chunk q = key q/16, dim chunk q%16)
-    u32x4 vr[16];
+    load_v(v_blk, last, vr);
+    load_k(k_blk, last, kr);
+    store_v(vr, vlds);
+    attend(kr, c, pos, scale_log2, vlds, [] {}, [] {});
+  }
+
+  // The phases of block_at, for callers that overlap one block's loads with
+  // the previous block's arithmetic.  Rows past `last` (= min(pos - 64c, 63);
+  // only in the own block, which may also run past the end of the cache) are
+  // read from row `last` instead and masked in attend().
+  __device__ __forceinline__ static void load_v(const uint16_t* v_blk, int last, u32x4 (&vr)[16]) {
+    const int lane = lane_id();
+    const u32x4* vb = reinterpret_cast<const u32x4*>(v_blk);
+    // V block: 1024 chunks of 16 B; chunk q = key q/16, dim chunk q%16
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       const int q = s * kWave + lane;
       vr[s] = vb[min(q / 16, last) * 16 + q % 16];
     }
-    u32x4 kr[4][4];
+  }
+  __device__ __forceinline__ static void load_k(const uint16_t* k_blk, int last,
+                                                u32x4 (&kr)[4][4]) {
+    const int lane = lane_id(), n = lane % 16, g = lane / 16;
+    const u32x4* kb = reinterpret_cast<const u32x4*>(k_blk);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kr[mt][ks] = kb[min(16 * mt + n, last) * 16 + 4 * ks + g];
+  }
+  // The V block straight into an LDS tile (laid out as store_v lays it out)
+  // with 16-byte LDS-bound loads: load t writes slots 64t .. 64t+63, so lane
+  // i fetches the chunk that belongs at slot 64t + i.  The data is in LDS once
+  // these 16 loads have completed (vmcnt).
+  __device__ __forceinline__ static void load_v_lds(const uint16_t* v_blk, int last, u32x4* tile) {
+    const int lane = lane_id();
+    const u32x4* vb = reinterpret_cast<const u32x4*>(v_blk);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int slot = t * kWave + lane;
+      const int key = slot >> 4;
+      const int ch = (slot & 15) ^ (((key >> 2) & 1) << 3);  // vtile_slot is its own inverse
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vb + min(key, last) * 16 + ch),
+                                       (__attribute__((address_space(3))) void*)(tile + t * kWave),
+                                       16, 0, 0);
+    }
+  }
+  // Copies the V block into this wave's LDS tile.  The previous block's reads
+  // of the tile must be complete (attend() ends with them).
+  __device__ __forceinline__ static void store_v(const u32x4 (&vr)[16], u32x4* vlds) {
+    const int lane = lane_id();
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       const int q = s * kWave + lane;
       vlds[vtile_slot(q / 16, q % 16)] = vr[s];
     }
+  }
+
+  // Attends block c from K in registers and V in the LDS tile; after_s() runs
+  // once the S products have taken their K operands (kr may then be reloaded),
+  // before_pv() right before the first read of the V tile.
+  template <typename AfterS, typename BeforePV>
+  __device__ __forceinline__ void attend(const u32x4 (&kr)[4][4], int c, int pos,
+                                         float scale_log2, const u32x4* vlds, AfterS&& after_s,
+                                         BeforePV&& before_pv) {
+    const int lane = lane_id(), n = lane % 16, g = lane / 16;
     // S^T = K Q^T
     f32x4 sc[4];
 #pragma unroll
@@ -100,6 +144,7 @@ struct WaveAttn {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) sc[mt] = mfma16(as_bf16x8(kr[mt][ks]), qf[ks], sc[mt]);
     }
+    after_s();
     // online softmax (log2 domain); keys beyond pos are masked
     const int key0 = c * kBlock + 4 * g;
     const bool partial = c * kBlock + kBlock - 1 > pos;
@@ -130,6 +175,7 @@ struct WaveAttn {
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] *= alpha;
     __builtin_amdgcn_wave_barrier();  // V tile writes above precede the reads below
+    before_pv();
     // O^T += V^T P^T
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {

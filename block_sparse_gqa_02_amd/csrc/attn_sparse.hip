@@ -89,8 +89,18 @@ struct DecodeArgs {
   int num_pages, nblk;
 };
 
+// s_waitcnt vmcnt(N) (N in {0, 32}; expcnt and lgkmcnt unconstrained: vmcnt
+// bits 3:0 and 15:14), fenced against compiler reordering of memory accesses.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N == 0 || N == 32, "encoded counts");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(N == 0 ? 0xf70 : (0xf70 | (2 << 14)));
+  asm volatile("" ::: "memory");
+}
+
 __global__ void __launch_bounds__(256) decode_partial_kernel(DecodeArgs a) {
-  __shared__ u32x4 vtile[kAttnWaves][kBlock * 16];
+  __shared__ u32x4 vtile[kAttnWaves][2][kBlock * 16];  // 128 KiB
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int split = blockIdx.x * kAttnWaves + wave;
@@ -102,24 +112,69 @@ __global__ void __launch_bounds__(256) decode_partial_kernel(DecodeArgs a) {
   WaveAttn st;
   st.init();
   st.load_q(a.q + ((size_t)b * a.Hq + hq0) * kHeadDim, a.G);
-  const uint16_t* kh = a.k + ((size_t)b * a.Hkv + h) * a.Skv * kHeadDim;
-  const uint16_t* vh = a.v + ((size_t)b * a.Hkv + h) * a.Skv * kHeadDim;
   const int rbeg = split * a.per_split;
   const int rend = a.sel ? min(rbeg + a.per_split, a.top_k) : min(rbeg + a.per_split, cur + 1);
   const int32_t* list = a.sel ? a.sel + ((size_t)b * a.Hkv + h) * a.top_k : nullptr;
-  for (int r = rbeg; r < rend; ++r) {
-    const int c = list ? list[r] : r;
-    if (c < 0 || c > cur) continue;
-    if (a.pages) {
-      // block c of this sequence is page pg of the pools ([page][Hkv][64][128]);
-      // ids outside the pool are skipped, never read
-      const int pg = a.pages[(size_t)b * a.nblk + c];
-      if (pg < 0 || pg >= a.num_pages) continue;
-      const size_t off = ((size_t)pg * a.Hkv + h) * kBlock * kHeadDim;
-      st.block_at(a.k + off, a.v + off, c, pos, a.scale_log2, vtile[wave]);
-    } else {
-      st.block(kh, vh, c, pos, a.scale_log2, vtile[wave]);
+  // Lane j < per_split looks up entry rbeg + j: its block c and the element
+  // offset of that block's K/V rows.  Ids outside [0, cur] and, with paged
+  // caches, pages outside the pool are skipped, never read.
+  int c_l = 0;
+  long long off_l = 0;
+  bool ok_l = false;
+  if (lane < a.per_split && rbeg + lane < rend) {
+    c_l = list ? list[rbeg + lane] : rbeg + lane;
+    ok_l = c_l >= 0 && c_l <= cur;
+    if (ok_l && a.pages) {
+      // block c of this sequence is page pg of the pools ([page][Hkv][64][128])
+      const int pg = a.pages[(size_t)b * a.nblk + c_l];
+      ok_l = pg >= 0 && pg < a.num_pages;
+      off_l = ((long long)pg * a.Hkv + h) * kBlock * kHeadDim;
+    } else if (ok_l) {
+      off_l = (((long long)b * a.Hkv + h) * a.Skv + (long long)c_l * kBlock) * kHeadDim;
     }
+  }
+  uint64_t todo = ballot(ok_l);
+  if (todo != 0ull) {
+    // Blocks in entry order; block i+1's V loads go out while block i is
+    // attended and its K loads right after block i's S products, so one
+    // block's loads are always in flight behind the arithmetic.
+    auto next = [&](int& c, long long& off) {
+      const int j = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      c = __builtin_amdgcn_readlane(c_l, j);
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)off_l, j);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((unsigned long long)off_l >> 32), j);
+      off = (long long)(((unsigned long long)hi << 32) | lo);
+    };
+    // V travels by LDS-bound loads into the wave's two V tiles (alternating),
+    // K through registers.  Block i+1's loads (V, then K) are issued right
+    // after block i's S products, so they are in flight during block i's
+    // softmax and PV.  Loads return in issue order: once block i's K has
+    // arrived (the compiler's wait before the S products) its V is in LDS
+    // too; the explicit waits before the V reads restate that with block i+1's
+    // 32 loads still allowed in flight, and keep the reads below them.
+    auto last_row = [&](int c) { return min(pos - c * kBlock, kBlock - 1); };
+    u32x4 kr[4][4];
+    int c, buf = 0;
+    long long off;
+    next(c, off);
+    WaveAttn::load_v_lds(a.v + off, last_row(c), vtile[wave][0]);
+    WaveAttn::load_k(a.k + off, last_row(c), kr);
+    while (todo != 0ull) {
+      int cn;
+      long long offn;
+      next(cn, offn);
+      st.attend(kr, c, pos, a.scale_log2, vtile[wave][buf],
+                [&] {
+                  __builtin_amdgcn_sched_barrier(0);  // keep the loads after the S products
+                  WaveAttn::load_v_lds(a.v + offn, last_row(cn), vtile[wave][buf ^ 1]);
+                  WaveAttn::load_k(a.k + offn, last_row(cn), kr);
+                },
+                [] { wait_vmcnt<32>(); });
+      c = cn;
+      buf ^= 1;
+    }
+    st.attend(kr, c, pos, a.scale_log2, vtile[wave][buf], [] {}, [] { wait_vmcnt<0>(); });
   }
   const float L = st.total_l();
   const int n = lane % 16, g = lane / 16;
