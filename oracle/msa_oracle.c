@@ -1,6 +1,6 @@
 /*
  * msa_oracle.c — plain, slow, single-threaded CPU oracle of the MSA forward
- * pass.  TEST INFRASTRUCTURE ONLY (see msa_oracle.h for the pages followed,
+ * pass and of the main branch's gradient.  TEST INFRASTRUCTURE ONLY (see msa_oracle.h for the pages followed,
  * the readings taken and the layouts).  Every loop here is the definition
  * written out; there is no tiling, fusion or reordering.
  */
@@ -243,5 +243,136 @@ int oracle_forward_rows(const oracle_problem* p, const uint16_t* q, const uint16
                            lse + r * p->n_q_heads);
   }
   free(bsrow);
+  return rc;
+}
+
+/* Tokens of the blocks in sel_h[0..top_k) (one KV head's selection, -1 =
+ * none) that row position pos may attend (j <= pos), in list order.
+ * Returns the count, or -1 for a block id past the cache. */
+static int32_t selected_tokens(const oracle_problem* p, const int32_t* sel_h, int32_t pos,
+                               int32_t* tok) {
+  const int32_t bs = p->block_size, nblk = oracle_num_blocks(p);
+  int32_t n = 0;
+  for (int32_t r = 0; r < p->top_k; ++r) {
+    int32_t c = sel_h[r];
+    if (c < 0) continue;
+    if (c >= nblk) return -1;
+    for (int32_t j = c * bs; j <= pos && j < (c + 1) * bs; ++j) tok[n++] = j;
+  }
+  return n;
+}
+
+int oracle_attend_row_f64(const oracle_problem* p, const double* q, const double* k,
+                          const double* v, const int32_t* seq_lens, const int32_t* sel,
+                          int32_t b, int32_t t, double* out, double* lse) {
+  int32_t pos = oracle_position(p, seq_lens, b, t);
+  if (pos < 0 || !q || !k || !v || !sel || !out || !lse) return ORACLE_EBADARG;
+  const int32_t D = p->head_dim, K = p->top_k;
+  const int32_t G = p->n_q_heads / p->n_kv_heads;
+  int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * (size_t)K * p->block_size);
+  double* z = (double*)malloc(sizeof(double) * (size_t)K * p->block_size);
+  if (!tok || !z) { free(tok); free(z); return ORACLE_ENOMEM; }
+  int rc = ORACLE_OK;
+  for (int32_t hq = 0; hq < p->n_q_heads; ++hq) {
+    const int32_t h = hq / G;
+    const int32_t n = selected_tokens(p, sel + (int64_t)h * K, pos, tok);
+    if (n < 0) { rc = ORACLE_EBADARG; break; }
+    double* o = out + (int64_t)hq * D;
+    for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+    if (n == 0) { lse[hq] = -INFINITY; continue; }
+    const double* qv = q + (((int64_t)b * p->seq_q + t) * p->n_q_heads + hq) * D;
+    double zmax = -INFINITY;
+    for (int32_t a = 0; a < n; ++a) {
+      const double* kv = k + (((int64_t)b * p->n_kv_heads + h) * p->seq_kv + tok[a]) * D;
+      double s = 0.0;
+      for (int32_t d = 0; d < D; ++d) s += qv[d] * kv[d];
+      z[a] = s * p->softmax_scale;
+      if (z[a] > zmax) zmax = z[a];
+    }
+    double l = 0.0;
+    for (int32_t a = 0; a < n; ++a) { z[a] = exp(z[a] - zmax); l += z[a]; }
+    for (int32_t a = 0; a < n; ++a) {
+      const double* vv = v + (((int64_t)b * p->n_kv_heads + h) * p->seq_kv + tok[a]) * D;
+      for (int32_t d = 0; d < D; ++d) o[d] += z[a] * vv[d];
+    }
+    for (int32_t d = 0; d < D; ++d) o[d] = o[d] / l;
+    lse[hq] = log(l) + zmax;
+  }
+  free(tok);
+  free(z);
+  return rc;
+}
+
+int oracle_attend_backward(const oracle_problem* p, const double* q, const double* k,
+                           const double* v, const double* dout, const int32_t* seq_lens,
+                           const int32_t* sel_all, double* dq, double* dk, double* dv) {
+  if (!problem_ok(p) || !q || !k || !v || !dout || !sel_all || !dq || !dk || !dv)
+    return ORACLE_EBADARG;
+  const int32_t D = p->head_dim, K = p->top_k, Hq = p->n_q_heads, Hkv = p->n_kv_heads;
+  const int32_t G = Hq / Hkv;
+  const int64_t nq = (int64_t)p->batch * p->seq_q * Hq * D;
+  const int64_t nkv = (int64_t)p->batch * Hkv * p->seq_kv * D;
+  for (int64_t i = 0; i < nq; ++i) dq[i] = 0.0;
+  for (int64_t i = 0; i < nkv; ++i) { dk[i] = 0.0; dv[i] = 0.0; }
+  int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * (size_t)K * p->block_size);
+  double* w = (double*)malloc(sizeof(double) * (size_t)K * p->block_size);
+  double* o = (double*)malloc(sizeof(double) * (size_t)D);
+  if (!tok || !w || !o) { free(tok); free(w); free(o); return ORACLE_ENOMEM; }
+  int rc = ORACLE_OK;
+  for (int32_t b = 0; b < p->batch && rc == ORACLE_OK; ++b) {
+    for (int32_t t = 0; t < p->seq_q && rc == ORACLE_OK; ++t) {
+      const int32_t pos = oracle_position(p, seq_lens, b, t);
+      if (pos < 0) { rc = ORACLE_EBADARG; break; }
+      const int32_t* sel_row = sel_all + ((int64_t)b * p->seq_q + t) * Hkv * K;
+      for (int32_t hq = 0; hq < Hq; ++hq) {
+        const int32_t h = hq / G;
+        const int32_t n = selected_tokens(p, sel_row + (int64_t)h * K, pos, tok);
+        if (n < 0) { rc = ORACLE_EBADARG; break; }
+        if (n == 0) continue;
+        const int64_t qoff = (((int64_t)b * p->seq_q + t) * Hq + hq) * D;
+        const int64_t kvbase = ((int64_t)b * Hkv + h) * p->seq_kv;
+        const double* qv = q + qoff;
+        const double* g = dout + qoff;
+        /* softmax weights over the attended tokens */
+        double zmax = -INFINITY;
+        for (int32_t a = 0; a < n; ++a) {
+          const double* kv = k + (kvbase + tok[a]) * D;
+          double s = 0.0;
+          for (int32_t d = 0; d < D; ++d) s += qv[d] * kv[d];
+          w[a] = p->softmax_scale * s;
+          if (w[a] > zmax) zmax = w[a];
+        }
+        double l = 0.0;
+        for (int32_t a = 0; a < n; ++a) { w[a] = exp(w[a] - zmax); l += w[a]; }
+        for (int32_t a = 0; a < n; ++a) w[a] /= l;
+        /* the row's output and Dsum = dout . out */
+        for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+        for (int32_t a = 0; a < n; ++a) {
+          const double* vv = v + (kvbase + tok[a]) * D;
+          for (int32_t d = 0; d < D; ++d) o[d] += w[a] * vv[d];
+        }
+        double dsum = 0.0;
+        for (int32_t d = 0; d < D; ++d) dsum += g[d] * o[d];
+        /* per token: dp, ds, and the three accumulations */
+        for (int32_t a = 0; a < n; ++a) {
+          const double* kv = k + (kvbase + tok[a]) * D;
+          const double* vv = v + (kvbase + tok[a]) * D;
+          double dp = 0.0;
+          for (int32_t d = 0; d < D; ++d) dp += g[d] * vv[d];
+          const double ds = w[a] * (dp - dsum);
+          double* dkv = dk + (kvbase + tok[a]) * D;
+          double* dvv = dv + (kvbase + tok[a]) * D;
+          for (int32_t d = 0; d < D; ++d) {
+            dq[qoff + d] += p->softmax_scale * ds * kv[d];
+            dkv[d] += p->softmax_scale * ds * qv[d];
+            dvv[d] += w[a] * g[d];
+          }
+        }
+      }
+    }
+  }
+  free(tok);
+  free(w);
+  free(o);
   return rc;
 }

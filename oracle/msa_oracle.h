@@ -1,6 +1,6 @@
 /*
  * msa_oracle.h — plain, slow, single-threaded CPU oracle of the MiniMax Sparse
- * Attention (MSA) forward pass.
+ * Attention (MSA) forward pass, and the gradient of its main branch.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
  * load or call this code: only the test suite, the smoke check and the CPU
@@ -104,6 +104,30 @@ int oracle_forward_rows(const oracle_problem* p, const uint16_t* q, const uint16
                         const uint16_t* v, const uint16_t* iq, const uint16_t* ik,
                         const int32_t* seq_lens, int64_t n_rows, const int64_t* rows,
                         int32_t* sel_out, double* out, double* lse, float* scores_out);
+
+/* The same attention as oracle_attend_row on fp64 inputs (q [B][Sq][Hq][D],
+ * k, v [B][Hkv][Skv][D] as double): the forward the gradient below is the
+ * derivative of, and what finite differences perturb. */
+int oracle_attend_row_f64(const oracle_problem* p, const double* q, const double* k,
+                          const double* v, const int32_t* seq_lens, const int32_t* sel,
+                          int32_t b, int32_t t, double* out, double* lse);
+
+/* Gradient of the main branch (the training direction the pages mention
+ * without detail: [A] section "MSA uses a lightweight index branch before
+ * sparse attention", kernels written for training as well as inference).
+ * With out(b, t, hq) = oracle_attend_row_f64 over the selection
+ * sel_all[(b * Sq + t) * Hkv * top_k + h * top_k + r] and a cotangent dout of
+ * the same shape as out ([B][Sq][Hq][D], double), returns the gradients of
+ * L = sum(dout * out) with respect to q, k and v:
+ *   dq [B][Sq][Hq][D], dk, dv [B][Hkv][Skv][D] (all overwritten).
+ * The selection is an input and receives no gradient.  Per attended token
+ * a of row (b, t), head hq: p_a = softmax weight, dp_a = dout . v_a,
+ * Dsum = dout . out, ds_a = p_a (dp_a - Dsum); dq += scale ds_a k_a,
+ * dk_a += scale ds_a q, dv_a += p_a dout.  A row that attends nothing
+ * contributes nothing. */
+int oracle_attend_backward(const oracle_problem* p, const double* q, const double* k,
+                           const double* v, const double* dout, const int32_t* seq_lens,
+                           const int32_t* sel_all, double* dq, double* dk, double* dv);
 
 #ifdef __cplusplus
 }

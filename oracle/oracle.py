@@ -98,8 +98,12 @@ def _bind(L):
                                    f64, f64]
     L.oracle_forward_rows.argtypes = [prob, u16, u16, u16, u16, u16, i32, ctypes.c_int64, i64,
                                       i32, f64, f64, f32]
+    L.oracle_attend_row_f64.argtypes = [prob, f64, f64, f64, i32, i32, ctypes.c_int32,
+                                        ctypes.c_int32, f64, f64]
+    L.oracle_attend_backward.argtypes = [prob, f64, f64, f64, f64, i32, i32, f64, f64, f64]
     for name in ("oracle_block_scores_row", "oracle_select_row", "oracle_attend_row",
-                 "oracle_dense_row", "oracle_forward_rows"):
+                 "oracle_dense_row", "oracle_forward_rows", "oracle_attend_row_f64",
+                 "oracle_attend_backward"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -221,3 +225,45 @@ def forward_rows_parallel(p: Problem, q, k, v, iq, ik, seq_lens, rows, threads: 
         if want_scores:
             scores[i::threads] = sc
     return sel, out, lse, scores
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def attend_row_f64(p: Problem, q, k, v, seq_lens, sel, b: int, t: int, L=None):
+    """oracle_attend_row on fp64 inputs (q [B][Sq][Hq][D], k, v [B][Hkv][Skv][D])."""
+    L = L or lib()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    s = np.ascontiguousarray(sel, dtype=np.int32).reshape(p.n_kv_heads, p.top_k)
+    sl = None if seq_lens is None else np.ascontiguousarray(seq_lens, dtype=np.int32)
+    out = np.empty((p.n_q_heads, p.head_dim), dtype=np.float64)
+    lse = np.empty((p.n_q_heads,), dtype=np.float64)
+    _check(L.oracle_attend_row_f64(ctypes.byref(p.c()), _ptr(q, ctypes.c_double),
+                                   _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
+                                   _ptr(sl, ctypes.c_int32), _ptr(s, ctypes.c_int32), b, t,
+                                   _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double)),
+           "attend_row_f64")
+    return out, lse
+
+
+def attend_backward(p: Problem, q, k, v, dout, seq_lens, sel_all, L=None):
+    """Gradients (dq [B][Sq][Hq][D], dk, dv [B][Hkv][Skv][D], fp64) of
+    sum(dout * out) for the sparse attention of every row over the selection
+    sel_all [B][Sq][Hkv][top_k]; inputs are fp64 arrays (or anything numpy
+    converts: pass bf16 values as exact doubles)."""
+    L = L or lib()
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    s = np.ascontiguousarray(sel_all, dtype=np.int32)
+    assert s.shape == (p.batch, p.seq_q, p.n_kv_heads, p.top_k)
+    sl = None if seq_lens is None else np.ascontiguousarray(seq_lens, dtype=np.int32)
+    dq = np.empty((p.batch, p.seq_q, p.n_q_heads, p.head_dim), dtype=np.float64)
+    dk = np.empty((p.batch, p.n_kv_heads, p.seq_kv, p.head_dim), dtype=np.float64)
+    dv = np.empty_like(dk)
+    _check(L.oracle_attend_backward(ctypes.byref(p.c()), _ptr(q, ctypes.c_double),
+                                    _ptr(k, ctypes.c_double), _ptr(v, ctypes.c_double),
+                                    _ptr(g, ctypes.c_double), _ptr(sl, ctypes.c_int32),
+                                    _ptr(s, ctypes.c_int32), _ptr(dq, ctypes.c_double),
+                                    _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double)),
+           "attend_backward")
+    return dq, dk, dv

@@ -21,7 +21,11 @@ What pins what:
   * selection         -> exhaustive subset enumeration (the k-subset with the
                          largest score sum, ties to the lexicographically
                          smallest ascending list) and the rank-count formula;
-  * golden            -> a hand-derived worked example (tests/golden).
+  * golden            -> a hand-derived worked example (tests/golden);
+  * gradient          -> central differences of the fp64 forward, torch
+                         autograd of dense causal attention (all blocks kept),
+                         and the sum rules over keys (sum of dk = 0, sum of
+                         dv = sum of dout over the rows reading the head).
 """
 from __future__ import annotations
 
@@ -361,9 +365,113 @@ def check_golden_hand_example(L):
     assert exp["out_formula"] and exp["lse_formula"]
 
 
+# ----------------------------------------------------------------- main-branch gradient
+def _random_selection(p, rng):
+    """[B][Sq][Hkv][k]: own block plus random earlier blocks, ascending, -1 padded."""
+    sel = np.full((p.batch, p.seq_q, p.n_kv_heads, p.top_k), -1, np.int32)
+    for b in range(p.batch):
+        for t in range(p.seq_q):
+            cur = (p.q_start + t) // p.block_size
+            for h in range(p.n_kv_heads):
+                others = list(range(cur))
+                m = min(len(others), p.top_k - 1)
+                pick = sorted(set(rng.choice(others, size=m, replace=False).tolist()) | {cur}) \
+                    if m > 0 else [cur]
+                sel[b, t, h, : len(pick)] = pick
+    return sel
+
+
+def _loss_f64(p, q, k, v, dout, sel, L):
+    tot = 0.0
+    for b in range(p.batch):
+        for t in range(p.seq_q):
+            o, _ = O.attend_row_f64(p, q, k, v, None, sel[b, t], b, t, L=L)
+            tot += float(np.sum(dout[b, t] * o))
+    return tot
+
+
+def check_backward_finite_differences(L):
+    """Gradient of sum(dout * out) against central differences of the fp64
+    forward, on sampled coordinates of q, k and v (random selections, a ragged
+    last block, two sequences)."""
+    p = problem(B=2, Sq=11, Skv=11, Hq=4, Hkv=2, D=8, Hi=2, bs=4, k=2)
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((p.batch, p.seq_q, p.n_q_heads, p.head_dim))
+    k = rng.standard_normal((p.batch, p.n_kv_heads, p.seq_kv, p.head_dim))
+    v = rng.standard_normal((p.batch, p.n_kv_heads, p.seq_kv, p.head_dim))
+    g = rng.standard_normal(q.shape)
+    sel = _random_selection(p, rng)
+    dq, dk, dv = O.attend_backward(p, q, k, v, g, None, sel, L=L)
+    h = 1e-6
+    for name, x, gx in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(12):
+            idx = tuple(int(rng.integers(0, n)) for n in x.shape)
+            x0 = x[idx]
+            x[idx] = x0 + h
+            lp = _loss_f64(p, q, k, v, g, sel, L)
+            x[idx] = x0 - h
+            lm = _loss_f64(p, q, k, v, g, sel, L)
+            x[idx] = x0
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - gx[idx]) <= 1e-6 * (1.0 + abs(fd)), \
+                f"d{name}{idx}: analytic {gx[idx]:.9e} vs central difference {fd:.9e}"
+
+
+def check_backward_dense_vs_autograd(L):
+    """Every causal block selected: the gradient is that of dense causal GQA
+    attention, taken by torch autograd in float64 (a library routine)."""
+    p = problem(B=1, Sq=19, Skv=23, q_start=4, Hq=6, Hkv=2, D=16, Hi=2, bs=4, k=8)
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((p.batch, p.seq_q, p.n_q_heads, p.head_dim))
+    k = rng.standard_normal((p.batch, p.n_kv_heads, p.seq_kv, p.head_dim))
+    v = rng.standard_normal((p.batch, p.n_kv_heads, p.seq_kv, p.head_dim))
+    g = rng.standard_normal(q.shape)
+    sel = np.full((p.batch, p.seq_q, p.n_kv_heads, p.top_k), -1, np.int32)
+    for t in range(p.seq_q):
+        cur = (p.q_start + t) // p.block_size
+        sel[0, t, :, : cur + 1] = np.arange(cur + 1)
+    dq, dk, dv = O.attend_backward(p, q, k, v, g, None, sel, L=L)
+    tq = torch.tensor(q[0].transpose(1, 0, 2)).unsqueeze(0).requires_grad_()  # [1,Hq,Sq,D]
+    tk = torch.tensor(k).requires_grad_()                                      # [1,Hkv,Skv,D]
+    tv = torch.tensor(v).requires_grad_()
+    pos = torch.arange(p.seq_q) + p.q_start
+    mask = pos[:, None] >= torch.arange(p.seq_kv)[None, :]
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=p.softmax_scale,
+                                       enable_gqa=True)
+    (o * torch.tensor(g[0].transpose(1, 0, 2)).unsqueeze(0)).sum().backward()
+    close(dq[0], tq.grad[0].transpose(0, 1).numpy(), 1e-10, "dense dq")
+    close(dk, tk.grad.numpy(), 1e-10, "dense dk")
+    close(dv, tv.grad.numpy(), 1e-10, "dense dv")
+
+
+def check_backward_invariants(L):
+    """Sparse selections: the softmax weights of a row sum to one, so the
+    key gradient summed over all keys of a KV head vanishes and the value
+    gradient summed over all keys equals the sum of dout over the rows and
+    query heads that read that KV head."""
+    p = problem(B=2, Sq=30, Skv=34, q_start=4, Hq=8, Hkv=2, D=16, Hi=2, bs=4, k=3)
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((p.batch, p.seq_q, p.n_q_heads, p.head_dim))
+    k = rng.standard_normal((p.batch, p.n_kv_heads, p.seq_kv, p.head_dim))
+    v = rng.standard_normal((p.batch, p.n_kv_heads, p.seq_kv, p.head_dim))
+    g = rng.standard_normal(q.shape)
+    sel = _random_selection(p, rng)
+    dq, dk, dv = O.attend_backward(p, q, k, v, g, None, sel, L=L)
+    G = p.n_q_heads // p.n_kv_heads
+    close(dk.sum(axis=2), np.zeros((p.batch, p.n_kv_heads, p.head_dim)), 1e-10, "sum of dk")
+    want = g.reshape(p.batch, p.seq_q, p.n_kv_heads, G, p.head_dim).sum(axis=(1, 3))
+    close(dv.sum(axis=2), want, 1e-10, "sum of dv")
+    # a cotangent of zero gives zero gradients
+    z = O.attend_backward(p, q, k, v, np.zeros_like(g), None, sel, L=L)
+    for a in z:
+        assert not np.any(a), "zero cotangent, nonzero gradient"
+
+
 ALL_CHECKS = [check_dense_vs_library, check_attend_vs_masked_library,
               check_all_blocks_equals_dense, check_softmax_closed_forms,
               check_decode_is_last_prefill_row, check_block_scores_integer_closed_form,
               check_block_scores_rational_brute_force, check_block_scores_causal_and_attribution,
               check_planted_winners_per_kv_head, check_select_brute_force,
-              check_select_edge_cases, check_golden_hand_example]
+              check_select_edge_cases, check_golden_hand_example,
+              check_backward_finite_differences, check_backward_dense_vs_autograd,
+              check_backward_invariants]

@@ -46,6 +46,21 @@ MUTANTS = [
     ("dense_head_map", "const int32_t kvh = hq / (p->n_q_heads / p->n_kv_heads);",
      "const int32_t kvh = hq % p->n_kv_heads;"),
     ("dense_scale", "w[j] = acc * p->softmax_scale;", "w[j] = acc;"),
+    # the main-branch gradient and its fp64 forward
+    ("bwd_missing_dsum", "const double ds = w[a] * (dp - dsum);", "const double ds = w[a] * dp;"),
+    ("bwd_dsum_sign", "const double ds = w[a] * (dp - dsum);",
+     "const double ds = w[a] * (dsum - dp);"),
+    ("bwd_dk_unscaled", "dkv[d] += p->softmax_scale * ds * qv[d];", "dkv[d] += ds * qv[d];"),
+    ("bwd_dq_reads_v", "dq[qoff + d] += p->softmax_scale * ds * kv[d];",
+     "dq[qoff + d] += p->softmax_scale * ds * vv[d];"),
+    ("bwd_dv_uses_ds", "dvv[d] += w[a] * g[d];", "dvv[d] += ds * g[d];"),
+    ("bwd_unnormalised_weights", "for (int32_t a = 0; a < n; ++a) w[a] /= l;",
+     "for (int32_t a = 0; a < n; ++a) w[a] /= (l + 0.5);"),
+    ("bwd_dsum_uses_q", "for (int32_t d = 0; d < D; ++d) dsum += g[d] * o[d];",
+     "for (int32_t d = 0; d < D; ++d) dsum += g[d] * qv[d];"),
+    ("bwd_tokens_not_causal", "for (int32_t j = c * bs; j <= pos && j < (c + 1) * bs; ++j) tok[n++] = j;",
+     "for (int32_t j = c * bs; j < (c + 1) * bs && j < p->seq_kv; ++j) tok[n++] = j;"),
+    ("f64_forward_unscaled", "z[a] = s * p->softmax_scale;", "z[a] = s;"),
 ]
 
 
