@@ -9,5 +9,6 @@ from . import configs, inputs  # noqa: F401
 from .binding import (Problem, MsaError, abi_version, msa_dense_attn_decode,  # noqa: F401
                       msa_dense_attn_prefill, msa_index_block_scores,
                       msa_index_block_scores_paged, msa_index_topk_fused, msa_sparse_attn_decode,
+                      msa_sparse_attn_prefill_backward,
                       msa_sparse_attn_decode_paged, msa_sparse_attn_prefill, msa_topk_blocks,
                       msa_workspace_bytes)

@@ -23,7 +23,7 @@ STATUS = {0: "MSA_OK", 1: "MSA_ERR_INVALID_ARGUMENT", 2: "MSA_ERR_UNSUPPORTED",
           3: "MSA_ERR_WORKSPACE_TOO_SMALL", 4: "MSA_ERR_HIP"}
 OPS = {"index_block_scores": 0, "topk_blocks": 1, "index_topk_fused": 2,
        "sparse_attn_prefill": 3, "sparse_attn_decode": 4, "dense_attn_prefill": 5,
-       "dense_attn_decode": 6}
+       "dense_attn_decode": 6, "sparse_attn_prefill_backward": 7}
 
 
 class MsaError(RuntimeError):
@@ -95,6 +95,8 @@ def lib():
             "msa_index_block_scores_paged": [pr, vp, vp, vp, ctypes.c_int32, vp, vp, vp],
             "msa_sparse_attn_decode_paged": [pr, vp, vp, vp, vp, ctypes.c_int32, vp, vp, vp, vp,
                                              vp, sz, vp],
+            "msa_sparse_attn_prefill_backward": [pr, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                 sz, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -193,6 +195,26 @@ def msa_sparse_attn_prefill(p: Problem, q, k, v, sel, out=None, lse=None, worksp
                                          _ptr(lse, torch.float32), _ptr(ws), nbytes,
                                          _stream(stream)))
     return out
+
+
+def msa_sparse_attn_prefill_backward(p: Problem, q, k, v, sel, out, lse, dout, dq=None, dk=None,
+                                     dv=None, workspace=None, stream=None):
+    """Gradients (dq [B][Sq][Hq][128], dk, dv [B][Hkv][Skv][128], fp32) of
+    sum(dout * out) for msa_sparse_attn_prefill's out and lse on these inputs."""
+    f32 = dict(dtype=torch.float32, device=q.device)
+    if dq is None:
+        dq = torch.empty(q.shape, **f32)
+    if dk is None:
+        dk = torch.empty(k.shape, **f32)
+    if dv is None:
+        dv = torch.empty(v.shape, **f32)
+    ws, nbytes = _workspace(p, "sparse_attn_prefill_backward", workspace, q.device)
+    _check(lib().msa_sparse_attn_prefill_backward(
+        ctypes.byref(p.c()), _ptr(q, torch.bfloat16), _ptr(k, torch.bfloat16),
+        _ptr(v, torch.bfloat16), _ptr(sel, torch.int32), _ptr(out, torch.bfloat16),
+        _ptr(lse, torch.float32), _ptr(dout, torch.bfloat16), _ptr(dq, torch.float32),
+        _ptr(dk, torch.float32), _ptr(dv, torch.float32), _ptr(ws), nbytes, _stream(stream)))
+    return dq, dk, dv
 
 
 def msa_sparse_attn_decode(p: Problem, q, k_cache, v_cache, seq_lens, sel, out=None, lse=None,

@@ -91,6 +91,15 @@ msa_status launched(hipError_t e, const char* what) {
   return ok();
 }
 
+// Backward-specific limits on top of check_problem.
+msa_status check_backward(const msa::Shape& s) {
+  if (64 % s.G != 0) return fail(MSA_ERR_UNSUPPORTED, "backward needs n_q_heads / n_kv_heads to divide 64");
+  if ((size_t)s.nblk * 8 > 160 * 1024) return fail(MSA_ERR_UNSUPPORTED, "backward needs seq_kv <= 1310720");
+  if ((int64_t)s.B * s.Hkv * s.Sq * s.top_k >= ((int64_t)1 << 31))
+    return fail(MSA_ERR_UNSUPPORTED, "backward needs batch * n_kv_heads * seq_q * top_k < 2^31");
+  return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -259,6 +268,35 @@ msa_status msa_sparse_attn_decode_paged(const msa_problem* p, const void* q,
                   "msa_sparse_attn_decode_paged");
 }
 
+msa_status msa_sparse_attn_prefill_backward(const msa_problem* p, const void* q, const void* k,
+                                            const void* v, const int32_t* sel, const void* out,
+                                            const float* lse, const void* dout, float* dq,
+                                            float* dk, float* dv, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream) {
+  msa::Shape s;
+  msa_status st = check_problem(p, Mode::kPrefill, true, &s);
+  if (st != MSA_OK) return st;
+  st = check_backward(s);
+  if (st != MSA_OK) return st;
+  NEED_PTR(q);
+  NEED_PTR(k);
+  NEED_PTR(v);
+  NEED_PTR4(sel);
+  NEED_PTR(out);
+  NEED_PTR4(lse);
+  NEED_PTR(dout);
+  NEED_PTR(dq);
+  NEED_PTR(dk);
+  NEED_PTR(dv);
+  NEED_PTR(workspace);
+  const size_t need = msa::sparse_bwd_workspace_bytes(s);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  return launched(msa::launch_sparse_attn_backward(s, q, k, v, sel, out, lse, dout, dq, dk, dv,
+                                                   workspace, stream),
+                  "msa_sparse_attn_prefill_backward");
+}
+
 msa_status msa_workspace_bytes(const msa_problem* p, msa_op op, size_t* bytes) {
   if (!bytes) return fail(MSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
   msa::Shape s;
@@ -276,6 +314,13 @@ msa_status msa_workspace_bytes(const msa_problem* p, msa_op op, size_t* bytes) {
       st = check_problem(p, Mode::kPrefill, true, &s);
       if (st != MSA_OK) return st;
       *bytes = msa::fused_workspace_bytes(s);
+      return ok();
+    case MSA_OP_SPARSE_ATTN_PREFILL_BACKWARD:
+      st = check_problem(p, Mode::kPrefill, true, &s);
+      if (st != MSA_OK) return st;
+      st = check_backward(s);
+      if (st != MSA_OK) return st;
+      *bytes = msa::sparse_bwd_workspace_bytes(s);
       return ok();
     case MSA_OP_SPARSE_ATTN_DECODE:
     case MSA_OP_DENSE_ATTN_DECODE:

@@ -135,7 +135,7 @@ struct WaveAttn {
   __device__ __forceinline__ void attend(const u32x4 (&kr)[4][4], int c, int pos,
                                          float scale_log2, const u32x4* vlds, AfterS&& after_s,
                                          BeforePV&& before_pv) {
-    const int lane = lane_id(), n = lane % 16, g = lane / 16;
+    const int lane = lane_id(), g = lane / 16;
     // S^T = K Q^T
     f32x4 sc[4];
 #pragma unroll
@@ -176,14 +176,24 @@ struct WaveAttn {
     for (int i = 0; i < 8; ++i) o[i] *= alpha;
     __builtin_amdgcn_wave_barrier();  // V tile writes above precede the reads below
     before_pv();
-    // O^T += V^T P^T
+    pv_step(sc, vlds, o);
+    __builtin_amdgcn_wave_barrier();  // reads done before the next block overwrites the tile
+  }
+
+  // acc^T += T^T P^T over one 64-row tile: T is the tile in LDS ([64][128]
+  // bf16 in the vtile_slot layout), P^T the probabilities in S^T layout (pt[mt]
+  // reg r = tile row 16mt + 4g + r, column n; rounded to bf16 here); acc has
+  // the O^T layout (M-tile 4hf + j, row 4g + r = dim 64hf + 16g + 4r + j).
+  __device__ __forceinline__ static void pv_step(const f32x4 (&pt)[4], const u32x4* tile,
+                                                 f32x4 (&acc)[8]) {
+    const int lane = lane_id(), n = lane % 16, g = lane / 16;
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
       u32x4 pw;
-      pw[0] = pack_bf16x2(sc[2 * kv][0], sc[2 * kv][1]);
-      pw[1] = pack_bf16x2(sc[2 * kv][2], sc[2 * kv][3]);
-      pw[2] = pack_bf16x2(sc[2 * kv + 1][0], sc[2 * kv + 1][1]);
-      pw[3] = pack_bf16x2(sc[2 * kv + 1][2], sc[2 * kv + 1][3]);
+      pw[0] = pack_bf16x2(pt[2 * kv][0], pt[2 * kv][1]);
+      pw[1] = pack_bf16x2(pt[2 * kv][2], pt[2 * kv][3]);
+      pw[2] = pack_bf16x2(pt[2 * kv + 1][0], pt[2 * kv + 1][1]);
+      pw[3] = pack_bf16x2(pt[2 * kv + 1][2], pt[2 * kv + 1][3]);
       const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -193,7 +203,7 @@ struct WaveAttn {
         for (int i = 0; i < 8; ++i) {
           const int key = 32 * kv + 16 * (i / 4) + 4 * g + (i % 4);
           const int ch = 8 * hf + n / 2;
-          const u32x2* p = reinterpret_cast<const u32x2*>(vlds + vtile_slot(key, ch)) + (n & 1);
+          const u32x2* p = reinterpret_cast<const u32x2*>(tile + vtile_slot(key, ch)) + (n & 1);
           rd[i] = *p;
         }
 #pragma unroll
@@ -204,11 +214,10 @@ struct WaveAttn {
             const uint32_t x = rd[2 * w][j / 2], y = rd[2 * w + 1][j / 2];
             a[w] = (j & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
           }
-          o[4 * hf + j] = mfma16(as_bf16x8(a), pb, o[4 * hf + j]);
+          acc[4 * hf + j] = mfma16(as_bf16x8(a), pb, acc[4 * hf + j]);
         }
       }
     }
-    __builtin_amdgcn_wave_barrier();  // reads done before the next block overwrites the tile
   }
 
   // Column normaliser (sum over the four lane groups).

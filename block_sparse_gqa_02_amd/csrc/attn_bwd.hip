@@ -1,0 +1,394 @@
+// attn_bwd.hip — gradient of the sparse GQA prefill attention (main branch).
+//
+// The pages say the authors wrote kernels for training as well as inference
+// (talk summary "How MiniMax M3 Was Built", section "MSA uses a lightweight
+// index branch before sparse attention"; news write-up "MiniMax Researcher
+// Olive Song: Sparse Attention Cannot Be Directly Ported…", paragraph 5).  This
+// is the gradient of the main branch for a given selection: with
+// p = softmax(scale q.k) over the selected causal tokens and o = sum p v,
+//   Dsum = dout . o,  dp_a = dout . v_a,  ds_a = p_a (dp_a - Dsum),
+//   dq = scale sum ds_a k_a,  dk_a += scale ds_a q,  dv_a += p_a dout.
+// The selection gets no gradient.  Softmax weights are recomputed from the
+// forward's log-sum-exp; Dsum uses the forward's (bf16) output.
+//
+// Kernels, in launch order:
+//   dsum_kernel      Dsum per (sequence, query head, row).
+//   inverse kernels  for every (sequence, KV head, block) the ascending list of
+//                    rows that selected it: per batch of 64 rows a bitmap over
+//                    blocks in LDS (bit i = row i of the batch), counted, scanned
+//                    over batches and over blocks, then filled in row order.
+//                    Deterministic: no atomics outside LDS bit sets.
+//   dq_kernel        one wave per (row, KV head): per selected block
+//                    S^T = K Q^T, dP^T = V dO^T, dS from the saved log-sum-exp,
+//                    dQ^T += K^T dS^T (the forward's PV step with K in the
+//                    V-tile role).
+//   dkdv_kernel      one work-group per (KV head, block), wave w owning keys
+//                    16w..16w+15: the block's rows are taken 64 query columns
+//                    (rows x group heads) at a time through LDS tiles of Q and
+//                    dO; X = Q K^T, Y = dO V^T, then dV^T += dO^T P and
+//                    dK^T += Q^T dS, again the forward's PV step.
+// Operand layouts and the PV step are those of attn_block.h.
+#include "attn_block.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace msa {
+namespace {
+
+constexpr float kLog2eB = 1.4426950408889634f;
+constexpr int kBatchRows = 64;  // rows per inverse-list batch (one bit each)
+
+struct BwdArgs {
+  const uint16_t* q;     // [B][Sq][Hq][128]
+  const uint16_t* k;     // [B][Hkv][Skv][128]
+  const uint16_t* v;
+  const int32_t* sel;    // [B][Hkv][Sq][top_k]
+  const uint16_t* out;   // [B][Sq][Hq][128] forward output
+  const float* lse;      // [B][Hq][Sq] forward log-sum-exp (natural log)
+  const uint16_t* dout;  // [B][Sq][Hq][128]
+  float* dq;             // [B][Sq][Hq][128]
+  float* dk;             // [B][Hkv][Skv][128]
+  float* dv;
+  float* dsum;           // workspace [B][Hq][Sq]
+  int32_t* bcnt;         // workspace [B][Hkv][nbatch][nblk]: counts, then offsets in the list
+  int32_t* base;         // workspace [B*Hkv*nblk + 1]: list starts (exclusive scan)
+  int32_t* lists;        // workspace [B*Hkv*Sq*top_k]: rows per (sequence, KV head, block)
+  int B, Sq, Skv, q_start, Hq, Hkv, G, top_k, nblk, nbatch;
+  float scale, scale_log2;
+};
+
+__device__ __forceinline__ float wave_sum64(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// acc has the O^T layout of attn_block.h (M-tile 4hf + j, row 4g + r = dim
+// 64hf + 16g + 4r + j of column n); writes column n's 128 dims times mul.
+__device__ __forceinline__ void store_cols_f32(const f32x4 (&acc)[8], float* col_base, float mul) {
+  const int g = lane_id() / 16;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 v = {acc[4 * hf + 0][r] * mul, acc[4 * hf + 1][r] * mul,
+                       acc[4 * hf + 2][r] * mul, acc[4 * hf + 3][r] * mul};
+      *reinterpret_cast<f32x4*>(col_base + 64 * hf + 16 * g + 4 * r) = v;
+    }
+}
+
+// Dsum[b][hq][t] = sum_d dout * out; one wave per (b, t, hq), lanes over dim pairs.
+__global__ void __launch_bounds__(256) dsum_kernel(BwdArgs a) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const long long w = (long long)blockIdx.x * 4 + wave;  // (b * Sq + t) * Hq + hq
+  if (w >= (long long)a.B * a.Sq * a.Hq) return;
+  const uint32_t o2 = reinterpret_cast<const uint32_t*>(a.out + w * kHeadDim)[lane];
+  const uint32_t g2 = reinterpret_cast<const uint32_t*>(a.dout + w * kHeadDim)[lane];
+  const float s = wave_sum64(bf16_lo(o2) * bf16_lo(g2) + bf16_hi(o2) * bf16_hi(g2));
+  if (lane == 0) {
+    const int hq = (int)(w % a.Hq);
+    const long long bt = w / a.Hq;
+    const int t = (int)(bt % a.Sq), b = (int)(bt / a.Sq);
+    a.dsum[((long long)b * a.Hq + hq) * a.Sq + t] = s;
+  }
+}
+
+// Inverse lists, pass 1 (FILL = false: per-batch counts) and pass 3 (FILL =
+// true: rows written at their offsets).  One work-group per (sequence, KV
+// head, batch of 64 rows); the bitmap (one 64-bit word per block, dynamic LDS)
+// marks which rows of the batch selected each block.  A selection entry
+// counts when 0 <= c <= the row's own block, the blocks the forward attends.
+template <bool FILL>
+__global__ void __launch_bounds__(256) inverse_kernel(BwdArgs a) {
+  extern __shared__ unsigned long long bm[];
+  const int batch = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int t0 = batch * kBatchRows;
+  const int rows = min(kBatchRows, a.Sq - t0);
+  const int cmax = (a.q_start + t0 + rows - 1) / kBlock;  // last block the batch can select
+  for (int c = threadIdx.x; c <= cmax; c += 256) bm[c] = 0ull;
+  __syncthreads();
+  const int32_t* srow = a.sel + (((long long)b * a.Hkv + h) * a.Sq + t0) * a.top_k;
+  for (int idx = threadIdx.x; idx < rows * a.top_k; idx += 256) {
+    const int i = idx / a.top_k;
+    const int c = srow[idx];
+    const int cur = (a.q_start + t0 + i) / kBlock;
+    if (c >= 0 && c <= cur) atomicOr(&bm[c], 1ull << i);
+  }
+  __syncthreads();
+  const long long hb = (long long)b * a.Hkv + h;
+  int32_t* cnt = a.bcnt + (hb * a.nbatch + batch) * a.nblk;
+  for (int c = threadIdx.x; c <= cmax; c += 256) {
+    unsigned long long m = bm[c];
+    if (!FILL) {
+      cnt[c] = __popcll(m);
+    } else {
+      int32_t* dst = a.lists + a.base[hb * a.nblk + c] + cnt[c];
+      while (m != 0ull) {
+        const int i = __builtin_ctzll(m);
+        m &= m - 1;
+        *dst++ = t0 + i;
+      }
+    }
+  }
+}
+
+// Pass 2a: per (sequence, KV head, block), the exclusive scan of the batch
+// counts (in place) and the list length.  One thread per block index.
+__global__ void __launch_bounds__(256) batch_scan_kernel(BwdArgs a) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const long long hb = blockIdx.y;  // b * Hkv + h
+  if (c >= a.nblk) return;
+  int32_t* cnt = a.bcnt + hb * a.nbatch * a.nblk + c;
+  // a batch whose last row's block is below c holds no count for c (pass 1
+  // never wrote it, pass 3 never reads it)
+  int run = 0;
+  for (int j = 0; j < a.nbatch; ++j) {
+    const int rows = min(kBatchRows, a.Sq - j * kBatchRows);
+    if ((a.q_start + j * kBatchRows + rows - 1) / kBlock < c) continue;
+    const int x = cnt[(long long)j * a.nblk];
+    cnt[(long long)j * a.nblk] = run;
+    run += x;
+  }
+  a.base[hb * a.nblk + c] = run;  // length; turned into the start by pass 2b
+}
+
+// Pass 2b: exclusive scan of the list lengths over all (sequence, KV head,
+// block), in one work-group; base[n] receives the total.
+__global__ void __launch_bounds__(256) base_scan_kernel(BwdArgs a) {
+  __shared__ int32_t part[256];
+  const long long n = (long long)a.B * a.Hkv * a.nblk;
+  const long long per = (n + 255) / 256;
+  const long long lo = threadIdx.x * per, hi = min(n, lo + per);
+  int32_t s = 0;
+  for (long long i = lo; i < hi; ++i) s += a.base[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int32_t x = part[i];
+      part[i] = run;
+      run += x;
+    }
+    a.base[n] = run;
+  }
+  __syncthreads();
+  int32_t run = part[threadIdx.x];
+  for (long long i = lo; i < hi; ++i) {
+    const int32_t x = a.base[i];
+    a.base[i] = run;
+    run += x;
+  }
+}
+
+// dQ: one wave per (sequence, KV head, row); columns n < G are the group's
+// query heads.
+__global__ void __launch_bounds__(256) dq_kernel(BwdArgs a) {
+  __shared__ u32x4 ktile[4][kBlock * 16];  // per wave: the block's K in the vtile layout
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int n = lane % 16, g = lane / 16;
+  const long long w = (long long)blockIdx.x * 4 + wave;  // ((b * Hkv + h) * Sq + t)
+  if (w >= (long long)a.B * a.Hkv * a.Sq) return;
+  const int t = (int)(w % a.Sq);
+  const long long hb = w / a.Sq;
+  const int h = (int)(hb % a.Hkv), b = (int)(hb / a.Hkv);
+  const int pos = a.q_start + t, cur = pos / kBlock;
+  const int hq0 = h * a.G;
+  WaveAttn qs, gs;  // Q^T and dO^T operands of the row's group
+  qs.load_q(a.q + ((long long)b * a.Sq + t) * a.Hq * kHeadDim + (long long)hq0 * kHeadDim, a.G);
+  gs.load_q(a.dout + ((long long)b * a.Sq + t) * a.Hq * kHeadDim + (long long)hq0 * kHeadDim, a.G);
+  const bool col_ok = n < a.G;
+  const float lse2 = col_ok ? a.lse[((long long)b * a.Hq + hq0 + n) * a.Sq + t] * kLog2eB : 0.f;
+  const float ds0 = col_ok ? a.dsum[((long long)b * a.Hq + hq0 + n) * a.Sq + t] : 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int32_t* list = a.sel + w * a.top_k;
+  u32x4* tile = ktile[wave];
+  for (int r = 0; r < a.top_k; ++r) {
+    const int c = list[r];
+    if (c < 0 || c > cur) continue;
+    const long long off = (hb * a.Skv + (long long)c * kBlock) * kHeadDim;
+    const int last = min(pos - c * kBlock, kBlock - 1);
+    u32x4 vr[16], vk[4][4];
+    WaveAttn::load_v(a.k + off, last, vr);   // K, for the LDS tile
+    WaveAttn::load_k(a.v + off, last, vk);   // V, as the A operand of dP^T
+    WaveAttn::store_v(vr, tile);
+    __builtin_amdgcn_wave_barrier();
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 kf = as_bf16x8(tile[vtile_slot(16 * mt + n, 4 * ks + g)]);
+        s[mt] = mfma16(kf, qs.qf[ks], s[mt]);
+        dp[mt] = mfma16(as_bf16x8(vk[mt][ks]), gs.qf[ks], dp[mt]);
+      }
+    }
+    // dS^T in the S^T layout: key 64c + 16mt + 4g + r, column n
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int key = c * kBlock + 16 * mt + 4 * g + rr;
+        const float p = (col_ok && key <= pos) ? exp2f(s[mt][rr] * a.scale_log2 - lse2) : 0.f;
+        s[mt][rr] = p * (dp[mt][rr] - ds0);
+      }
+    WaveAttn::pv_step(s, tile, acc);
+    __builtin_amdgcn_wave_barrier();  // tile reads done before the next block's writes
+  }
+  if (col_ok) store_cols_f32(acc, a.dq + (((long long)b * a.Sq + t) * a.Hq + hq0 + n) * kHeadDim,
+                             a.scale);
+}
+
+// dK and dV of one block: work-group per (block, KV head, sequence), wave w
+// owns keys 16w..16w+15.  Query columns (row slot i / G, head i % G) are taken
+// 64 at a time from the block's row list.
+__global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
+  __shared__ u32x4 qtile[kBlock * 16];  // 64 columns x 128 dims, vtile layout
+  __shared__ u32x4 gtile[kBlock * 16];  // the same columns of dO
+  __shared__ float clse[64], cds[64];
+  __shared__ int cpos[64];
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int n = lane % 16, g = lane / 16;
+  const long long hb = (long long)b * a.Hkv + h;
+  const int key0 = c * kBlock + 16 * wave;        // this wave's first key
+  const int nkeys = max(0, min(16, a.Skv - key0));  // keys of the wave inside the cache
+  const long long koff = (hb * a.Skv + key0) * kHeadDim;
+  WaveAttn ks_, vs_;  // K^T and V^T operands: column n = key key0 + n (zero past the cache)
+  ks_.load_q(a.k + (nkeys > 0 ? koff : 0), nkeys);
+  vs_.load_q(a.v + (nkeys > 0 ? koff : 0), nkeys);
+  f32x4 dka[8], dva[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    dka[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dva[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int32_t beg = a.base[hb * a.nblk + c], len = a.base[hb * a.nblk + c + 1] - beg;
+  const int32_t* rows = a.lists + beg;
+  const int R = 64 / a.G;  // rows per 64 columns
+  for (int r0 = 0; r0 < len; r0 += R) {
+    // stage the 64 columns' Q and dO rows (1024 chunks of 16 bytes each)
+    for (int qd = tid; qd < 64 * 16; qd += 256) {
+      const int col = qd / 16, ch = qd % 16;
+      const int slot = r0 + col / a.G;
+      u32x4 qv = {0, 0, 0, 0}, gv = {0, 0, 0, 0};
+      if (slot < len) {
+        const long long e = (((long long)b * a.Sq + rows[slot]) * a.Hq + h * a.G + col % a.G) *
+                            kHeadDim;
+        qv = reinterpret_cast<const u32x4*>(a.q + e)[ch];
+        gv = reinterpret_cast<const u32x4*>(a.dout + e)[ch];
+      }
+      qtile[vtile_slot(col, ch)] = qv;
+      gtile[vtile_slot(col, ch)] = gv;
+    }
+    if (tid < 64) {
+      const int slot = r0 + tid / a.G;
+      float l2 = 0.f, dsv = 0.f;
+      int ps = -1;  // no row: every key masked
+      if (slot < len) {
+        const int t = rows[slot], hq = h * a.G + tid % a.G;
+        l2 = a.lse[((long long)b * a.Hq + hq) * a.Sq + t] * kLog2eB;
+        dsv = a.dsum[((long long)b * a.Hq + hq) * a.Sq + t];
+        ps = a.q_start + t;
+      }
+      clse[tid] = l2;
+      cds[tid] = dsv;
+      cpos[tid] = ps;
+    }
+    __syncthreads();
+    // X = Q K^T and Y = dO V^T: M = columns (M-tile mt: columns 16mt + 4g + r
+    // in the result), N = this wave's keys
+    f32x4 x[4], y[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      x[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      y[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 qa = as_bf16x8(qtile[vtile_slot(16 * mt + n, 4 * ks + g)]);
+        const bf16x8 ga = as_bf16x8(gtile[vtile_slot(16 * mt + n, 4 * ks + g)]);
+        x[mt] = mfma16(qa, ks_.qf[ks], x[mt]);
+        y[mt] = mfma16(ga, vs_.qf[ks], y[mt]);
+      }
+    }
+    const int key = key0 + n;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int col = 16 * mt + 4 * g + rr;
+        const float p = (n < nkeys && key <= cpos[col])
+                            ? exp2f(x[mt][rr] * a.scale_log2 - clse[col]) : 0.f;
+        x[mt][rr] = p;                       // P (columns x keys)
+        y[mt][rr] = p * (y[mt][rr] - cds[col]);  // dS
+      }
+    WaveAttn::pv_step(x, gtile, dva);  // dV^T += dO^T P
+    WaveAttn::pv_step(y, qtile, dka);  // dK^T += Q^T dS
+    __syncthreads();                   // tiles free for the next 64 columns
+  }
+  if (n < nkeys) {
+    store_cols_f32(dva, a.dv + (hb * a.Skv + key0 + n) * kHeadDim, 1.f);
+    store_cols_f32(dka, a.dk + (hb * a.Skv + key0 + n) * kHeadDim, a.scale);
+  }
+}
+
+}  // namespace
+
+size_t sparse_bwd_workspace_bytes(const Shape& s) {
+  const size_t nbatch = (size_t)ceil_div(s.Sq, kBatchRows);
+  size_t bytes = 0;
+  bytes += (size_t)s.B * s.Hq * s.Sq * 4;                   // dsum
+  bytes += (size_t)s.B * s.Hkv * nbatch * s.nblk * 4;       // batch counts / offsets
+  bytes += ((size_t)s.B * s.Hkv * s.nblk + 1) * 4;          // list starts
+  bytes += (size_t)s.B * s.Hkv * s.Sq * s.top_k * 4;        // row lists
+  return bytes + 4 * 256;                                    // alignment slack
+}
+
+hipError_t launch_sparse_attn_backward(const Shape& s, const void* q, const void* k, const void* v,
+                                       const int32_t* sel, const void* out, const float* lse,
+                                       const void* dout, float* dq, float* dk, float* dv, void* ws,
+                                       hipStream_t st) {
+  if (s.G > 64 || 64 % s.G != 0) return hipErrorInvalidValue;
+  const int nbatch = ceil_div(s.Sq, kBatchRows);
+  const size_t bm_bytes = (size_t)s.nblk * 8;
+  if (bm_bytes > 160 * 1024) return hipErrorInvalidValue;
+  auto align = [](char* p) { return reinterpret_cast<char*>(((uintptr_t)p + 255) & ~(uintptr_t)255); };
+  char* p = align(static_cast<char*>(ws));
+  float* dsum = reinterpret_cast<float*>(p);
+  p = align(p + (size_t)s.B * s.Hq * s.Sq * 4);
+  int32_t* bcnt = reinterpret_cast<int32_t*>(p);
+  p = align(p + (size_t)s.B * s.Hkv * nbatch * s.nblk * 4);
+  int32_t* base = reinterpret_cast<int32_t*>(p);
+  p = align(p + ((size_t)s.B * s.Hkv * s.nblk + 1) * 4);
+  int32_t* lists = reinterpret_cast<int32_t*>(p);
+  BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+            static_cast<const uint16_t*>(v), sel, static_cast<const uint16_t*>(out), lse,
+            static_cast<const uint16_t*>(dout), dq, dk, dv, dsum, bcnt, base, lists,
+            s.B, s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.G, s.top_k, s.nblk, nbatch,
+            s.scale, s.scale * kLog2eB};
+  hipError_t e;
+  if (bm_bytes > 64 * 1024) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&inverse_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bm_bytes);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&inverse_kernel<true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bm_bytes);
+    if (e != hipSuccess) return e;
+  }
+  const long long nrows = (long long)s.B * s.Sq * s.Hq;
+  dsum_kernel<<<(unsigned)((nrows + 3) / 4), 256, 0, st>>>(a);
+  inverse_kernel<false><<<dim3(nbatch, s.Hkv, s.B), 256, bm_bytes, st>>>(a);
+  batch_scan_kernel<<<dim3(ceil_div(s.nblk, 256), s.B * s.Hkv), 256, 0, st>>>(a);
+  base_scan_kernel<<<1, 256, 0, st>>>(a);
+  inverse_kernel<true><<<dim3(nbatch, s.Hkv, s.B), 256, bm_bytes, st>>>(a);
+  const long long nw = (long long)s.B * s.Hkv * s.Sq;
+  dq_kernel<<<(unsigned)((nw + 3) / 4), 256, 0, st>>>(a);
+  dkdv_kernel<<<dim3(s.nblk, s.Hkv, s.B), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -36,6 +36,15 @@ hipError_t launch_topk_blocks(const Shape& s, const float* scores, const int32_t
 
 // Fused index scoring + running top-k (prefill).
 size_t fused_workspace_bytes(const Shape& s);
+
+// Main-branch gradient (prefill): dq [B][Sq][Hq][128], dk, dv [B][Hkv][Skv][128]
+// in fp32 from q, k, v, dout (bf16), the selection, the forward output (bf16)
+// and log-sum-exp ([B][Hq][Sq]).
+size_t sparse_bwd_workspace_bytes(const Shape& s);
+hipError_t launch_sparse_attn_backward(const Shape& s, const void* q, const void* k, const void* v,
+                                       const int32_t* sel, const void* out, const float* lse,
+                                       const void* dout, float* dq, float* dk, float* dv, void* ws,
+                                       hipStream_t st);
 hipError_t launch_index_topk_fused(const Shape& s, const void* iq, const void* ik, int32_t* sel,
                                    void* ws, hipStream_t st);
 

@@ -109,6 +109,16 @@ def generate(w: Workload, device, *, seed: Optional[int] = None, integer: bool =
     return Inputs(q, k, v, iq, ik, lens)
 
 
+def cotangent(like: torch.Tensor, seed: int) -> torch.Tensor:
+    """Seeded N(0, 1) bf16 tensor shaped like `like` (the output gradient fed
+    to the main branch's backward), drawn on like's device."""
+    gen = torch.Generator(device=like.device)
+    gen.manual_seed(seed)
+    out = torch.empty(like.shape, dtype=torch.bfloat16, device=like.device)
+    _fill(out, gen, False)
+    return out
+
+
 def bf16_bits(t: torch.Tensor):
     """Host numpy uint16 view of a bf16 tensor's bytes (for the oracle)."""
     import numpy as np

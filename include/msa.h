@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 2
+#define MSA_ABI_VERSION 3
 
 typedef enum {
   MSA_OK = 0,
@@ -96,7 +96,8 @@ typedef enum {
   MSA_OP_SPARSE_ATTN_PREFILL = 3,
   MSA_OP_SPARSE_ATTN_DECODE = 4,
   MSA_OP_DENSE_ATTN_PREFILL = 5,
-  MSA_OP_DENSE_ATTN_DECODE = 6
+  MSA_OP_DENSE_ATTN_DECODE = 6,
+  MSA_OP_SPARSE_ATTN_PREFILL_BACKWARD = 7
 } msa_op;
 
 /* Index branch: block scores.  For every sequence b, KV head h, row t and
@@ -203,6 +204,33 @@ msa_status msa_sparse_attn_decode_paged(const msa_problem* p, const void* q,
                                         const int32_t* seq_lens, const int32_t* sel, void* out,
                                         float* lse, void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
+
+/* Gradient of the main branch, prefill (the pages mention kernels written for
+ * training as well as inference without detail: talk summary "How MiniMax M3
+ * Was Built", section "MSA uses a lightweight index branch before sparse
+ * attention").  For the attention msa_sparse_attn_prefill computes over the
+ * selection sel, returns the gradients of sum(dout * out) with respect to q,
+ * k and v; the selection gets none.  Per attended token j of row t, query
+ * head hq: p_j = exp(softmax_scale q.k_j - lse), Dsum = dout . out,
+ * ds_j = p_j (dout . v_j - Dsum); dq = softmax_scale sum_j ds_j k_j,
+ * dk_j += softmax_scale ds_j q, dv_j += p_j dout, summed over every row and
+ * query head that attends j.
+ * Inputs (device): q, dout [B][Sq][Hq][128] bf16; k, v [B][Hkv][Skv][128]
+ * bf16; sel [B][Hkv][Sq][top_k] as for msa_sparse_attn_prefill, with each
+ * block at most once per list; out (bf16, [B][Sq][Hq][128]) and lse (fp32,
+ * [B][Hq][Sq], natural log) as msa_sparse_attn_prefill returned them for
+ * these inputs.  Outputs (device, fp32, fully overwritten): dq
+ * [B][Sq][Hq][128]; dk, dv [B][Hkv][Skv][128] (zero for keys no row attends).
+ * Hq / Hkv must divide 64; seq_kv at most 1310720 (the inverse selection's
+ * block bitmap lives in LDS).  workspace: msa_workspace_bytes(p,
+ * MSA_OP_SPARSE_ATTN_PREFILL_BACKWARD) bytes, any contents.  bf16 products
+ * (P and dS rounded to bf16, as P is in the forward), fp32 accumulation;
+ * deterministic (no floating-point atomics). */
+msa_status msa_sparse_attn_prefill_backward(const msa_problem* p, const void* q, const void* k,
+                                            const void* v, const int32_t* sel, const void* out,
+                                            const float* lse, const void* dout, float* dq,
+                                            float* dk, float* dv, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes an operation needs for problem p (0 if none).  Host only. */
 msa_status msa_workspace_bytes(const msa_problem* p, msa_op op, size_t* bytes);

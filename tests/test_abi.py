@@ -30,7 +30,7 @@ def test_header_declares_entry_points():
               "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_dense_attn_prefill",
               "msa_dense_attn_decode", "msa_workspace_bytes", "msa_status_string",
               "msa_last_error", "msa_abi_version", "msa_index_block_scores_paged",
-              "msa_sparse_attn_decode_paged"]:
+              "msa_sparse_attn_decode_paged", "msa_sparse_attn_prefill_backward"]:
         assert n in names
 
 
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = binding.lib()
-    assert L.msa_abi_version() == 2
+    assert L.msa_abi_version() == 3
     for code, name in binding.STATUS.items():
         assert L.msa_status_string(code).decode() == name
 
@@ -136,13 +136,13 @@ def test_fused_rules():
 def test_workspace_bytes_every_op_and_workload():
     for w in ALL:
         p = prob(w)
-        for op in range(7):
+        for op in range(8):
             is_decode_op = op in (4, 6)
             out = ctypes.c_size_t(12345)
             st, msg = call("msa_workspace_bytes", P(p), op, ctypes.byref(out))
             if is_decode_op and not w.decode:
                 continue  # decode ops need seq_q == 1
-            if op == 2 and w.decode:
+            if op in (2, 7) and w.decode:
                 continue
             assert st == 0, (w.name, op, msg)
     assert call("msa_workspace_bytes", P(prob()), 99, ctypes.byref(ctypes.c_size_t()))[0] == 1
@@ -153,3 +153,32 @@ def test_binding_raises_with_detail():
     p = msa.Problem.from_workload(PREFILL_128K, head_dim=64)
     with pytest.raises(msa.MsaError, match="UNSUPPORTED"):
         msa.msa_workspace_bytes(p, "sparse_attn_prefill")
+
+
+def test_backward_rules():
+    """Host-side checks of the main-branch gradient entry: workspace size,
+    group sizes that do not divide 64, caches too long for the LDS bitmap,
+    missing pointers, rows past the cache."""
+    p = prob()
+    need = ctypes.c_size_t()
+    assert call("msa_workspace_bytes", P(p), 7, ctypes.byref(need))[0] == 0
+    assert need.value > 0
+    args = [A, A, A, A4, A, A4, A, A, A, A]
+    st, msg = call("msa_sparse_attn_prefill_backward", P(p), *args, A, need.value - 1, NULL)
+    assert st == 3, msg
+    st, msg = call("msa_sparse_attn_prefill_backward", P(p), *args, NULL, need.value, NULL)
+    assert st == 1, msg
+    for i in range(len(args)):
+        a = list(args)
+        a[i] = NULL
+        assert call("msa_sparse_attn_prefill_backward", P(p), *a, A, need.value, NULL)[0] == 1, i
+    # 12 query heads over 4 KV heads: G = 3 does not divide 64
+    st, msg = call("msa_sparse_attn_prefill_backward", P(prob(n_q_heads=12)), *args, A,
+                   1 << 40, NULL)
+    assert st == 2 and "divide 64" in msg, msg
+    # the block bitmap of 2M cached tokens does not fit LDS
+    big = prob(CHUNK_1M, seq_kv=2 * 1048576)
+    assert call("msa_workspace_bytes", P(big), 7, ctypes.byref(need))[0] == 2
+    # rows past the cache
+    bad = prob(q_start=1)
+    assert call("msa_workspace_bytes", P(bad), 7, ctypes.byref(need))[0] == 1

@@ -1,0 +1,90 @@
+"""Main-branch gradient (msa_sparse_attn_prefill_backward) against the CPU
+oracle's gradient (oracle_attend_backward) on the GPU's own selection and the
+same bf16 inputs, every element compared.  Sizes span several 64-row batches
+and 64-key blocks with ragged tails, rows that precede k blocks (short, padded
+lists), a chunk whose rows start past 0 with a cache longer than the rows
+(blocks no row reads: their dk, dv must be exactly zero), and query groups of
+4 and 8 heads.
+
+Tolerance, per tensor, from the arithmetic: the kernels round P and dS to
+bf16 (as the forward rounds P) and take Dsum from the bf16 forward output, so
+each term carries a few bf16 roundings (unit roundoff 2^-9) while sums stay in
+fp32.  Errors are measured against the reference's scale: max |gpu - ref| <=
+2e-2 * max |ref| and mean |gpu - ref| <= 4e-3 * mean |ref|."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_gqa_02_amd as msa
+from block_sparse_gqa_02_amd.configs import TINY_PREFILL_2K
+from block_sparse_gqa_02_amd.inputs import cotangent, generate
+import oracle.oracle as O
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL = 2e-2
+MEAN_REL = 4e-3
+
+CASES = {
+    # G = 4, k = 8, 1000 rows (ragged last batch and block), rows < 448 hold short lists
+    "g4_ragged": TINY_PREFILL_2K.shrink(name="bwd_g4", seq_q=1000, seq_kv=1000),
+    # G = 8, two sequences, rows 650..1349 of a 1500-token cache (blocks past the rows)
+    "g8_chunk": TINY_PREFILL_2K.shrink(name="bwd_g8", batch=2, seq_q=700, seq_kv=1500,
+                                       q_start=650, n_q_heads=16, n_kv_heads=2, top_k=6),
+    # G = 8 over 4 KV heads, k larger than the causal block count of most rows
+    "g8_hkv4": TINY_PREFILL_2K.shrink(name="bwd_hkv4", seq_q=520, seq_kv=520, n_q_heads=32,
+                                      n_kv_heads=4, top_k=12),
+}
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def f64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def oprob(w):
+    return O.Problem(w.batch, w.seq_q, w.seq_kv, w.q_start, w.n_q_heads, w.n_kv_heads,
+                     w.head_dim, w.n_idx_heads, w.idx_head_dim, w.block_size, w.top_k, False,
+                     w.softmax_scale)
+
+
+def rel_errors(gpu, ref):
+    d = np.abs(gpu - ref)
+    return float(d.max() / max(np.abs(ref).max(), 1e-30)), float(d.mean() / max(np.abs(ref).mean(), 1e-30))
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_backward_matches_oracle(case):
+    need_gpu()
+    w = CASES[case]
+    print(f"[backward] {case}: B={w.batch} Sq={w.seq_q} Skv={w.seq_kv} q_start={w.q_start} "
+          f"Hq={w.n_q_heads} Hkv={w.n_kv_heads} k={w.top_k}", flush=True)
+    inp = generate(w, "cuda")
+    p = msa.Problem.from_workload(w)
+    bs = msa.msa_index_block_scores(p, inp.iq, inp.ik)
+    sel = msa.msa_topk_blocks(p, bs)
+    lse = torch.empty((w.batch, w.n_q_heads, w.seq_q), dtype=torch.float32, device="cuda")
+    out = msa.msa_sparse_attn_prefill(p, inp.q, inp.k, inp.v, sel, lse=lse)
+    dout = cotangent(out, w.seed + 7)
+    dq, dk, dv = msa.msa_sparse_attn_prefill_backward(p, inp.q, inp.k, inp.v, sel, out, lse, dout)
+    dq2, dk2, dv2 = msa.msa_sparse_attn_prefill_backward(p, inp.q, inp.k, inp.v, sel, out, lse,
+                                                         dout)
+    torch.cuda.synchronize()
+    for a, b, n in ((dq, dq2, "dq"), (dk, dk2, "dk"), (dv, dv2, "dv")):
+        assert torch.equal(a, b), f"{n} differs between two identical calls"
+    sel_rows = sel.permute(0, 2, 1, 3).contiguous().cpu().numpy()  # [B][Sq][Hkv][k]
+    rq, rk, rv = O.attend_backward(oprob(w), f64(inp.q), f64(inp.k), f64(inp.v), f64(dout), None,
+                                   sel_rows)
+    # keys past the last row's position are read by no row: exactly zero
+    last = w.q_start + w.seq_q
+    if last < w.seq_kv:
+        assert not torch.any(dk[:, :, last:]) and not torch.any(dv[:, :, last:])
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        mx, mn = rel_errors(f64(g), r)
+        print(f"  {name}: max {mx:.2e} mean {mn:.2e} (of the reference's max / mean magnitude)",
+              flush=True)
+        assert mx <= MAX_REL and mn <= MEAN_REL, (name, mx, mn)
