@@ -102,15 +102,21 @@ __device__ __forceinline__ void index_sweep(const IndexTile& T, int cbeg, int ce
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    // all eight K fragments first, then the MFMAs: one LDS wait per block
+    bf16x8 kfr[4][2];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int ch = 2 * ks + lane / 32;
-      const bf16x8 k0 = as_bf16x8(L.ktile[buf][ktile_slot(lane % 32, ch)]);
-      const bf16x8 k1 = as_bf16x8(L.ktile[buf][ktile_slot(32 + lane % 32, ch)]);
-      acc[0][0] = mfma32(k0, qf[0][ks], acc[0][0]);
-      acc[0][1] = mfma32(k0, qf[1][ks], acc[0][1]);
-      acc[1][0] = mfma32(k1, qf[0][ks], acc[1][0]);
-      acc[1][1] = mfma32(k1, qf[1][ks], acc[1][1]);
+      kfr[ks][0] = as_bf16x8(L.ktile[buf][ktile_slot(lane % 32, ch)]);
+      kfr[ks][1] = as_bf16x8(L.ktile[buf][ktile_slot(32 + lane % 32, ch)]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      acc[0][0] = mfma32(kfr[ks][0], qf[0][ks], acc[0][0]);
+      acc[0][1] = mfma32(kfr[ks][0], qf[1][ks], acc[0][1]);
+      acc[1][0] = mfma32(kfr[ks][1], qf[0][ks], acc[1][0]);
+      acc[1][1] = mfma32(kfr[ks][1], qf[1][ks], acc[1][1]);
     }
     float m0 = fmaxf(acc[0][0][0], acc[1][0][0]), m1 = fmaxf(acc[0][1][0], acc[1][1][0]);
 #pragma unroll
