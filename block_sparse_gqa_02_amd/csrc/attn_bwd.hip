@@ -243,19 +243,29 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdArgs a) {
                              a.scale);
 }
 
+// s_waitcnt vmcnt(0) with a compiler fence: the LDS-bound loads of the
+// staged columns are complete (for this wave) before anything below.
+__device__ __forceinline__ void wait_all_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xf70);  // vmcnt 0; expcnt, lgkmcnt unconstrained
+  asm volatile("" ::: "memory");
+}
+
 // dK and dV of one block: work-group per (block, KV head, sequence), wave w
 // owns keys 16w..16w+15.  Query columns (row slot i / G, head i % G) are taken
-// 64 at a time from the block's row list.
+// 64 at a time ("chunks") from the block's row list.  Chunk j+1's Q and dO rows
+// travel by LDS-bound loads into the second pair of tiles while chunk j is
+// computed; the row indices that address them are loaded a chunk earlier.
 __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
-  __shared__ u32x4 qtile[kBlock * 16];  // 64 columns x 128 dims, vtile layout
-  __shared__ u32x4 gtile[kBlock * 16];  // the same columns of dO
-  __shared__ float clse[64], cds[64];
-  __shared__ int cpos[64];
+  __shared__ u32x4 qtile[2][kBlock * 16];  // 64 columns x 128 dims, vtile layout
+  __shared__ u32x4 gtile[2][kBlock * 16];  // the same columns of dO
+  __shared__ float clse[2][64], cds[2][64];
+  __shared__ int cpos[2][64];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n = lane % 16, g = lane / 16;
   const long long hb = (long long)b * a.Hkv + h;
-  const int key0 = c * kBlock + 16 * wave;        // this wave's first key
+  const int key0 = c * kBlock + 16 * wave;          // this wave's first key
   const int nkeys = max(0, min(16, a.Skv - key0));  // keys of the wave inside the cache
   const long long koff = (hb * a.Skv + key0) * kHeadDim;
   WaveAttn ks_, vs_;  // K^T and V^T operands: column n = key key0 + n (zero past the cache)
@@ -269,37 +279,67 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
   }
   const int32_t beg = a.base[hb * a.nblk + c], len = a.base[hb * a.nblk + c + 1] - beg;
   const int32_t* rows = a.lists + beg;
-  const int R = 64 / a.G;  // rows per 64 columns
-  for (int r0 = 0; r0 < len; r0 += R) {
-    // stage the 64 columns' Q and dO rows (1024 chunks of 16 bytes each)
-    for (int qd = tid; qd < 64 * 16; qd += 256) {
-      const int col = qd / 16, ch = qd % 16;
-      const int slot = r0 + col / a.G;
-      u32x4 qv = {0, 0, 0, 0}, gv = {0, 0, 0, 0};
-      if (slot < len) {
-        const long long e = (((long long)b * a.Sq + rows[slot]) * a.Hq + h * a.G + col % a.G) *
-                            kHeadDim;
-        qv = reinterpret_cast<const u32x4*>(a.q + e)[ch];
-        gv = reinterpret_cast<const u32x4*>(a.dout + e)[ch];
-      }
-      qtile[vtile_slot(col, ch)] = qv;
-      gtile[vtile_slot(col, ch)] = gv;
+  const int R = 64 / a.G;  // rows per chunk
+  const int nchunk = (len + R - 1) / R;
+  // This thread's four 16-byte slots of a tile: load t of the wave fills slots
+  // 64 (4 wave + t) + lane, i.e. column 4 (4 wave + t) + lane / 16 and, through
+  // the tile's XOR swizzle, dim chunk ch_t.
+  int colt[4], cht[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    colt[t] = 4 * (4 * wave + t) + lane / 16;
+    cht[t] = (lane & 15) ^ (((colt[t] >> 2) & 1) << 3);
+  }
+  // row of column col in chunk j (entries past the list repeat its first row;
+  // their columns are masked through cpos = -1)
+  auto row_of = [&](int j, int col) { return rows[min(j * R + col / a.G, len - 1)]; };
+  int rt[4];          // rows of this thread's slots, next chunk to stage
+  int rmeta = 0;      // row of column tid (tid < 64), next chunk to stage
+  float ml = 0.f, md = 0.f;  // its staged metadata, written at the next iteration
+  int mp = -1;
+  auto stage = [&](int j, int bf) {  // issue chunk j's loads (rows already in rt / rmeta)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const long long e = (((long long)b * a.Sq + rt[t]) * a.Hq + h * a.G + colt[t] % a.G) *
+                          kHeadDim + 8 * cht[t];
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.q + e),
+                                       (__attribute__((address_space(3))) void*)(&qtile[bf][64 * (4 * wave + t)]),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.dout + e),
+                                       (__attribute__((address_space(3))) void*)(&gtile[bf][64 * (4 * wave + t)]),
+                                       16, 0, 0);
     }
     if (tid < 64) {
-      const int slot = r0 + tid / a.G;
-      float l2 = 0.f, dsv = 0.f;
-      int ps = -1;  // no row: every key masked
-      if (slot < len) {
-        const int t = rows[slot], hq = h * a.G + tid % a.G;
-        l2 = a.lse[((long long)b * a.Hq + hq) * a.Sq + t] * kLog2eB;
-        dsv = a.dsum[((long long)b * a.Hq + hq) * a.Sq + t];
-        ps = a.q_start + t;
-      }
-      clse[tid] = l2;
-      cds[tid] = dsv;
-      cpos[tid] = ps;
+      const bool ok = j * R + tid / a.G < len;
+      const long long li = ((long long)b * a.Hq + h * a.G + tid % a.G) * a.Sq + rmeta;
+      ml = ok ? a.lse[li] * kLog2eB : 0.f;
+      md = ok ? a.dsum[li] : 0.f;
+      mp = ok ? a.q_start + rmeta : -1;
+    }
+  };
+  auto fetch_rows = [&](int j) {  // row indices of chunk j into rt / rmeta
+#pragma unroll
+    for (int t = 0; t < 4; ++t) rt[t] = row_of(j, colt[t]);
+    if (tid < 64) rmeta = row_of(j, tid);
+  };
+  if (nchunk > 0) {
+    fetch_rows(0);
+    stage(0, 0);
+    if (nchunk > 1) fetch_rows(1);
+  }
+  for (int j = 0; j < nchunk; ++j) {
+    const int bf = j & 1;
+    wait_all_loads();  // chunk j's tiles (issued last iteration) and its metadata values
+    if (tid < 64) {
+      clse[bf][tid] = ml;
+      cds[bf][tid] = md;
+      cpos[bf][tid] = mp;
     }
     __syncthreads();
+    if (j + 1 < nchunk) {
+      stage(j + 1, bf ^ 1);
+      if (j + 2 < nchunk) fetch_rows(j + 2);
+    }
     // X = Q K^T and Y = dO V^T: M = columns (M-tile mt: columns 16mt + 4g + r
     // in the result), N = this wave's keys
     f32x4 x[4], y[4];
@@ -309,8 +349,8 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
       y[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 qa = as_bf16x8(qtile[vtile_slot(16 * mt + n, 4 * ks + g)]);
-        const bf16x8 ga = as_bf16x8(gtile[vtile_slot(16 * mt + n, 4 * ks + g)]);
+        const bf16x8 qa = as_bf16x8(qtile[bf][vtile_slot(16 * mt + n, 4 * ks + g)]);
+        const bf16x8 ga = as_bf16x8(gtile[bf][vtile_slot(16 * mt + n, 4 * ks + g)]);
         x[mt] = mfma16(qa, ks_.qf[ks], x[mt]);
         y[mt] = mfma16(ga, vs_.qf[ks], y[mt]);
       }
@@ -321,14 +361,14 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int col = 16 * mt + 4 * g + rr;
-        const float p = (n < nkeys && key <= cpos[col])
-                            ? exp2f(x[mt][rr] * a.scale_log2 - clse[col]) : 0.f;
-        x[mt][rr] = p;                       // P (columns x keys)
-        y[mt][rr] = p * (y[mt][rr] - cds[col]);  // dS
+        const float p = (n < nkeys && key <= cpos[bf][col])
+                            ? exp2f(x[mt][rr] * a.scale_log2 - clse[bf][col]) : 0.f;
+        x[mt][rr] = p;                              // P (columns x keys)
+        y[mt][rr] = p * (y[mt][rr] - cds[bf][col]);  // dS
       }
-    WaveAttn::pv_step(x, gtile, dva);  // dV^T += dO^T P
-    WaveAttn::pv_step(y, qtile, dka);  // dK^T += Q^T dS
-    __syncthreads();                   // tiles free for the next 64 columns
+    WaveAttn::pv_step(x, gtile[bf], dva);  // dV^T += dO^T P
+    WaveAttn::pv_step(y, qtile[bf], dka);  // dK^T += Q^T dS
+    __syncthreads();                       // buffers bf free for chunk j + 2
   }
   if (n < nkeys) {
     store_cols_f32(dva, a.dv + (hb * a.Skv + key0 + n) * kHeadDim, 1.f);
