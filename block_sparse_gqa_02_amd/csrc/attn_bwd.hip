@@ -18,10 +18,13 @@
 //                    blocks in LDS (bit i = row i of the batch), counted, scanned
 //                    over batches and over blocks, then filled in row order.
 //                    Deterministic: no atomics outside LDS bit sets.
-//   dq_kernel        one wave per (row, KV head): per selected block
-//                    S^T = K Q^T, dP^T = V dO^T, dS from the saved log-sum-exp,
-//                    dQ^T += K^T dS^T (the forward's PV step with K in the
-//                    V-tile role).
+//   dq_tile_kernel   (groups of 4 or 8 heads) a work-group per 16-row tile
+//                    walks the union of the tile's selected blocks, each
+//                    block's K and V fetched once into LDS; per block and
+//                    wanting row group S^T = K Q^T, dP^T = V dO^T, dS from the
+//                    saved log-sum-exp, dQ^T += K^T dS^T (the forward's PV step
+//                    with K in the V-tile role).
+//   dq_kernel        the same per (row, KV head) wave, for other group sizes.
 //   dkdv_kernel      one work-group per (KV head, block), wave w owning keys
 //                    16w..16w+15: the block's rows are taken 64 query columns
 //                    (rows x group heads) at a time through LDS tiles of Q and
@@ -376,6 +379,148 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
   }
 }
 
+// dQ, tile-union schedule (groups of 4 or 8 query heads): a work-group owns
+// 16 consecutive rows of one (sequence, KV head), split into row groups of
+// 16 / G rows x G heads (the 16 MFMA columns), two groups per wave.  A 32-bit
+// mask per block (LDS) records which of the tile's rows selected it; the
+// work-group walks the blocks with a nonzero mask in ascending order, fetching
+// each one's K and V once into double-buffered LDS tiles by LDS-bound loads
+// (the next block's while the current one is computed).  A group computes a
+// block only if one of its rows selected it, and a column whose row did not
+// gets P = 0.  Per block: S^T = K Q^T and dP^T = V dO^T from the tiles, dS,
+// and dQ^T += K^T dS^T (the PV step with the K tile).
+constexpr int kDqTileRows = 16;  // 4 waves at G = 8: two work-groups share a CU
+
+__global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
+  extern __shared__ u32x4 dqlds[];
+  u32x4* ktiles = dqlds;                      // [2][1024]: K of the current / next block
+  u32x4* vtiles = dqlds + 2 * kBlock * 16;    // [2][1024]: V
+  uint32_t* rmask = reinterpret_cast<uint32_t*>(dqlds + 4 * kBlock * 16);  // [cmax + 1]
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int nwaves = blockDim.x / kWave;
+  const int n = lane % 16, g = lane / 16;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int RPG = 16 / a.G;  // rows per group
+  const int t0 = blockIdx.x * kDqTileRows;
+  const int rows = min(kDqTileRows, a.Sq - t0);
+  const int cmax = (a.q_start + t0 + rows - 1) / kBlock;
+  const long long hb = (long long)b * a.Hkv + h;
+  for (int c = tid; c <= cmax; c += blockDim.x) rmask[c] = 0u;
+  __syncthreads();
+  const int32_t* srow = a.sel + (hb * a.Sq + t0) * a.top_k;
+  for (int idx = tid; idx < rows * a.top_k; idx += blockDim.x) {
+    const int i = idx / a.top_k;
+    const int c = srow[idx];
+    if (c >= 0 && c <= (a.q_start + t0 + i) / kBlock) atomicOr(&rmask[c], 1u << i);
+  }
+  __syncthreads();
+  // this lane's column in each of the wave's two groups
+  bf16x8 qf[2][4], gf[2][4];
+  float lse2[2], dsv[2];
+  int pos[2], rloc[2];
+  long long colbase[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    rloc[j] = (2 * wave + j) * RPG + n / a.G;
+    const bool ok = rloc[j] < rows;
+    const int t = t0 + (ok ? rloc[j] : 0), hq = h * a.G + n % a.G;
+    colbase[j] = ((long long)b * a.Sq + t) * a.Hq + hq;
+    const u32x4* qs = reinterpret_cast<const u32x4*>(a.q + colbase[j] * kHeadDim);
+    const u32x4* gs = reinterpret_cast<const u32x4*>(a.dout + colbase[j] * kHeadDim);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 qv = {0, 0, 0, 0}, gv = {0, 0, 0, 0};
+      if (ok) {
+        qv = qs[4 * ks + g];
+        gv = gs[4 * ks + g];
+      }
+      qf[j][ks] = as_bf16x8(qv);
+      gf[j][ks] = as_bf16x8(gv);
+    }
+    const long long li = ((long long)b * a.Hq + hq) * a.Sq + t;
+    lse2[j] = ok ? a.lse[li] * kLog2eB : 0.f;
+    dsv[j] = ok ? a.dsum[li] : 0.f;
+    pos[j] = ok ? a.q_start + t : -1;
+  }
+  f32x4 acc[2][8];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // first block >= from with a nonzero mask (cmax + 1 if none); same in every wave
+  auto next_block = [&](int from) {
+    for (int base = from; base <= cmax; base += kWave) {
+      const int c = base + lane;
+      const uint64_t bal = ballot(c <= cmax && rmask[c] != 0u);
+      if (bal != 0ull) return base + (int)__builtin_ctzll(bal);
+    }
+    return cmax + 1;
+  };
+  // LDS-bound loads of block c's K and V into tiles bf (swizzled vtile layout)
+  auto fetch = [&](int c, int bf) {
+    const long long off0 = (hb * a.Skv + (long long)c * kBlock) * kHeadDim;
+    for (int inst = wave; inst < 16; inst += nwaves) {
+      const int slot = inst * kWave + lane;
+      const int key = slot >> 4;
+      const int ch = (slot & 15) ^ (((key >> 2) & 1) << 3);
+      const int krow = min(c * kBlock + key, a.Skv - 1) - c * kBlock;  // rows past the cache: masked
+      const long long e = off0 + (long long)krow * kHeadDim + 8 * ch;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.k + e),
+                                       (__attribute__((address_space(3))) void*)(ktiles + bf * 1024 + inst * kWave),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.v + e),
+                                       (__attribute__((address_space(3))) void*)(vtiles + bf * 1024 + inst * kWave),
+                                       16, 0, 0);
+    }
+  };
+  int c = next_block(0), bf = 0;
+  if (c <= cmax) fetch(c, 0);
+  while (c <= cmax) {
+    const int cn = next_block(c + 1);
+    wait_all_loads();
+    __syncthreads();  // block c's tiles complete in every wave
+    if (cn <= cmax) fetch(cn, bf ^ 1);
+    const uint32_t m = rmask[c];
+    const u32x4* kt = ktiles + bf * 1024;
+    const u32x4* vt = vtiles + bf * 1024;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int grp = 2 * wave + j;
+      if (((m >> (grp * RPG)) & ((1u << RPG) - 1u)) == 0u) continue;  // wave-uniform
+      const bool wants = (m >> rloc[j]) & 1u;
+      f32x4 sv[4], dp[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        sv[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 kf = as_bf16x8(kt[vtile_slot(16 * mt + n, 4 * ks + g)]);
+          const bf16x8 vf = as_bf16x8(vt[vtile_slot(16 * mt + n, 4 * ks + g)]);
+          sv[mt] = mfma16(kf, qf[j][ks], sv[mt]);
+          dp[mt] = mfma16(vf, gf[j][ks], dp[mt]);
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int key = c * kBlock + 16 * mt + 4 * g + rr;
+          const float p = (wants && key <= pos[j])
+                              ? exp2f(sv[mt][rr] * a.scale_log2 - lse2[j]) : 0.f;
+          sv[mt][rr] = p * (dp[mt][rr] - dsv[j]);
+        }
+      WaveAttn::pv_step(sv, kt, acc[j]);
+    }
+    __syncthreads();  // tiles bf free for the block after cn
+    c = cn;
+    bf ^= 1;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (rloc[j] < rows) store_cols_f32(acc[j], a.dq + colbase[j] * kHeadDim, a.scale);
+}
+
 }  // namespace
 
 size_t sparse_bwd_workspace_bytes(const Shape& s) {
@@ -425,8 +570,17 @@ hipError_t launch_sparse_attn_backward(const Shape& s, const void* q, const void
   batch_scan_kernel<<<dim3(ceil_div(s.nblk, 256), s.B * s.Hkv), 256, 0, st>>>(a);
   base_scan_kernel<<<1, 256, 0, st>>>(a);
   inverse_kernel<true><<<dim3(nbatch, s.Hkv, s.B), 256, bm_bytes, st>>>(a);
-  const long long nw = (long long)s.B * s.Hkv * s.Sq;
-  dq_kernel<<<(unsigned)((nw + 3) / 4), 256, 0, st>>>(a);
+  if (s.G == 4 || s.G == 8) {
+    const size_t dq_lds = (size_t)4 * kBlock * 16 * 16 + (size_t)s.nblk * 4;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dq_tile_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dq_lds);
+    if (e != hipSuccess) return e;
+    const int waves = (kDqTileRows / (16 / s.G)) / 2;  // two row groups per wave
+    dq_tile_kernel<<<dim3(ceil_div(s.Sq, kDqTileRows), s.Hkv, s.B), waves * kWave, dq_lds, st>>>(a);
+  } else {
+    const long long nw = (long long)s.B * s.Hkv * s.Sq;
+    dq_kernel<<<(unsigned)((nw + 3) / 4), 256, 0, st>>>(a);
+  }
   dkdv_kernel<<<dim3(s.nblk, s.Hkv, s.B), 256, 0, st>>>(a);
   return hipGetLastError();
 }
