@@ -79,7 +79,7 @@ typedef struct {
   int32_t seq_kv;         /* Skv >= 1: token capacity of k, v, ik per sequence */
   int32_t q_start;        /* prefill: position of row 0; ignored in decode */
   int32_t n_q_heads;      /* Hq */
-  int32_t n_kv_heads;     /* Hkv; Hq / Hkv must be 4 or 8 */
+  int32_t n_kv_heads;     /* Hkv in {1, 2, 4}; Hq / Hkv <= 16 (4 and 8 take the tiled kernels) */
   int32_t head_dim;       /* must be 128 */
   int32_t n_idx_heads;    /* must be 4 (the pages' index branch), multiple of Hkv */
   int32_t idx_head_dim;   /* must be 64 */

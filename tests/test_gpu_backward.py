@@ -4,7 +4,8 @@ same bf16 inputs, every element compared.  Sizes span several 64-row batches
 and 64-key blocks with ragged tails, rows that precede k blocks (short, padded
 lists), a chunk whose rows start past 0 with a cache longer than the rows
 (blocks no row reads: their dk, dv must be exactly zero), and query groups of
-4 and 8 heads.
+2, 4, 8 and 16 heads (4 and 8 take the tile-union dq kernel, the others the
+per-row one).
 
 Tolerance, per tensor, from the arithmetic: the kernels round P and dS to
 bf16 (as the forward rounds P) and take Dsum from the bf16 forward output, so
@@ -34,6 +35,11 @@ CASES = {
     # G = 8 over 4 KV heads, k larger than the causal block count of most rows
     "g8_hkv4": TINY_PREFILL_2K.shrink(name="bwd_hkv4", seq_q=520, seq_kv=520, n_q_heads=32,
                                       n_kv_heads=4, top_k=12),
+    # group sizes outside 4 and 8 take the per-row dq kernel
+    "g2_rowwise": TINY_PREFILL_2K.shrink(name="bwd_g2", seq_q=300, seq_kv=300, n_q_heads=8,
+                                         n_kv_heads=4, top_k=3),
+    "g16_rowwise": TINY_PREFILL_2K.shrink(name="bwd_g16", seq_q=400, seq_kv=900, q_start=500,
+                                          n_q_heads=32, n_kv_heads=2, top_k=6),
 }
 
 
