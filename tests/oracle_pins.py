@@ -22,6 +22,9 @@ What pins what:
                          largest score sum, ties to the lexicographically
                          smallest ascending list) and the rank-count formula;
   * golden            -> a hand-derived worked example (tests/golden);
+  * block size 1      -> exact rational token scores, a lexicographic sort for
+                         the selection, library attention under a token mask
+                         (token-level selection, the pages' contrast case);
   * gradient          -> central differences of the fp64 forward, torch
                          autograd of dense causal attention (all blocks kept),
                          and the sum rules over keys (sum of dk = 0, sum of
@@ -467,6 +470,52 @@ def check_backward_invariants(L):
         assert not np.any(a), "zero cotangent, nonzero gradient"
 
 
+# ----------------------------------------------------------------- token level
+def check_token_level_block_size_one(L):
+    """Block size 1 (token-level selection, the ablation the pages contrast
+    with blocks): a block score is the fp32 rounding of the exact token score
+    (max over the attributed index heads), the selection is a plain lexicographic
+    sort (score descending, token ascending) cut at k, and attention is library
+    attention under the mask of the selected tokens; k >= pos + 1 keeps every
+    causal token, i.e. dense attention."""
+    S, Hi, Hkv, Di = 23, 4, 2, 6
+    p = problem(Sq=S, Skv=S, Hq=4, Hkv=Hkv, D=16, Hi=Hi, Di=Di, bs=1, k=5)
+    q, k, v, iq, ik = make(p, 31)
+    iqf = [[[Fraction(float(x)) for x in iq[0, t, i]] for i in range(Hi)] for t in range(S)]
+    ikf = [[Fraction(float(x)) for x in ik[0, j]] for j in range(S)]
+    G = p.n_q_heads // Hkv
+    for t in range(S):
+        got = O.block_scores_row(p, bits(iq), bits(ik), None, 0, t, L=L)
+        sel = np.full((Hkv, p.top_k), -1, np.int32)
+        for h in range(Hkv):
+            for j in range(S):
+                if j < t:
+                    exact = max(sum(a * b for a, b in zip(iqf[t][i], ikf[j]))
+                                for i in range(Hi) if i % Hkv == h)
+                    want = np.float32(float(exact))
+                else:
+                    want = np.float32(np.inf if j == t else -np.inf)
+                assert got[h, j] == want, f"row {t} head {h} token {j}: {got[h, j]} != {want}"
+            order = np.lexsort((np.arange(t + 1), -got[h, : t + 1].astype(np.float64)))
+            m = min(p.top_k, t + 1)
+            want_sel = sorted(order[:m].tolist()) + [-1] * (p.top_k - m)
+            got_sel = O.select_row(p, got[h], t, L=L)
+            assert got_sel.tolist() == want_sel, f"row {t} head {h}: {got_sel} != {want_sel}"
+            sel[h] = got_sel
+        allowed = np.zeros((p.n_q_heads, S), bool)
+        for hq in range(p.n_q_heads):
+            for j in sel[hq // G]:
+                if j >= 0:
+                    allowed[hq, j] = True
+        out, _ = O.attend_row(p, bits(q), bits(k), bits(v), None, sel, 0, t, L=L)
+        close(out, sdpa_row(p, q, k, v, 0, t, t, allowed), 1e-12, f"token attend row {t}")
+        full = np.tile(np.arange(S, dtype=np.int32), (Hkv, 1))
+        full[:, t + 1:] = -1
+        pf = problem(Sq=S, Skv=S, Hq=4, Hkv=Hkv, D=16, Hi=Hi, Di=Di, bs=1, k=S)
+        out, _ = O.attend_row(pf, bits(q), bits(k), bits(v), None, full, 0, t, L=L)
+        close(out, sdpa_row(p, q, k, v, 0, t, t), 1e-12, f"token attend all row {t}")
+
+
 ALL_CHECKS = [check_dense_vs_library, check_attend_vs_masked_library,
               check_all_blocks_equals_dense, check_softmax_closed_forms,
               check_decode_is_last_prefill_row, check_block_scores_integer_closed_form,
@@ -474,4 +523,4 @@ ALL_CHECKS = [check_dense_vs_library, check_attend_vs_masked_library,
               check_planted_winners_per_kv_head, check_select_brute_force,
               check_select_edge_cases, check_golden_hand_example,
               check_backward_finite_differences, check_backward_dense_vs_autograd,
-              check_backward_invariants]
+              check_backward_invariants, check_token_level_block_size_one]
