@@ -45,8 +45,13 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 enum class Mode { kPrefill, kDecode, kEither };
 
-// Common checks; fills the launcher's Shape.  need_k: top_k must be usable.
-msa_status check_problem(const msa_problem* p, Mode mode, bool need_k, msa::Shape* s) {
+// Largest k of a token-level (block size 1) selection.
+constexpr int kMaxTokenTopK = 65536;
+
+// Common checks; fills the launcher's Shape.  need_k: top_k must be usable;
+// tokens: the call also implements block size 1 (prefill positions only).
+msa_status check_problem(const msa_problem* p, Mode mode, bool need_k, msa::Shape* s,
+                         bool tokens = false) {
   if (!p) return fail(MSA_ERR_INVALID_ARGUMENT, "problem is NULL");
   if (p->batch < 1 || p->seq_q < 1 || p->seq_kv < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1 ||
       p->head_dim < 1 || p->n_idx_heads < 1 || p->idx_head_dim < 1 || p->block_size < 1)
@@ -65,13 +70,25 @@ msa_status check_problem(const msa_problem* p, Mode mode, bool need_k, msa::Shap
   // what the kernels implement
   if (p->head_dim != 128) return fail(MSA_ERR_UNSUPPORTED, "head_dim must be 128");
   if (p->idx_head_dim != 64) return fail(MSA_ERR_UNSUPPORTED, "idx_head_dim must be 64");
-  if (p->block_size != 64) return fail(MSA_ERR_UNSUPPORTED, "block_size must be 64");
+  if (p->block_size == 1) {
+    if (!tokens)
+      return fail(MSA_ERR_UNSUPPORTED,
+                  "block_size 1 (token-level selection) is implemented by msa_index_block_scores, "
+                  "msa_topk_blocks and msa_sparse_attn_prefill at prefill positions only");
+    if (mode == Mode::kDecode)
+      return fail(MSA_ERR_UNSUPPORTED, "block_size 1 needs prefill positions (seq_lens == NULL)");
+  } else if (p->block_size != 64) {
+    return fail(MSA_ERR_UNSUPPORTED, "block_size must be 64 (or 1 for token-level selection)");
+  }
   if (p->n_idx_heads != 4) return fail(MSA_ERR_UNSUPPORTED, "n_idx_heads must be 4");
   if (p->n_kv_heads > 4 || 4 % p->n_kv_heads != 0)
     return fail(MSA_ERR_UNSUPPORTED, "n_kv_heads must divide the 4 index heads (1, 2 or 4)");
   const int G = p->n_q_heads / p->n_kv_heads;
   if (G > 16) return fail(MSA_ERR_UNSUPPORTED, "n_q_heads / n_kv_heads must be <= 16");
-  if (need_k && p->top_k > 256) return fail(MSA_ERR_UNSUPPORTED, "top_k must be <= 256");
+  if (need_k && p->block_size == 64 && p->top_k > 256)
+    return fail(MSA_ERR_UNSUPPORTED, "top_k must be <= 256");
+  if (need_k && p->block_size == 1 && p->top_k > kMaxTokenTopK)
+    return fail(MSA_ERR_UNSUPPORTED, "top_k must be <= %d at block_size 1", kMaxTokenTopK);
   if (p->batch > 65535) return fail(MSA_ERR_UNSUPPORTED, "batch must be <= 65535");
   s->B = p->batch;
   s->Sq = p->seq_q;
@@ -82,7 +99,8 @@ msa_status check_problem(const msa_problem* p, Mode mode, bool need_k, msa::Shap
   s->G = G;
   s->top_k = p->top_k;
   s->scale = p->softmax_scale;
-  s->nblk = (p->seq_kv + 63) / 64;
+  s->bs = p->block_size;
+  s->nblk = (p->seq_kv + p->block_size - 1) / p->block_size;
   return MSA_OK;
 }
 
@@ -108,11 +126,14 @@ msa_status msa_index_block_scores(const msa_problem* p, const void* iq, const vo
                                   const int32_t* seq_lens, float* block_scores,
                                   hipStream_t stream) {
   msa::Shape s;
-  msa_status st = check_problem(p, seq_lens ? Mode::kDecode : Mode::kPrefill, false, &s);
+  msa_status st = check_problem(p, seq_lens ? Mode::kDecode : Mode::kPrefill, false, &s, true);
   if (st != MSA_OK) return st;
   NEED_PTR(iq);
   NEED_PTR(ik);
   NEED_PTR4(block_scores);
+  if (s.bs == 1)
+    return launched(msa::launch_token_scores(s, iq, ik, block_scores, stream),
+                    "msa_index_block_scores");
   return launched(msa::launch_index_block_scores(s, iq, ik, seq_lens, block_scores, stream),
                   "msa_index_block_scores");
 }
@@ -120,10 +141,12 @@ msa_status msa_index_block_scores(const msa_problem* p, const void* iq, const vo
 msa_status msa_topk_blocks(const msa_problem* p, const float* block_scores,
                            const int32_t* seq_lens, int32_t* sel, hipStream_t stream) {
   msa::Shape s;
-  msa_status st = check_problem(p, seq_lens ? Mode::kDecode : Mode::kPrefill, true, &s);
+  msa_status st = check_problem(p, seq_lens ? Mode::kDecode : Mode::kPrefill, true, &s, true);
   if (st != MSA_OK) return st;
   NEED_PTR4(block_scores);
   NEED_PTR4(sel);
+  if (s.bs == 1)
+    return launched(msa::launch_token_topk(s, block_scores, sel, stream), "msa_topk_blocks");
   return launched(msa::launch_topk_blocks(s, block_scores, seq_lens, sel, stream),
                   "msa_topk_blocks");
 }
@@ -154,7 +177,7 @@ msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const vo
   (void)workspace;
   (void)workspace_bytes;
   msa::Shape s;
-  msa_status st = check_problem(p, Mode::kPrefill, true, &s);
+  msa_status st = check_problem(p, Mode::kPrefill, true, &s, true);
   if (st != MSA_OK) return st;
   NEED_PTR(q);
   NEED_PTR(k);
@@ -162,6 +185,9 @@ msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const vo
   NEED_PTR4(sel);
   NEED_PTR(out);
   if (lse && !aligned(lse, 4)) return fail(MSA_ERR_INVALID_ARGUMENT, "lse is not 4-byte aligned");
+  if (s.bs == 1)
+    return launched(msa::launch_token_attn_prefill(s, q, k, v, sel, out, lse, stream),
+                    "msa_sparse_attn_prefill");
   return launched(msa::launch_sparse_attn_prefill(s, q, k, v, sel, out, lse, stream),
                   "msa_sparse_attn_prefill");
 }
@@ -306,7 +332,8 @@ msa_status msa_workspace_bytes(const msa_problem* p, msa_op op, size_t* bytes) {
     case MSA_OP_TOPK_BLOCKS:
     case MSA_OP_SPARSE_ATTN_PREFILL:
     case MSA_OP_DENSE_ATTN_PREFILL:
-      st = check_problem(p, Mode::kEither, op == MSA_OP_TOPK_BLOCKS || op == MSA_OP_SPARSE_ATTN_PREFILL, &s);
+      st = check_problem(p, Mode::kEither, op == MSA_OP_TOPK_BLOCKS || op == MSA_OP_SPARSE_ATTN_PREFILL, &s,
+                         op != MSA_OP_DENSE_ATTN_PREFILL);
       if (st != MSA_OK) return st;
       *bytes = 0;
       return ok();

@@ -14,7 +14,8 @@ struct Shape {
   int Hq, Hkv, G;     // query heads, KV heads, Hq / Hkv
   int top_k;
   float scale;        // main-branch softmax scale
-  int nblk;           // ceil(Skv / 64)
+  int nblk;           // ceil(Skv / bs)
+  int bs;             // tokens per selection block: 64, or 1 (token-level selection)
 };
 
 // Paged caches (decode): block c of sequence b lives in page table[b * nblk + c]
@@ -61,6 +62,15 @@ size_t decode_workspace_bytes(const Shape& s, bool dense);
 hipError_t launch_attn_decode(const Shape& s, const void* q, const void* k, const void* v,
                               const int32_t* seq_lens, const int32_t* sel, void* out, float* lse,
                               void* ws, hipStream_t st, const Paging* pg = nullptr);
+
+// Token-level selection (block size 1, prefill positions): token scores
+// [B][Hkv][Sq][Skv] (entries j <= pos written), per-KV-head top-k over them,
+// and attention over the selected tokens.
+hipError_t launch_token_scores(const Shape& s, const void* iq, const void* ik, float* scores,
+                               hipStream_t st);
+hipError_t launch_token_topk(const Shape& s, const float* scores, int32_t* sel, hipStream_t st);
+hipError_t launch_token_attn_prefill(const Shape& s, const void* q, const void* k, const void* v,
+                                     const int32_t* sel, void* out, float* lse, hipStream_t st);
 
 // Dense causal attention (baseline): row-wise (one wave per row and KV head)
 // and tiled (K/V tiles shared by a work-group of rows).

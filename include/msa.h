@@ -24,6 +24,15 @@
  * hq / (n_q_heads / n_kv_heads); inside the own block only keys j <= pos are
  * attended.
  *
+ * Token-level selection (block_size 1), the alternative the pages weigh
+ * blocks against (news write-up, paragraph 6: fewer candidates make top-k
+ * cheaper; talk summary, section "Block-level retrieval makes sparse attention
+ * easier to run on GPUs": blocks keep reads contiguous), is accepted by
+ * msa_index_block_scores, msa_topk_blocks and msa_sparse_attn_prefill at
+ * prefill positions, with the same definitions read at one token per block:
+ * nblk = Skv, block_scores holds one score per token (own token +inf), sel
+ * lists tokens.  Every other entry point rejects it (MSA_ERR_UNSUPPORTED).
+ *
  * Conventions for every entry point:
  *   - Tensors are device pointers (hipMalloc'd or equivalent), densely packed
  *     row-major in the layouts below, 16-byte aligned.  bf16 is IEEE
@@ -63,7 +72,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 3
+#define MSA_ABI_VERSION 4
 
 typedef enum {
   MSA_OK = 0,
@@ -83,8 +92,9 @@ typedef struct {
   int32_t head_dim;       /* must be 128 */
   int32_t n_idx_heads;    /* must be 4 (the pages' index branch), multiple of Hkv */
   int32_t idx_head_dim;   /* must be 64 */
-  int32_t block_size;     /* must be 64 */
-  int32_t top_k;          /* 1..256 blocks per KV head per query (own block included) */
+  int32_t block_size;     /* 64; or 1 = token-level selection (see below) */
+  int32_t top_k;          /* 1..256 blocks per KV head per query (own block included);
+                             1..65536 tokens at block_size 1 */
   float softmax_scale;    /* scale of q.k in the main branch, e.g. 1/sqrt(128) */
 } msa_problem;
 
@@ -145,6 +155,8 @@ msa_status msa_index_topk_fused(const msa_problem* p, const void* iq, const void
  * sel entries must be -1 or in [0, cur(t)] (others give unspecified results,
  * never out-of-range reads); a row whose list is all -1 gets out = 0,
  * lse = -inf.  lse may be NULL.  bf16 operands, fp32 accumulation and softmax.
+ * At block_size 1 a row's list holds distinct tokens and is read up to its
+ * first entry outside [0, pos(t)] (the -1 padding of msa_topk_blocks).
  * Source: topic page "MiniMax稀疏注意力", summary paragraph (exact attention
  * only over the selected blocks). */
 msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const void* k,

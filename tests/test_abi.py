@@ -8,7 +8,7 @@ import pytest
 
 import block_sparse_gqa_02_amd as msa
 from block_sparse_gqa_02_amd import binding
-from block_sparse_gqa_02_amd.configs import ALL, CHUNK_1M, DECODE_32x256K, PREFILL_128K
+from block_sparse_gqa_02_amd.configs import ALL, CHUNK_1M, DECODE_32x256K, PREFILL_128K, PREFILL_32K
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "msa.h")
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = binding.lib()
-    assert L.msa_abi_version() == 3
+    assert L.msa_abi_version() == 4
     for code, name in binding.STATUS.items():
         assert L.msa_status_string(code).decode() == name
 
@@ -147,6 +147,37 @@ def test_workspace_bytes_every_op_and_workload():
             assert st == 0, (w.name, op, msg)
     assert call("msa_workspace_bytes", P(prob()), 99, ctypes.byref(ctypes.c_size_t()))[0] == 1
     assert call("msa_workspace_bytes", P(prob()), 0, None)[0] == 1
+
+
+def test_token_level_rules():
+    """Block size 1 (token-level selection): accepted by the index scores, the
+    top-k and the sparse prefill at prefill positions, with top_k up to 65536
+    tokens; every other entry point and decode positions reject it."""
+    p = prob(PREFILL_32K, block_size=1, top_k=2048)
+    need = ctypes.c_size_t(7)
+    for op in (0, 1, 3):
+        assert call("msa_workspace_bytes", P(p), op, ctypes.byref(need))[0] == 0 and need.value == 0
+    for op in (2, 5, 7):
+        st, msg = call("msa_workspace_bytes", P(p), op, ctypes.byref(need))
+        assert st == 2 and "block_size 1" in msg, (op, msg)
+    st, msg = call("msa_index_topk_fused", P(p), A, A, NULL, A4, A, 1 << 40, NULL)
+    assert st == 2 and "block_size 1" in msg, msg
+    # decode positions
+    d = prob(DECODE_32x256K, block_size=1, top_k=4096)
+    st, msg = call("msa_index_block_scores", P(d), A, A, A4, A4, NULL)
+    assert st == 2 and "prefill" in msg, msg
+    st, msg = call("msa_sparse_attn_decode", P(d), A, A, A, A4, A4, A, NULL, A, 1 << 40, NULL)
+    assert st == 2, msg
+    # k limits: tokens up to 65536, blocks up to 256
+    assert call("msa_topk_blocks", P(prob(PREFILL_32K, block_size=1, top_k=65537)), A4, NULL, A4,
+                NULL)[0] == 2
+    assert call("msa_workspace_bytes", P(prob(PREFILL_32K, block_size=1, top_k=65536)), 1,
+                ctypes.byref(need))[0] == 0
+    assert call("msa_workspace_bytes", P(prob(PREFILL_32K, top_k=2048)), 1,
+                ctypes.byref(need))[0] == 2
+    # pointers are still checked
+    assert call("msa_topk_blocks", P(p), NULL, NULL, A4, NULL)[0] == 1
+    assert call("msa_sparse_attn_prefill", P(p), A, A, A, NULL, A, NULL, NULL, 0, NULL)[0] == 1
 
 
 def test_binding_raises_with_detail():
