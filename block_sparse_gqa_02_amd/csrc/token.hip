@@ -37,6 +37,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kTokSpan = 4096;   // tokens per score wave
 constexpr int kScoreWaves = 4;   // waves per score work-group
 constexpr int kSelThreads = 256; // threads per top-k work-group
+constexpr int kSelE = 8;         // candidates per thread per top-k chunk
 constexpr int kAttnWaves = 4;    // waves per attention work-group
 
 // ----------------------------------------------------------------- scores
@@ -162,9 +163,10 @@ __device__ __forceinline__ uint32_t sum_above(uint32_t v, uint32_t* part, uint32
 }
 
 __global__ void __launch_bounds__(kSelThreads) token_topk_kernel(SelArgs a) {
+  constexpr int W = kSelThreads / kWave;
   __shared__ uint32_t hist[2048];
-  __shared__ uint32_t part[kSelThreads / kWave];
-  __shared__ uint32_t cnt_eq[kSelThreads / kWave], cnt_take[kSelThreads / kWave];
+  __shared__ uint32_t part[W];
+  __shared__ uint32_t cnt_eq[kSelE][W], cnt_take[kSelE][W];
   __shared__ uint32_t found[2];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const long long row = blockIdx.x;  // (b * Hkv + h) * Sq + t
@@ -174,13 +176,26 @@ __global__ void __launch_bounds__(kSelThreads) token_topk_kernel(SelArgs a) {
   const float* src = a.scores + (size_t)row * a.Skv;
   int32_t* dst = a.sel + (size_t)row * a.k;
   const int m = min(a.k, n);
-  // the own token takes the top key whatever the score row holds there
-  auto key = [&](int j) -> uint32_t { return j == pos ? 0xffffffffu : score_key(src[j]); };
 
   if (m == n) {  // every causal token is kept
     for (int x = tid; x < a.k; x += kSelThreads) dst[x] = x < n ? x : -1;
     return;
   }
+  // Keys of one chunk of kSelE * kSelThreads candidates: element e of this
+  // thread is token j0 + e * kSelThreads + tid (every load is a contiguous
+  // 1 KiB run across the work-group, and the kSelE loads are in flight
+  // together).  Tokens past pos read pos's entry and are flagged invalid; the
+  // own token takes the top key whatever the score row holds there.
+  auto load = [&](int j0, uint32_t (&u)[kSelE]) {
+    float f[kSelE];
+#pragma unroll
+    for (int e = 0; e < kSelE; ++e) f[e] = src[min(j0 + e * kSelThreads + tid, pos)];
+#pragma unroll
+    for (int e = 0; e < kSelE; ++e) {
+      const int j = j0 + e * kSelThreads + tid;
+      u[e] = j == pos ? 0xffffffffu : score_key(f[e]);
+    }
+  };
   // radix select of the m-th largest key: after the three digits, `prefix`
   // is that key T and `rem` the number of keys equal to T still to take
   uint32_t prefix = 0, pmask = 0, rem = (uint32_t)m;
@@ -189,9 +204,13 @@ __global__ void __launch_bounds__(kSelThreads) token_topk_kernel(SelArgs a) {
     const int nb = pass == 2 ? 1024 : 2048;
     for (int x = tid; x < 2048; x += kSelThreads) hist[x] = 0;
     __syncthreads();
-    for (int j = tid; j < n; j += kSelThreads) {
-      const uint32_t u = key(j);
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
+    for (int j0 = 0; j0 < n; j0 += kSelE * kSelThreads) {
+      uint32_t u[kSelE];
+      load(j0, u);
+#pragma unroll
+      for (int e = 0; e < kSelE; ++e)
+        if (j0 + e * kSelThreads + tid < n && (u[e] & pmask) == prefix)
+          atomicAdd(&hist[(u[e] >> shift) & (nb - 1)], 1u);
     }
     __syncthreads();
     const int per = nb / kSelThreads;
@@ -220,35 +239,58 @@ __global__ void __launch_bounds__(kSelThreads) token_topk_kernel(SelArgs a) {
   }
   const uint32_t T = prefix;
 
-  // ascending emission: keys above T, then the first `rem` keys equal to T
+  // ascending emission: keys above T, then the first `rem` keys equal to T.
+  // Token order within a chunk is (e, wave, lane), so an element's rank is
+  // the counts of the earlier sub-chunks, of the lower waves in its own, and
+  // of the lower lanes of its wave.
   uint32_t base_eq = 0, base_out = 0;
-  for (int j0 = 0; j0 < n; j0 += kSelThreads) {
-    const int j = j0 + tid;
-    const uint32_t u = j < n ? key(j) : 0u;
-    const bool gt = j < n && u > T;
-    const bool eq = j < n && u == T;
-    const uint64_t eb = ballot(eq);
-    if (lane == 0) cnt_eq[wave] = (uint32_t)__popcll(eb);
-    __syncthreads();
-    uint32_t eq_before = base_eq + (uint32_t)prefix_count(eb), eq_total = 0;
+  for (int j0 = 0; j0 < n; j0 += kSelE * kSelThreads) {
+    uint32_t u[kSelE];
+    load(j0, u);
+    uint64_t eb[kSelE];
 #pragma unroll
-    for (int w = 0; w < kSelThreads / kWave; ++w) {
-      if (w < wave) eq_before += cnt_eq[w];
-      eq_total += cnt_eq[w];
+    for (int e = 0; e < kSelE; ++e) {
+      const bool ok = j0 + e * kSelThreads + tid < n;
+      eb[e] = ballot(ok && u[e] == T);
     }
-    const bool take = gt || (eq && eq_before < rem);
-    const uint64_t tb = ballot(take);
-    if (lane == 0) cnt_take[wave] = (uint32_t)__popcll(tb);
-    __syncthreads();
-    uint32_t out_before = base_out + (uint32_t)prefix_count(tb), take_total = 0;
+    if (lane == 0) {
 #pragma unroll
-    for (int w = 0; w < kSelThreads / kWave; ++w) {
-      if (w < wave) out_before += cnt_take[w];
-      take_total += cnt_take[w];
+      for (int e = 0; e < kSelE; ++e) cnt_eq[e][wave] = (uint32_t)__popcll(eb[e]);
     }
-    if (take && out_before < (uint32_t)a.k) dst[out_before] = j;  // always < m; the bound guards the row
-    base_eq += eq_total;
-    base_out += take_total;
+    __syncthreads();
+    uint64_t tb[kSelE];
+    uint32_t run = base_eq;
+#pragma unroll
+    for (int e = 0; e < kSelE; ++e) {
+      uint32_t before = run + (uint32_t)prefix_count(eb[e]);
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        if (w < wave) before += cnt_eq[e][w];
+        run += cnt_eq[e][w];
+      }
+      const bool ok = j0 + e * kSelThreads + tid < n;
+      const bool eq = (eb[e] >> lane) & 1ull;
+      tb[e] = ballot((ok && u[e] > T) || (eq && before < rem));
+    }
+    base_eq = run;
+    if (lane == 0) {
+#pragma unroll
+      for (int e = 0; e < kSelE; ++e) cnt_take[e][wave] = (uint32_t)__popcll(tb[e]);
+    }
+    __syncthreads();
+    run = base_out;
+#pragma unroll
+    for (int e = 0; e < kSelE; ++e) {
+      uint32_t at = run + (uint32_t)prefix_count(tb[e]);
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        if (w < wave) at += cnt_take[e][w];
+        run += cnt_take[e][w];
+      }
+      // at < m always; the bound keeps a write inside the row regardless
+      if (((tb[e] >> lane) & 1ull) && at < (uint32_t)a.k) dst[at] = j0 + e * kSelThreads + tid;
+    }
+    base_out = run;
   }
   for (int x = m + tid; x < a.k; x += kSelThreads) dst[x] = -1;
 }
