@@ -1,0 +1,71 @@
+"""The decode step (index block scores -> top-k -> split-K sparse attention and
+its merge) captured once as a HIP graph and replayed, the serving form of the
+step: one launch per step and no host work.  The library allocates,
+synchronises and clears nothing itself, so the captured kernels are exactly
+the eager ones.  Every replay, with eager library work on other inputs between
+replays, must give the eager step's selection, output and LSE bit for bit, and
+the output must match the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_gqa_02_amd as msa
+from block_sparse_gqa_02_amd.configs import DECODE_32x256K
+from block_sparse_gqa_02_amd.inputs import bf16_bits, generate
+import oracle.oracle as O
+import parity as PAR
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def test_decode_step_graph_replays_match_eager():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w = DECODE_32x256K.shrink(batch=6, seq_kv=6000, top_k=12)
+    lens = [6000, 1, 65, 4097, 3000, 64]
+    inp = generate(w, DEV, seed=17, seq_lens=lens)
+    other = generate(w, DEV, seed=18, seq_lens=lens)
+    p = msa.Problem.from_workload(w)
+    bs = torch.empty((w.batch, w.n_kv_heads, 1, w.nblk), dtype=torch.float32, device=DEV)
+    sel = torch.empty((w.batch, w.n_kv_heads, 1, w.top_k), dtype=torch.int32, device=DEV)
+    out = torch.empty_like(inp.q)
+    lse = torch.empty((w.batch, w.n_q_heads, 1), dtype=torch.float32, device=DEV)
+    ws = torch.empty(msa.msa_workspace_bytes(p, "sparse_attn_decode"), dtype=torch.uint8,
+                     device=DEV)
+
+    def step(x):
+        msa.msa_index_block_scores(p, x.iq, x.ik, x.seq_lens, bs)
+        msa.msa_topk_blocks(p, bs, x.seq_lens, sel)
+        msa.msa_sparse_attn_decode(p, x.q, x.k, x.v, x.seq_lens, sel, out, lse, ws)
+
+    step(inp)
+    torch.cuda.synchronize()
+    want = (sel.clone(), out.clone(), lse.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(inp)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(inp)
+    torch.cuda.synchronize()
+    for r in range(4):
+        step(other)  # eager work on other inputs rewrites every buffer
+        torch.cuda.synchronize()
+        assert not torch.equal(out.view(torch.int16), want[1].view(torch.int16))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(sel, want[0]), f"replay {r}: selection"
+        assert torch.equal(out.view(torch.int16), want[1].view(torch.int16)), f"replay {r}: output"
+        assert torch.equal(lse, want[2]), f"replay {r}: lse"
+    po = O.Problem(w.batch, 1, w.seq_kv, 0, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_idx_heads,
+                   w.idx_head_dim, w.block_size, w.top_k, True, w.softmax_scale)
+    q, k, v = bf16_bits(inp.q), bf16_bits(inp.k), bf16_bits(inp.v)
+    sl = np.array(lens, dtype=np.int32)
+    sel_h, out_h = sel.cpu().numpy(), out.float().cpu().numpy()
+    for b in range(w.batch):
+        o, _ = O.attend_row(po, q, k, v, sl, sel_h[b, :, 0], b, 0)
+        PAR.assert_attention_close(out_h[b, 0], o, f"seq {b}")
