@@ -174,8 +174,6 @@ msa_status msa_index_topk_fused(const msa_problem* p, const void* iq, const void
 msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const void* k,
                                    const void* v, const int32_t* sel, void* out, float* lse,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   msa::Shape s;
   msa_status st = check_problem(p, Mode::kPrefill, true, &s, true);
   if (st != MSA_OK) return st;
@@ -188,7 +186,13 @@ msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const vo
   if (s.bs == 1)
     return launched(msa::launch_token_attn_prefill(s, q, k, v, sel, out, lse, stream),
                     "msa_sparse_attn_prefill");
-  return launched(msa::launch_sparse_attn_prefill(s, q, k, v, sel, out, lse, stream),
+  const size_t need = msa::sparse_prefill_workspace_bytes(s);
+  if (need > 0) {
+    NEED_PTR(workspace);
+    if (workspace_bytes < need)
+      return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  }
+  return launched(msa::launch_sparse_attn_prefill(s, q, k, v, sel, out, lse, workspace, stream),
                   "msa_sparse_attn_prefill");
 }
 
@@ -330,12 +334,16 @@ msa_status msa_workspace_bytes(const msa_problem* p, msa_op op, size_t* bytes) {
   switch (op) {
     case MSA_OP_INDEX_BLOCK_SCORES:
     case MSA_OP_TOPK_BLOCKS:
-    case MSA_OP_SPARSE_ATTN_PREFILL:
     case MSA_OP_DENSE_ATTN_PREFILL:
-      st = check_problem(p, Mode::kEither, op == MSA_OP_TOPK_BLOCKS || op == MSA_OP_SPARSE_ATTN_PREFILL, &s,
+      st = check_problem(p, Mode::kEither, op == MSA_OP_TOPK_BLOCKS, &s,
                          op != MSA_OP_DENSE_ATTN_PREFILL);
       if (st != MSA_OK) return st;
       *bytes = 0;
+      return ok();
+    case MSA_OP_SPARSE_ATTN_PREFILL:
+      st = check_problem(p, Mode::kPrefill, true, &s, true);
+      if (st != MSA_OK) return st;
+      *bytes = s.bs == 1 ? 0 : msa::sparse_prefill_workspace_bytes(s);
       return ok();
     case MSA_OP_INDEX_TOPK_FUSED:
       st = check_problem(p, Mode::kPrefill, true, &s);

@@ -232,13 +232,19 @@ int decode_nsplit(const Shape& s, bool dense) {
 
 }  // namespace
 
+size_t sparse_prefill_workspace_bytes(const Shape& s) {
+  return union_prefill_supported(s) ? union_prefill_workspace_bytes(s) : 0;
+}
+
 hipError_t launch_sparse_attn_prefill(const Shape& s, const void* q, const void* k, const void* v,
-                                      const int32_t* sel, void* out, float* lse, hipStream_t st) {
+                                      const int32_t* sel, void* out, float* lse, void* ws,
+                                      hipStream_t st) {
   PrefillArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                 static_cast<const uint16_t*>(v), sel, static_cast<uint16_t*>(out), lse,
                 s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.G, s.top_k, s.scale * kLog2e,
                 (long long)s.B * s.Hkv * s.Sq};
-  if (sel && union_prefill_supported(s)) return launch_union_prefill(s, q, k, v, sel, out, lse, st);
+  if (sel && union_prefill_supported(s))
+    return launch_union_prefill(s, q, k, v, sel, out, lse, ws, st);
   const long long grid = (a.units + kAttnWaves - 1) / kAttnWaves;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   sparse_prefill_kernel<<<(unsigned)grid, 256, 0, st>>>(a);
@@ -248,7 +254,7 @@ hipError_t launch_sparse_attn_prefill(const Shape& s, const void* q, const void*
 hipError_t launch_dense_attn_prefill_rowwise(const Shape& s, const void* q, const void* k,
                                              const void* v, void* out, float* lse,
                                              hipStream_t st) {
-  return launch_sparse_attn_prefill(s, q, k, v, nullptr, out, lse, st);
+  return launch_sparse_attn_prefill(s, q, k, v, nullptr, out, lse, nullptr, st);
 }
 
 size_t decode_workspace_bytes(const Shape& s, bool dense) {

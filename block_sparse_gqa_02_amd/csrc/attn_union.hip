@@ -31,12 +31,17 @@
 // the kernel stops waiting and stores NaN outputs (a caller-visible failure,
 // never a hang).
 //
-// LDS layouts (256-byte rows, 16-byte chunks).  K: chunk c of row r sits at
+// V arrives transposed.  A pre-pass writes, for every context block, a 16 KiB
+// V^T tile: 128 dim rows of 64 keys, the keys of each 32-key half permuted so
+// that the eight keys one lane feeds to the PV product (k-slots 8g .. 8g+7 of
+// a K-step) are adjacent.  The ring then holds V^T, and every V operand is one
+// plain 16-byte LDS read instead of two transposing 8-byte reads.
+//
+// LDS layouts (16-byte chunks).  K (256-byte rows): chunk c of row r sits at
 // chunk c ^ (r & 15), so the 16 rows of an S-tile read at one chunk hit 16
-// distinct chunks.  V: chunk c of row r sits at chunk c ^ ((r & 7) << 1); the V
-// operand of O^T += V^T P^T is read with ds_read_b64_tr_b16, which hands each
-// lane of a 16-lane group one dim of four consecutive keys, and the swizzle
-// spreads the 16 rows of one such read evenly over the banks.
+// distinct chunks.  V^T (128-byte rows): chunk c of row r sits at chunk
+// c ^ ((r >> 1) & 7); the 16 dim rows of one operand read then cover all 16
+// chunk positions of a 256-byte bank line.
 #include "common.h"
 #include "kernels.h"
 
@@ -58,20 +63,62 @@ constexpr int kRsrcFlags = 0x00020000;              // raw buffer descriptor wor
 struct UnionArgs {
   const uint16_t* q;    // [B][Sq][Hq][128]
   const uint16_t* k;    // [B][Hkv][Skv][128]
-  const uint16_t* v;
+  const uint16_t* vt;   // [B][Hkv][nblk_ctx] V^T tiles of 16 KiB
   const int32_t* sel;   // [B][Hkv][Sq][k]
   uint16_t* out;        // [B][Sq][Hq][128]
   float* lse;           // [B][Hq][Sq] or null
-  int Sq, Skv, q_start, Hq, Hkv, top_k, ntiles;
+  int Sq, Skv, q_start, Hq, Hkv, top_k, ntiles, nblk_ctx;
   float scale_log2;
 };
 
+// V^T tile of block c: position 32kv + 8g + i of dim row d holds V[64c + 32kv +
+// 16(i/4) + 4g + i%4][d], the key of k-slot 8g + i of K-step kv in the PV
+// product.  Keys at or past the context end (q_start + Sq) repeat the last
+// context row: their probabilities are exactly zero, and the copy keeps them
+// finite whatever the cache holds beyond the context.
+struct VtArgs {
+  const uint16_t* v;    // [B][Hkv][Skv][128]
+  uint16_t* vt;         // [B][Hkv][nblk_ctx][128][64]
+  int Skv, ctx, nblk_ctx;
+};
+
+__global__ void __launch_bounds__(256) vt_kernel(VtArgs a) {
+  // V block in LDS: chunk ch (dims 8ch .. 8ch+7) of key k at slot k*16 + (ch ^ (k & 15))
+  __shared__ u32x4 blk[kBlock * 16];
+  const long long tl = blockIdx.x;  // (b * Hkv + h) * nblk_ctx + c
+  const int c = (int)(tl % a.nblk_ctx);
+  const long long head = tl / a.nblk_ctx;
+  const u32x4* src = reinterpret_cast<const u32x4*>(a.v + head * a.Skv * kHeadDim);
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = i * 256 + tid;  // chunk q of the block: key q / 16, dim chunk q % 16
+    const int key = q >> 4, ch = q & 15;
+    const int row = min(c * kBlock + key, a.ctx - 1);
+    blk[key * 16 + (ch ^ (key & 15))] = src[(size_t)row * 16 + ch];
+  }
+  __syncthreads();
+  const uint16_t* b16 = reinterpret_cast<const uint16_t*>(blk);
+  u32x4* dst = reinterpret_cast<u32x4*>(a.vt + tl * (kBlock * kHeadDim));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = i * 256 + tid;  // chunk q of the tile: dim q / 8, positions 8(q % 8) .. +7
+    const int d = q >> 3, kv = (q >> 2) & 1, g = q & 3;
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int k0 = 32 * kv + 16 * (e / 4) + 4 * g + (e % 4);  // position e; e + 1 is k0 + 1
+      const uint32_t x0 = b16[(k0 * 16 + ((d >> 3) ^ (k0 & 15))) * 8 + (d & 7)];
+      const uint32_t x1 = b16[((k0 + 1) * 16 + ((d >> 3) ^ ((k0 + 1) & 15))) * 8 + (d & 7)];
+      w[e / 2] = x0 | (x1 << 16);
+    }
+    dst[q] = w;
+  }
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
 __device__ __forceinline__ int kswz(int row) { return row & 15; }
-__device__ __forceinline__ int vswz(int row) { return (row & 7) << 1; }
 
 __device__ __forceinline__ void cbarrier() { asm volatile("" ::: "memory"); }
 
@@ -153,7 +200,8 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.k + head * a.Skv * kHeadDim), (short)0, a.Skv * kHeadDim * 2, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.v + head * a.Skv * kHeadDim), (short)0, a.Skv * kHeadDim * 2, kRsrcFlags);
+      (void*)(a.vt + head * a.nblk_ctx * (kBlock * kHeadDim)), (short)0,
+      a.nblk_ctx * kBlockBytes, kRsrcFlags);
   const __amdgpu_buffer_rsrc_t rtag = __builtin_amdgcn_make_buffer_rsrc(
       (void*)&kEntryIds, (short)0, (int)sizeof(kEntryIds), kRsrcFlags);
   const int32_t* selh = a.sel + (head * a.Sq + t0) * a.top_k;
@@ -182,18 +230,22 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
   }
   if (tid == 0) failed = 0;
 
-  // Ring fill.  Instruction j of a block (64 lanes x 16 B) covers rows 4j..4j+3:
-  // lane -> row 4j + lane/16, LDS chunk lane%16, which holds the row's chunk
-  // (lane%16) ^ swz(row).  Blocks wholly at or before every tile row's position
-  // take precomputed per-lane offsets (the swizzles depend on j mod 4 / mod 2);
-  // the diagonal block re-reads its last used row in place of later ones.
-  int koff[4], voff[2];
+  // Ring fill.  K instruction j of a block (64 lanes x 16 B) covers rows
+  // 4j..4j+3: lane -> row 4j + lane/16, LDS chunk lane%16, which holds the
+  // row's chunk (lane%16) ^ kswz(row).  Blocks wholly at or before every tile
+  // row's position take precomputed per-lane offsets (the swizzle depends on
+  // j mod 4); the diagonal block re-reads its last used row in place of later
+  // ones.  V^T instruction j covers dim rows 8j..8j+7: lane -> row
+  // 8j + lane/8, LDS chunk lane%8, which holds chunk (lane%8) ^ ((row >> 1) & 7)
+  // (depends on j mod 2).
+  int koff[4];
 #pragma unroll
   for (int jm = 0; jm < 4; ++jm) {
     const int row = 4 * jm + lane / 16;
     koff[jm] = (lane / 16) * 256 + 16 * ((lane % 16) ^ kswz(row));
-    if (jm < 2) voff[jm] = (lane / 16) * 256 + 16 * ((lane % 16) ^ vswz(row));
   }
+  auto vtoff = [&](int j) { return (lane / 8) * 128 + 16 * ((lane % 8) ^ ((4 * j + lane / 16) & 7)); };
+  const int voff[2] = {vtoff(0), vtoff(1)};
   auto fetch_full = [&](int c, int sl) {
     const int sb = c * kBlockBytes;
     if (c * kBlock + kBlock - 1 <= pos_last) {
@@ -207,7 +259,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
       for (int j = 0; j < 16; ++j) {
         const int row = 4 * j + lane / 16, srow = min(row, last);
         load_lds16(rk, &ktile[sl][j * kWave], srow * 256 + 16 * ((lane % 16) ^ kswz(row)), sb);
-        load_lds16(rv, &vtile[sl][j * kWave], srow * 256 + 16 * ((lane % 16) ^ vswz(row)), sb);
+        load_lds16(rv, &vtile[sl][j * kWave], vtoff(j), sb + j * 1024);
       }
     }
   };
@@ -217,7 +269,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
     for (int j = j0; j < j1; ++j) {
       const int row = 4 * j + lane / 16, srow = min(row, last);
       load_lds16(rk, &ktile[sl][j * kWave], srow * 256 + 16 * ((lane % 16) ^ kswz(row)), sb);
-      load_lds16(rv, &vtile[sl][j * kWave], srow * 256 + 16 * ((lane % 16) ^ vswz(row)), sb);
+      load_lds16(rv, &vtile[sl][j * kWave], vtoff(j), sb + j * 1024);
     }
   };
 
@@ -225,17 +277,14 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
   int kbyte[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) kbyte[ks] = n * 256 + (((4 * ks + g) ^ n) << 4);
-  // V operand (transposed read): lane (g, n) of the read for M-tile mt, K-step
-  // kv and half hf loads dims 16mt + 4(n%4) .. +3 of key 32kv + 16hf + 4g + n/4,
-  // and the read returns to lane (g, n) dim 16mt + n of keys 32kv + 16hf + 4g +
-  // 0..3.  With that key's swizzle the byte offset in the tile is
-  //   (32kv + 16hf) * 256 + (vlane ^ 32mt).
-  const int r7 = (4 * g + n / 4) & 7;
-  const int vlane = (4 * g + n / 4) * 256 + 32 * r7 + 16 * ((n >> 1) & 1) + 8 * (n & 1);
+  // V^T operand: lane (g, n) of M-tile mt, K-step kv reads dim row 16mt + n,
+  // chunk 4kv + g (k-slots 8g .. 8g+7), stored at chunk (4kv + g) ^ (n >> 1):
+  // byte 2048 mt + (vlane ^ 64 kv).
+  const int vlane = n * 128 + 16 * (g ^ (n >> 1));
 
   auto compute = [&](int sl, int c, uint32_t gm, const uint32_t* rm) {
     const char* kt = reinterpret_cast<const char*>(&ktile[sl][0]);
-    const uint32_t vt = lds_addr(&vtile[sl][0]);
+    const char* vt = reinterpret_cast<const char*>(&vtile[sl][0]);
     const int key0 = c * kBlock + 4 * g;
 #pragma unroll
     for (int j = 0; j < kGPW; ++j) {
@@ -310,10 +359,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
       // 32kv + 16(e/4) + 4g + e%4, matching this lane's own P registers.  V
       // fragments are read three (K-step, M-tile) steps ahead of their multiply.
       auto vfrag = [&](int kv, int mt) {
-        const uint32_t va = vt + (uint32_t)(vlane ^ (32 * mt)) + (32 * kv) * 256;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)va);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)(va + 16 * 256));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        return as_bf16x8(*reinterpret_cast<const u32x4*>(vt + mt * 2048 + (vlane ^ (64 * kv))));
       };
       bf16x8 vf[4];
       vf[0] = vfrag(0, 0);
@@ -465,17 +511,31 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
 
 bool union_prefill_supported(const Shape& s) { return s.G == 8 || s.G == 4; }
 
+static int context_blocks(const Shape& s) { return ceil_div(s.q_start + s.Sq, kBlock); }
+
+size_t union_prefill_workspace_bytes(const Shape& s) {
+  return (size_t)s.B * s.Hkv * context_blocks(s) * kBlockBytes;
+}
+
 hipError_t launch_union_prefill(const Shape& s, const void* q, const void* k, const void* v,
-                                const int32_t* sel, void* out, float* lse, hipStream_t st) {
+                                const int32_t* sel, void* out, float* lse, void* ws,
+                                hipStream_t st) {
   const int TR = kNG * 16 / s.G;
   const int ntiles = ceil_div(s.Sq, TR);
-  // the buffer descriptors address one head's K or V with 32-bit byte offsets
+  const int nblk_ctx = context_blocks(s);
+  // the buffer descriptors address one head's K or V^T with 32-bit byte offsets
   if ((long long)s.Skv * kHeadDim * 2 > 0x7fffffffLL) return hipErrorInvalidValue;
-  UnionArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-              static_cast<const uint16_t*>(v), sel, static_cast<uint16_t*>(out), lse,
-              s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.top_k, ntiles, s.scale * kLog2e};
+  const long long tiles_vt = (long long)s.B * s.Hkv * nblk_ctx;
   const long long grid = (long long)ntiles * s.Hkv * s.B;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (grid > 0x7fffffffLL || tiles_vt > 0x7fffffffLL) return hipErrorInvalidValue;
+  VtArgs t{static_cast<const uint16_t*>(v), static_cast<uint16_t*>(ws), s.Skv, s.q_start + s.Sq,
+           nblk_ctx};
+  vt_kernel<<<(unsigned)tiles_vt, 256, 0, st>>>(t);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  UnionArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+              static_cast<const uint16_t*>(ws), sel, static_cast<uint16_t*>(out), lse,
+              s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.top_k, ntiles, nblk_ctx, s.scale * kLog2e};
   if (s.G == 8) union_prefill_kernel<8><<<(unsigned)grid, kWaves * kWave, 0, st>>>(a);
   else if (s.G == 4) union_prefill_kernel<4><<<(unsigned)grid, kWaves * kWave, 0, st>>>(a);
   else return hipErrorInvalidValue;

@@ -49,14 +49,18 @@ hipError_t launch_sparse_attn_backward(const Shape& s, const void* q, const void
 hipError_t launch_index_topk_fused(const Shape& s, const void* iq, const void* ik, int32_t* sel,
                                    void* ws, hipStream_t st);
 
-// Sparse attention.
+// Sparse attention.  ws: sparse_prefill_workspace_bytes(s) bytes (the
+// tile-union kernel's transposed V tiles; unused by the row-wise kernel).
+size_t sparse_prefill_workspace_bytes(const Shape& s);
 hipError_t launch_sparse_attn_prefill(const Shape& s, const void* q, const void* k,
                                       const void* v, const int32_t* sel, void* out, float* lse,
-                                      hipStream_t st);
+                                      void* ws, hipStream_t st);
 // Tile-union schedule of the sparse prefill (used for G = 4 and 8).
 bool union_prefill_supported(const Shape& s);
+size_t union_prefill_workspace_bytes(const Shape& s);
 hipError_t launch_union_prefill(const Shape& s, const void* q, const void* k, const void* v,
-                                const int32_t* sel, void* out, float* lse, hipStream_t st);
+                                const int32_t* sel, void* out, float* lse, void* ws,
+                                hipStream_t st);
 size_t decode_workspace_bytes(const Shape& s, bool dense);
 // sel == NULL: dense; pg: k and v are pools of [num_pages][Hkv][64][128] pages.
 hipError_t launch_attn_decode(const Shape& s, const void* q, const void* k, const void* v,

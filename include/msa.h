@@ -157,6 +157,11 @@ msa_status msa_index_topk_fused(const msa_problem* p, const void* iq, const void
  * lse = -inf.  lse may be NULL.  bf16 operands, fp32 accumulation and softmax.
  * At block_size 1 a row's list holds distinct tokens and is read up to its
  * first entry outside [0, pos(t)] (the -1 padding of msa_topk_blocks).
+ * workspace: msa_workspace_bytes(p, MSA_OP_SPARSE_ATTN_PREFILL) bytes, any
+ * content (may be NULL when that is 0).  For n_q_heads / n_kv_heads of 4 or 8
+ * at block_size 64 it receives a transposed copy of V's context blocks,
+ * B * n_kv_heads * ceil((q_start + seq_q) / 64) * 16 KiB, which the kernel
+ * streams instead of V.
  * Source: topic page "MiniMax稀疏注意力", summary paragraph (exact attention
  * only over the selected blocks). */
 msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const void* k,

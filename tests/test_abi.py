@@ -149,6 +149,26 @@ def test_workspace_bytes_every_op_and_workload():
     assert call("msa_workspace_bytes", P(prob()), 0, None)[0] == 1
 
 
+def test_sparse_prefill_workspace_rules():
+    """The tiled sparse prefill (G = 4 or 8) needs a workspace of one 16 KiB
+    transposed V tile per (sequence, KV head, context block); the row-wise
+    kernel (other G) and token-level selection need none."""
+    p = prob()  # 128K, G = 8
+    need = ctypes.c_size_t()
+    assert call("msa_workspace_bytes", P(p), 3, ctypes.byref(need))[0] == 0
+    assert need.value == 1 * 4 * (131072 // 64) * 16384
+    st, msg = call("msa_sparse_attn_prefill", P(p), A, A, A, A4, A, NULL, A, need.value - 1, NULL)
+    assert st == 3 and "workspace" in msg, msg
+    st, msg = call("msa_sparse_attn_prefill", P(p), A, A, A, A4, A, NULL, NULL, need.value, NULL)
+    assert st == 1, msg
+    chunk = prob(CHUNK_1M)  # context = q_start + seq_q = 1048576 tokens
+    assert call("msa_workspace_bytes", P(chunk), 3, ctypes.byref(need))[0] == 0
+    assert need.value == 4 * (1048576 // 64) * 16384
+    for kw in (dict(n_q_heads=8), dict(block_size=1, top_k=4096)):  # G = 2; tokens
+        assert call("msa_workspace_bytes", P(prob(**kw)), 3, ctypes.byref(need))[0] == 0
+        assert need.value == 0, kw
+
+
 def test_token_level_rules():
     """Block size 1 (token-level selection): accepted by the index scores, the
     top-k and the sparse prefill at prefill positions, with top_k up to 65536
