@@ -388,8 +388,24 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
 // (the next block's while the current one is computed).  A group computes a
 // block only if one of its rows selected it, and a column whose row did not
 // gets P = 0.  Per block: S^T = K Q^T and dP^T = V dO^T from the tiles, dS,
-// and dQ^T += K^T dS^T (the PV step with the K tile).
+// and dQ^T += K^T dS^T.
+//
+// Tile layout: chunk c (16 bytes) of key row r sits at chunk c ^ (r & 15), so
+// the 16 rows of an S^T or dP^T operand read hit 16 distinct chunks.  The K^T
+// operand of dQ^T is read with ds_read_b64_tr_b16: lane (g, n) of the read for
+// K-step kv, half hf and M-tile mt loads dims 16mt + 4(n%4) .. +3 of key
+// 32kv + 16hf + 4g + n/4 and receives dim 16mt + n of keys 32kv + 16hf + 4g +
+// 0..3, so k-slot i of the operand is key 32kv + 16(i/4) + 4g + i%4, the key
+// of the lane's own dS^T register.  dQ^T M-tile mt, register r is dim
+// 16mt + 4g + r of column n.
 constexpr int kDqTileRows = 16;  // 4 waves at G = 8: two work-groups share a CU
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+__device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
 
 __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
   extern __shared__ u32x4 dqlds[];
@@ -456,13 +472,14 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
     }
     return cmax + 1;
   };
-  // LDS-bound loads of block c's K and V into tiles bf (swizzled vtile layout)
+  // LDS-bound loads of block c's K and V into tiles bf: load inst writes key
+  // rows 4 inst .. 4 inst + 3, lane -> row 4 inst + lane/16, stored chunk lane%16
   auto fetch = [&](int c, int bf) {
     const long long off0 = (hb * a.Skv + (long long)c * kBlock) * kHeadDim;
     for (int inst = wave; inst < 16; inst += nwaves) {
       const int slot = inst * kWave + lane;
       const int key = slot >> 4;
-      const int ch = (slot & 15) ^ (((key >> 2) & 1) << 3);
+      const int ch = (slot & 15) ^ (key & 15);
       const int krow = min(c * kBlock + key, a.Skv - 1) - c * kBlock;  // rows past the cache: masked
       const long long e = off0 + (long long)krow * kHeadDim + 8 * ch;
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.k + e),
@@ -473,6 +490,9 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
                                        16, 0, 0);
     }
   };
+  // K^T operand of dQ^T: byte (32kv + 16hf) * 256 + (vlane ^ 32mt) of the K tile
+  const int r15 = 4 * g + n / 4;
+  const int vlane = r15 * 256 + 16 * (((n >> 1) & 1) ^ r15) + 8 * (n & 1);
   int c = next_block(0), bf = 0;
   if (c <= cmax) fetch(c, 0);
   while (c <= cmax) {
@@ -495,8 +515,8 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
         dp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 kf = as_bf16x8(kt[vtile_slot(16 * mt + n, 4 * ks + g)]);
-          const bf16x8 vf = as_bf16x8(vt[vtile_slot(16 * mt + n, 4 * ks + g)]);
+          const bf16x8 kf = as_bf16x8(kt[(16 * mt + n) * 16 + ((4 * ks + g) ^ n)]);
+          const bf16x8 vf = as_bf16x8(vt[(16 * mt + n) * 16 + ((4 * ks + g) ^ n)]);
           sv[mt] = mfma16(kf, qf[j][ks], sv[mt]);
           dp[mt] = mfma16(vf, gf[j][ks], dp[mt]);
         }
@@ -510,7 +530,26 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
                               ? exp2f(sv[mt][rr] * a.scale_log2 - lse2[j]) : 0.f;
           sv[mt][rr] = p * (dp[mt][rr] - dsv[j]);
         }
-      WaveAttn::pv_step(sv, kt, acc[j]);
+      // dQ^T += K^T dS^T over two K-steps of 32 keys
+      const uint32_t kb = lds_byte_addr(kt);
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) {
+        u32x4 pw;
+        pw[0] = pack_bf16x2(sv[2 * kv][0], sv[2 * kv][1]);
+        pw[1] = pack_bf16x2(sv[2 * kv][2], sv[2 * kv][3]);
+        pw[2] = pack_bf16x2(sv[2 * kv + 1][0], sv[2 * kv + 1][1]);
+        pw[3] = pack_bf16x2(sv[2 * kv + 1][2], sv[2 * kv + 1][3]);
+        const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const uint32_t va = kb + (uint32_t)(32 * kv * 256) + (uint32_t)(vlane ^ (32 * mt));
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)va);
+          const s16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)(va + 16 * 256));
+          const bf16x8 kf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[j][mt] = mfma16(kf, pb, acc[j][mt]);
+        }
+      }
     }
     __syncthreads();  // tiles bf free for the block after cn
     c = cn;
@@ -518,7 +557,12 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    if (rloc[j] < rows) store_cols_f32(acc[j], a.dq + colbase[j] * kHeadDim, a.scale);
+    if (rloc[j] < rows) {
+      float* dst = a.dq + colbase[j] * kHeadDim + 4 * g;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        *reinterpret_cast<f32x4*>(dst + 16 * mt) = acc[j][mt] * a.scale;
+    }
 }
 
 }  // namespace

@@ -255,3 +255,31 @@ def test_fused_equals_separate_and_oracle(name, ov, integer):
         for hh in range(w.n_kv_heads):
             PAR.check_selection_row(sel_h[0, hh, t], o_sc[t, hh], cur, w.top_k, integer,
                                     f"{name} row {t} head {hh}")
+
+
+@pytest.mark.parametrize("heads", [(32, 4), (8, 2), (8, 4)], ids=["g8_tiled", "g4_tiled", "g2_rowwise"])
+def test_prefill_ignores_cache_rows_past_the_context(heads):
+    """Rows of K and V at or past q_start + seq_q belong to no query's context:
+    filling them with NaN must leave the output and LSE bit-identical (the
+    tiled kernel's transposed V tiles repeat the last context row there, the
+    diagonal K fetch re-reads the last used row, the row-wise kernel stops at
+    the query)."""
+    need_gpu()
+    hq, hkv = heads
+    w = TINY_PREFILL_2K.shrink(seq_q=300, seq_kv=1000, q_start=610, n_q_heads=hq, n_kv_heads=hkv,
+                               top_k=6)
+    inp = generate(w, DEV, seed=77)
+    p = msa.Problem.from_workload(w)
+    sel = msa.msa_topk_blocks(p, msa.msa_index_block_scores(p, inp.iq, inp.ik))
+    lse_a = torch.empty((1, w.n_q_heads, w.seq_q), dtype=torch.float32, device=DEV)
+    lse_b = torch.empty_like(lse_a)
+    a = msa.msa_sparse_attn_prefill(p, inp.q, inp.k, inp.v, sel, lse=lse_a)
+    ctx = w.q_start + w.seq_q
+    k2, v2 = inp.k.clone(), inp.v.clone()
+    k2[:, :, ctx:] = float("nan")
+    v2[:, :, ctx:] = float("nan")
+    b = msa.msa_sparse_attn_prefill(p, inp.q, k2, v2, sel, lse=lse_b)
+    torch.cuda.synchronize()
+    assert torch.isfinite(a.float()).all()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(lse_a, lse_b)
