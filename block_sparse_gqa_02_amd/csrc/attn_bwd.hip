@@ -80,6 +80,59 @@ __device__ __forceinline__ void store_cols_f32(const f32x4 (&acc)[8], float* col
     }
 }
 
+// LDS tiles of the tiled gradient kernels: 64 rows x 128 bf16, chunk c (16
+// bytes) of row r at chunk c ^ (r & 15), so the 16 rows of a 16-byte operand
+// read (one chunk column) hit 16 distinct chunks.
+__device__ __forceinline__ int swz_slot(int row, int ch) { return row * 16 + (ch ^ (row & 15)); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+__device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// acc += T^T P^T over one tile T (swz_slot layout; its 64 rows are the
+// contraction index) with P^T in S^T register layout: pt[mt] register r is
+// tile row 16mt + 4g + r, column n; rounded to bf16 here.  The T^T operand is
+// read with ds_read_b64_tr_b16: lane (g, n) of the read for K-step kv, half hf
+// and M-tile mt loads dims 16mt + 4(n%4) .. +3 of tile row 32kv + 16hf + 4g +
+// n/4 and receives dim 16mt + n of rows 32kv + 16hf + 4g + 0..3, so k-slot i
+// of the operand is row 32kv + 16(i/4) + 4g + i%4, the row of the lane's own
+// P^T register.  acc[mt] register r is dim 16mt + 4g + r of column n.
+__device__ __forceinline__ void pv_tr(const f32x4 (&pt)[4], const u32x4* tile, f32x4 (&acc)[8]) {
+  const int lane = lane_id(), n = lane % 16, g = lane / 16;
+  // byte (32kv + 16hf) * 256 + (vlane ^ 32mt) of the tile
+  const int r15 = 4 * g + n / 4;
+  const int vlane = r15 * 256 + 16 * (((n >> 1) & 1) ^ r15) + 8 * (n & 1);
+  const uint32_t tb = lds_byte_addr(tile);
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    u32x4 pw;
+    pw[0] = pack_bf16x2(pt[2 * kv][0], pt[2 * kv][1]);
+    pw[1] = pack_bf16x2(pt[2 * kv][2], pt[2 * kv][3]);
+    pw[2] = pack_bf16x2(pt[2 * kv + 1][0], pt[2 * kv + 1][1]);
+    pw[3] = pack_bf16x2(pt[2 * kv + 1][2], pt[2 * kv + 1][3]);
+    const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const uint32_t va = tb + (uint32_t)(32 * kv * 256) + (uint32_t)(vlane ^ (32 * mt));
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)va);
+      const s16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)(va + 16 * 256));
+      const bf16x8 tf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[mt] = mfma16(tf, pb, acc[mt]);
+    }
+  }
+}
+
+// acc in pv_tr's layout; writes column n's 128 dims times mul.
+__device__ __forceinline__ void store_tr_f32(const f32x4 (&acc)[8], float* col_base, float mul) {
+  const int g = lane_id() / 16;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(col_base + 16 * mt + 4 * g) = acc[mt] * mul;
+}
+
 // Dsum[b][hq][t] = sum_d dout * out; one wave per (b, t, hq), lanes over dim pairs.
 __global__ void __launch_bounds__(256) dsum_kernel(BwdArgs a) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -260,7 +313,7 @@ __device__ __forceinline__ void wait_all_loads() {
 // travel by LDS-bound loads into the second pair of tiles while chunk j is
 // computed; the row indices that address them are loaded a chunk earlier.
 __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
-  __shared__ u32x4 qtile[2][kBlock * 16];  // 64 columns x 128 dims, vtile layout
+  __shared__ u32x4 qtile[2][kBlock * 16];  // 64 columns x 128 dims, swz_slot layout
   __shared__ u32x4 gtile[2][kBlock * 16];  // the same columns of dO
   __shared__ float clse[2][64], cds[2][64];
   __shared__ int cpos[2][64];
@@ -291,7 +344,7 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     colt[t] = 4 * (4 * wave + t) + lane / 16;
-    cht[t] = (lane & 15) ^ (((colt[t] >> 2) & 1) << 3);
+    cht[t] = (lane & 15) ^ (colt[t] & 15);
   }
   // row of column col in chunk j (entries past the list repeat its first row;
   // their columns are masked through cpos = -1)
@@ -352,8 +405,8 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
       y[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 qa = as_bf16x8(qtile[bf][vtile_slot(16 * mt + n, 4 * ks + g)]);
-        const bf16x8 ga = as_bf16x8(gtile[bf][vtile_slot(16 * mt + n, 4 * ks + g)]);
+        const bf16x8 qa = as_bf16x8(qtile[bf][swz_slot(16 * mt + n, 4 * ks + g)]);
+        const bf16x8 ga = as_bf16x8(gtile[bf][swz_slot(16 * mt + n, 4 * ks + g)]);
         x[mt] = mfma16(qa, ks_.qf[ks], x[mt]);
         y[mt] = mfma16(ga, vs_.qf[ks], y[mt]);
       }
@@ -369,13 +422,13 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
         x[mt][rr] = p;                              // P (columns x keys)
         y[mt][rr] = p * (y[mt][rr] - cds[bf][col]);  // dS
       }
-    WaveAttn::pv_step(x, gtile[bf], dva);  // dV^T += dO^T P
-    WaveAttn::pv_step(y, qtile[bf], dka);  // dK^T += Q^T dS
+    pv_tr(x, gtile[bf], dva);  // dV^T += dO^T P
+    pv_tr(y, qtile[bf], dka);  // dK^T += Q^T dS
     __syncthreads();                       // buffers bf free for chunk j + 2
   }
   if (n < nkeys) {
-    store_cols_f32(dva, a.dv + (hb * a.Skv + key0 + n) * kHeadDim, 1.f);
-    store_cols_f32(dka, a.dk + (hb * a.Skv + key0 + n) * kHeadDim, a.scale);
+    store_tr_f32(dva, a.dv + (hb * a.Skv + key0 + n) * kHeadDim, 1.f);
+    store_tr_f32(dka, a.dk + (hb * a.Skv + key0 + n) * kHeadDim, a.scale);
   }
 }
 
@@ -390,22 +443,10 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
 // gets P = 0.  Per block: S^T = K Q^T and dP^T = V dO^T from the tiles, dS,
 // and dQ^T += K^T dS^T.
 //
-// Tile layout: chunk c (16 bytes) of key row r sits at chunk c ^ (r & 15), so
-// the 16 rows of an S^T or dP^T operand read hit 16 distinct chunks.  The K^T
-// operand of dQ^T is read with ds_read_b64_tr_b16: lane (g, n) of the read for
-// K-step kv, half hf and M-tile mt loads dims 16mt + 4(n%4) .. +3 of key
-// 32kv + 16hf + 4g + n/4 and receives dim 16mt + n of keys 32kv + 16hf + 4g +
-// 0..3, so k-slot i of the operand is key 32kv + 16(i/4) + 4g + i%4, the key
-// of the lane's own dS^T register.  dQ^T M-tile mt, register r is dim
-// 16mt + 4g + r of column n.
+// The K and V tiles use the swz_slot layout; dQ^T += K^T dS^T is pv_tr with
+// the K tile.
 constexpr int kDqTileRows = 16;  // 4 waves at G = 8: two work-groups share a CU
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
-
-__device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
 
 __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
   extern __shared__ u32x4 dqlds[];
@@ -490,9 +531,6 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
                                        16, 0, 0);
     }
   };
-  // K^T operand of dQ^T: byte (32kv + 16hf) * 256 + (vlane ^ 32mt) of the K tile
-  const int r15 = 4 * g + n / 4;
-  const int vlane = r15 * 256 + 16 * (((n >> 1) & 1) ^ r15) + 8 * (n & 1);
   int c = next_block(0), bf = 0;
   if (c <= cmax) fetch(c, 0);
   while (c <= cmax) {
@@ -515,8 +553,8 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
         dp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 kf = as_bf16x8(kt[(16 * mt + n) * 16 + ((4 * ks + g) ^ n)]);
-          const bf16x8 vf = as_bf16x8(vt[(16 * mt + n) * 16 + ((4 * ks + g) ^ n)]);
+          const bf16x8 kf = as_bf16x8(kt[swz_slot(16 * mt + n, 4 * ks + g)]);
+          const bf16x8 vf = as_bf16x8(vt[swz_slot(16 * mt + n, 4 * ks + g)]);
           sv[mt] = mfma16(kf, qf[j][ks], sv[mt]);
           dp[mt] = mfma16(vf, gf[j][ks], dp[mt]);
         }
@@ -530,26 +568,7 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
                               ? exp2f(sv[mt][rr] * a.scale_log2 - lse2[j]) : 0.f;
           sv[mt][rr] = p * (dp[mt][rr] - dsv[j]);
         }
-      // dQ^T += K^T dS^T over two K-steps of 32 keys
-      const uint32_t kb = lds_byte_addr(kt);
-#pragma unroll
-      for (int kv = 0; kv < 2; ++kv) {
-        u32x4 pw;
-        pw[0] = pack_bf16x2(sv[2 * kv][0], sv[2 * kv][1]);
-        pw[1] = pack_bf16x2(sv[2 * kv][2], sv[2 * kv][3]);
-        pw[2] = pack_bf16x2(sv[2 * kv + 1][0], sv[2 * kv + 1][1]);
-        pw[3] = pack_bf16x2(sv[2 * kv + 1][2], sv[2 * kv + 1][3]);
-        const bf16x8 pb = as_bf16x8(pw);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-          const uint32_t va = kb + (uint32_t)(32 * kv * 256) + (uint32_t)(vlane ^ (32 * mt));
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)va);
-          const s16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)(va + 16 * 256));
-          const bf16x8 kf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[j][mt] = mfma16(kf, pb, acc[j][mt]);
-        }
-      }
+      pv_tr(sv, kt, acc[j]);  // dQ^T += K^T dS^T
     }
     __syncthreads();  // tiles bf free for the block after cn
     c = cn;
@@ -557,12 +576,7 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    if (rloc[j] < rows) {
-      float* dst = a.dq + colbase[j] * kHeadDim + 4 * g;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-        *reinterpret_cast<f32x4*>(dst + 16 * mt) = acc[j][mt] * a.scale;
-    }
+    if (rloc[j] < rows) store_tr_f32(acc[j], a.dq + colbase[j] * kHeadDim, a.scale);
 }
 
 }  // namespace
