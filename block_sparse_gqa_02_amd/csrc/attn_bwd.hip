@@ -30,7 +30,8 @@
 //                    (rows x group heads) at a time through LDS tiles of Q and
 //                    dO; X = Q K^T, Y = dO V^T, then dV^T += dO^T P and
 //                    dK^T += Q^T dS, again the forward's PV step.
-// Operand layouts and the PV step are those of attn_block.h.
+// Score-side operand layouts follow attn_block.h; the products with a transposed
+// tile (dQ^T += K^T dS^T, dV^T += dO^T P, dK^T += Q^T dS) use pv_tr below.
 #include "attn_block.h"
 #include "common.h"
 #include "kernels.h"
@@ -64,20 +65,6 @@ __device__ __forceinline__ float wave_sum64(float v) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
   return v;
-}
-
-// acc has the O^T layout of attn_block.h (M-tile 4hf + j, row 4g + r = dim
-// 64hf + 16g + 4r + j of column n); writes column n's 128 dims times mul.
-__device__ __forceinline__ void store_cols_f32(const f32x4 (&acc)[8], float* col_base, float mul) {
-  const int g = lane_id() / 16;
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const f32x4 v = {acc[4 * hf + 0][r] * mul, acc[4 * hf + 1][r] * mul,
-                       acc[4 * hf + 2][r] * mul, acc[4 * hf + 3][r] * mul};
-      *reinterpret_cast<f32x4*>(col_base + 64 * hf + 16 * g + 4 * r) = v;
-    }
 }
 
 // LDS tiles of the tiled gradient kernels: 64 rows x 128 bf16, chunk c (16
@@ -240,7 +227,7 @@ __global__ void __launch_bounds__(256) base_scan_kernel(BwdArgs a) {
 // dQ: one wave per (sequence, KV head, row); columns n < G are the group's
 // query heads.
 __global__ void __launch_bounds__(256) dq_kernel(BwdArgs a) {
-  __shared__ u32x4 ktile[4][kBlock * 16];  // per wave: the block's K in the vtile layout
+  __shared__ u32x4 ktile[4][kBlock * 16];  // per wave: the block's K in the swz_slot layout
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int n = lane % 16, g = lane / 16;
   const long long w = (long long)blockIdx.x * 4 + wave;  // ((b * Hkv + h) * Sq + t)
@@ -269,7 +256,11 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdArgs a) {
     u32x4 vr[16], vk[4][4];
     WaveAttn::load_v(a.k + off, last, vr);   // K, for the LDS tile
     WaveAttn::load_k(a.v + off, last, vk);   // V, as the A operand of dP^T
-    WaveAttn::store_v(vr, tile);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {  // chunk q = 64 i + lane: key q / 16, dim chunk q % 16
+      const int q = i * kWave + lane;
+      tile[swz_slot(q >> 4, q & 15)] = vr[i];
+    }
     __builtin_amdgcn_wave_barrier();
     f32x4 s[4], dp[4];
 #pragma unroll
@@ -278,7 +269,7 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdArgs a) {
       dp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 kf = as_bf16x8(tile[vtile_slot(16 * mt + n, 4 * ks + g)]);
+        const bf16x8 kf = as_bf16x8(tile[swz_slot(16 * mt + n, 4 * ks + g)]);
         s[mt] = mfma16(kf, qs.qf[ks], s[mt]);
         dp[mt] = mfma16(as_bf16x8(vk[mt][ks]), gs.qf[ks], dp[mt]);
       }
@@ -292,11 +283,11 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdArgs a) {
         const float p = (col_ok && key <= pos) ? exp2f(s[mt][rr] * a.scale_log2 - lse2) : 0.f;
         s[mt][rr] = p * (dp[mt][rr] - ds0);
       }
-    WaveAttn::pv_step(s, tile, acc);
+    pv_tr(s, tile, acc);  // dQ^T += K^T dS^T
     __builtin_amdgcn_wave_barrier();  // tile reads done before the next block's writes
   }
-  if (col_ok) store_cols_f32(acc, a.dq + (((long long)b * a.Sq + t) * a.Hq + hq0 + n) * kHeadDim,
-                             a.scale);
+  if (col_ok) store_tr_f32(acc, a.dq + (((long long)b * a.Sq + t) * a.Hq + hq0 + n) * kHeadDim,
+                           a.scale);
 }
 
 // s_waitcnt vmcnt(0) with a compiler fence: the LDS-bound loads of the
