@@ -91,6 +91,8 @@ struct WaveAttn {
       vr[s] = vb[min(q / 16, last) * 16 + q % 16];
     }
   }
+  // Stream: non-temporal loads, for data read once (decode caches).
+  template <bool Stream = false>
   __device__ __forceinline__ static void load_k(const uint16_t* k_blk, int last,
                                                 u32x4 (&kr)[4][4]) {
     const int lane = lane_id(), n = lane % 16, g = lane / 16;
@@ -98,12 +100,16 @@ struct WaveAttn {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kr[mt][ks] = kb[min(16 * mt + n, last) * 16 + 4 * ks + g];
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4* src = kb + min(16 * mt + n, last) * 16 + 4 * ks + g;
+        kr[mt][ks] = Stream ? __builtin_nontemporal_load(src) : *src;
+      }
   }
   // The V block straight into an LDS tile (laid out as store_v lays it out)
   // with 16-byte LDS-bound loads: load t writes slots 64t .. 64t+63, so lane
   // i fetches the chunk that belongs at slot 64t + i.  The data is in LDS once
-  // these 16 loads have completed (vmcnt).
+  // these 16 loads have completed (vmcnt).  The loads are non-temporal (the
+  // decode caches are read once).
   __device__ __forceinline__ static void load_v_lds(const uint16_t* v_blk, int last, u32x4* tile) {
     const int lane = lane_id();
     const u32x4* vb = reinterpret_cast<const u32x4*>(v_blk);
@@ -114,7 +120,7 @@ struct WaveAttn {
       const int ch = (slot & 15) ^ (((key >> 2) & 1) << 3);  // vtile_slot is its own inverse
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vb + min(key, last) * 16 + ch),
                                        (__attribute__((address_space(3))) void*)(tile + t * kWave),
-                                       16, 0, 0);
+                                       16, 0, kCachePolicyNT);
     }
   }
   // Copies the V block into this wave's LDS tile.  The previous block's reads

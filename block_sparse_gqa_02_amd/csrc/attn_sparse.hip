@@ -159,7 +159,7 @@ __global__ void __launch_bounds__(256) decode_partial_kernel(DecodeArgs a) {
     long long off;
     next(c, off);
     WaveAttn::load_v_lds(a.v + off, last_row(c), vtile[wave][0]);
-    WaveAttn::load_k(a.k + off, last_row(c), kr);
+    WaveAttn::load_k<true>(a.k + off, last_row(c), kr);
     while (todo != 0ull) {
       int cn;
       long long offn;
@@ -168,7 +168,7 @@ __global__ void __launch_bounds__(256) decode_partial_kernel(DecodeArgs a) {
                 [&] {
                   __builtin_amdgcn_sched_barrier(0);  // keep the loads after the S products
                   WaveAttn::load_v_lds(a.v + offn, last_row(cn), vtile[wave][buf ^ 1]);
-                  WaveAttn::load_k(a.k + offn, last_row(cn), kr);
+                  WaveAttn::load_k<true>(a.k + offn, last_row(cn), kr);
                 },
                 [] { wait_vmcnt<32>(); });
       c = cn;

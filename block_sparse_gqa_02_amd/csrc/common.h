@@ -72,6 +72,14 @@ __device__ __forceinline__ int prefix_count(uint64_t mask) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// Cache-policy operand of the LDS-bound load builtins: the non-temporal bit.
+constexpr int kCachePolicyNT = 2;
+
+// The value of lane l ^ 1 (DPP quad permutation 1, 0, 3, 2).
+__device__ __forceinline__ float swap_lane_pairs(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xb1, 0xf, 0xf, false));
+}
+
 // Reductions over the four lanes l, l^16, l^32, l^48 (the same MFMA column
 // in every 16-lane row), with lane swaps instead of LDS permutes:
 // v_permlane16_swap pairs rows 0/1 and 2/3, v_permlane32_swap the two halves.

@@ -19,7 +19,7 @@
 //
 // Decode kernel: one query per sequence; the index-K cache is streamed from
 // HBM once, each wave taking a run of blocks, with v_mfma_f32_16x16x32_bf16
-// (keys on M, the 4 index heads on N).
+// (half-keys on M, half index heads on N, so that loads read whole cache rows).
 #include "common.h"
 #include "index_sweep.h"
 #include "kernels.h"
@@ -89,16 +89,19 @@ index_scores_decode_kernel(IndexArgs a) {
   if (blockIdx.x == 0 && wave == 0 && lane < HKV) out[(size_t)lane * a.nblk + cur] = __builtin_huge_valf();
   if (cbeg >= cend) return;
 
-  // B operand: column n = index head (n < 4), lane group g = l/16 holds dims
-  // 32ks + 8g .. +7 for K-step ks.
+  // One K-step per M-tile, with each 64-dim key split over two operand rows:
+  // A-operand row v of M-tile mt is dims 32(v & 1) .. +31 of key 8mt + v/2, so
+  // the eight lanes that hold one key read its whole 128-byte row and every
+  // load instruction reads one contiguous KiB of the cache.  B-operand column
+  // 2i + h holds dims 32h .. 32h+31 of index head i (columns 8..15 are zero);
+  // the products of a half-row with the other half's column are never used.
   const int n = lane % 16, g = lane / 16;
-  bf16x8 qf[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  bf16x8 qf;
+  {
     u32x4 v = {0, 0, 0, 0};
-    if (n < kIdxHeads)
-      v = reinterpret_cast<const u32x4*>(a.iq + ((size_t)b * kIdxHeads + n) * kIdxDim)[4 * ks + g];
-    qf[ks] = as_bf16x8(v);
+    if (n < 2 * kIdxHeads)
+      v = reinterpret_cast<const u32x4*>(a.iq + ((size_t)b * kIdxHeads + (n >> 1)) * kIdxDim)[4 * (n & 1) + g];
+    qf = as_bf16x8(v);
   }
   const u32x4* ikb = reinterpret_cast<const u32x4*>(a.ik + (size_t)b * a.Skv * kIdxDim);
   // index-K block c: contiguous cache, or its page (ids outside the pool read
@@ -114,32 +117,34 @@ index_scores_decode_kernel(IndexArgs a) {
     const int pg = a.pages[(size_t)b * a.nblk + c];
     return pg >= 0 && pg < a.num_pages;
   };
-  // two blocks per step: 16 independent 16-byte loads in flight per lane
-  auto load = [&](int c, u32x4 (&kr)[4][2]) {
-    const u32x4* base = block_base(c);
+  // two blocks per step: 16 independent 16-byte loads in flight per lane.  The
+  // cache is read once, so the loads are non-temporal.
+  auto load = [&](int c, u32x4 (&kr)[8]) {
+    const u32x4* base = block_base(c) + 8 * (n >> 1) + 4 * (n & 1) + g;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) kr[mt][ks] = base[(16 * mt + n) * 8 + 4 * ks + g];
+    for (int mt = 0; mt < 8; ++mt) kr[mt] = __builtin_nontemporal_load(base + 64 * mt);
   };
-  auto score = [&](int c, const u32x4 (&kr)[4][2]) {
-    // A operand: M-tile mt holds keys 64c + 16mt + (l%16), same dim mapping.
+  auto score = [&](int c, const u32x4 (&kr)[8]) {
+    // result register r of lane (n, g) is row 4g + r of column n: key
+    // 8mt + 2g + r/2, half r & 1.  On an even lane (column 2i, dims 0..31)
+    // registers 0 and 2 hold the low halves of keys 8mt + 2g and 8mt + 2g + 1,
+    // and the odd neighbour's registers 1 and 3 the matching high halves.
     float m = -__builtin_huge_valf();
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < 8; ++mt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma16(as_bf16x8(kr[mt][0]), qf[0], acc);
-      acc = mfma16(as_bf16x8(kr[mt][1]), qf[1], acc);
-      m = fmaxf(m, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+      acc = mfma16(as_bf16x8(kr[mt]), qf, acc);
+      const float hi0 = swap_lane_pairs(acc[1]), hi1 = swap_lane_pairs(acc[3]);
+      m = fmaxf(m, fmaxf(acc[0] + hi0, acc[2] + hi1));
     }
-    m = wave_max_xor16_32(m);  // block max of column n (index head n)
-    if (HKV <= 2) m = fmaxf(m, __shfl_xor(m, 2));
-    if (HKV == 1) m = fmaxf(m, __shfl_xor(m, 1));
+    m = wave_max_xor16_32(m);  // lane 2i: block max of index head i
+    if (HKV <= 2) m = fmaxf(m, __shfl_xor(m, 4));
+    if (HKV == 1) m = fmaxf(m, __shfl_xor(m, 2));
     if (!page_ok(c)) m = -__builtin_huge_valf();
-    if (lane < HKV) out[(size_t)lane * a.nblk + c] = m;
+    if (lane < 2 * HKV && (lane & 1) == 0) out[(size_t)(lane >> 1) * a.nblk + c] = m;
   };
   for (int c = cbeg; c < cend; c += 2) {
-    u32x4 k0[4][2], k1[4][2];
+    u32x4 k0[8], k1[8];
     load(c, k0);
     const bool two = c + 1 < cend;
     if (two) load(c + 1, k1);
