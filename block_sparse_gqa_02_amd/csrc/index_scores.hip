@@ -50,18 +50,39 @@ index_scores_prefill_kernel(IndexArgs a) {
   const IndexTile T{a.iq, a.ik, b, t0, rows, a.Sq, a.Skv};
 
   index_sweep(T, 0, cur_last, lds, [&](int c0, int len, u32x4*) {
-    // list (h, row): max over index heads i = h (mod HKV); written row-contiguous
-    for (int f = tid; f < HKV * kTileRows * kStageCols; f += 256) {
-      const int e = f % kStageCols;
-      const int list = f / kStageCols;
-      const int h = list / kTileRows, row = list % kTileRows;
-      if (e >= len || row >= rows) continue;
-      const int c = c0 + e;
-      if (c >= (a.q_start + t0 + row) / kBlock) continue;  // own or later block
-      float v = lds.stage[h][row][e];
+    // list (h, row): max over index heads i = h (mod HKV); written row-contiguous.
+    // thread: blocks 4(tid % 8) .. +3 of the stage, rows tid / 8 + 32r of every
+    // head; whole runs of four go out as one 16-byte store
+    const int e4 = 4 * (tid % 8), r0 = tid / 8;
+    const int c = c0 + e4;
+    const bool vec_ok = (a.nblk & 3) == 0;
+    if (e4 < len) {
 #pragma unroll
-      for (int i = h + HKV; i < kIdxHeads; i += HKV) v = fmaxf(v, lds.stage[i][row][e]);
-      a.scores[(((size_t)b * HKV + h) * a.Sq + t0 + row) * a.nblk + c] = v;
+      for (int h = 0; h < HKV; ++h) {
+#pragma unroll
+        for (int rr = 0; rr < kTileRows / 32; ++rr) {
+          const int row = r0 + 32 * rr;
+          if (row >= rows) continue;
+          const int cur = (a.q_start + t0 + row) / kBlock;
+          if (c >= cur) continue;
+          f32x4 v;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            float x = lds.stage[h][row][e4 + k];
+#pragma unroll
+            for (int i = h + HKV; i < kIdxHeads; i += HKV) x = fmaxf(x, lds.stage[i][row][e4 + k]);
+            v[k] = x;
+          }
+          float* dst = a.scores + (((size_t)b * HKV + h) * a.Sq + t0 + row) * a.nblk + c;
+          if (vec_ok && c + 3 < cur && e4 + 3 < len) {
+            *reinterpret_cast<f32x4*>(dst) = v;
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (c + k < cur && e4 + k < len) dst[k] = v[k];
+          }
+        }
+      }
     }
   });
   // own block: +inf
