@@ -455,7 +455,10 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
             break;
           }
         }
+        // A wave that holds a slot issues ahead of its SIMD's other wave from
+        // here until its refill has gone out, so slots turn over sooner.
         cbarrier();
+        __builtin_amdgcn_s_setprio(2);
         compute(sl, c, gmask[c - wb], rmask[c - wb]);
         cbarrier();
         // count this wave done (its slot reads precede the increment in the
@@ -476,6 +479,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
                                                        (u + kRing) * 4, 0, 0);
           }
         }
+        __builtin_amdgcn_s_setprio(0);
       }
     }
     wait_vm(0);
