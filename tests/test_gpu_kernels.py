@@ -138,9 +138,12 @@ def test_topk_exact_against_oracle_on_same_scores(k, nblk, seed):
             assert np.array_equal(sel[0, hh, t], ref), (hh, t, sel[0, hh, t], ref)
 
 
-def test_index_scores_decode_and_topk_ragged():
+@pytest.mark.parametrize("hkv", [4, 2, 1], ids=["hkv4", "hkv2", "hkv1"])
+def test_index_scores_decode_and_topk_ragged(hkv):
+    # with fewer KV heads than index heads, a KV head's block score is the max
+    # over the index heads i = h (mod Hkv): the decode kernel folds them across lanes
     need_gpu()
-    w = DECODE_32x256K.shrink(batch=5, seq_kv=5000, top_k=9)
+    w = DECODE_32x256K.shrink(batch=5, seq_kv=5000, top_k=9, n_kv_heads=hkv, n_q_heads=8 * hkv)
     lens = [5000, 1, 4097, 64, 65]
     inp = generate(w, DEV, seed=77, seq_lens=lens)
     p = msa.Problem.from_workload(w)
