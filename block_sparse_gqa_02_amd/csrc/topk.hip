@@ -180,6 +180,7 @@ template <int E>
 __global__ void __launch_bounds__(kRadixThreads) topk_radix_kernel(TopkArgs a) {
   __shared__ int hist[256];
   __shared__ int wsum[kRadixThreads / kWave];
+  __shared__ uint32_t wand[kRadixThreads / kWave], wor[kRadixThreads / kWave];
   __shared__ int pick[2];  // digit, remaining count
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   for (long long row = blockIdx.x; row < a.nrows; row += gridDim.x) {
@@ -191,23 +192,55 @@ __global__ void __launch_bounds__(kRadixThreads) topk_radix_kernel(TopkArgs a) {
     const int m = min(a.k, n);
     const float* src = a.scores + row * a.nblk;
     const int c0 = tid * E;
+    // the own block is always kept; the other candidates compete for m - 1 places
     uint32_t key[E];
+    uint32_t kand = 0xffffffffu, kor = 0u;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int c = c0 + e;
-      key[e] = c < n ? (c == cur ? 0xffffffffu : score_key(src[c])) : 0u;  // 0: below every real key
+      key[e] = c < cur ? score_key(src[c]) : 0u;  // 0: below every real key
+      if (c < cur) {
+        kand &= key[e];
+        kor |= key[e];
+      }
     }
-    // radix select of the m-th largest key, most significant digit first
-    uint32_t prefix = 0, pmask = 0;
-    int rem = m;
+    // Bits shared by every other candidate (block scores share their sign and
+    // exponent): the radix passes start below them, so the first digit is not
+    // one crowded histogram bin.
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      kand &= (uint32_t)__shfl_xor((int)kand, off);
+      kor |= (uint32_t)__shfl_xor((int)kor, off);
+    }
+    if (lane == 0) {
+      wand[wave] = kand;
+      wor[wave] = kor;
+    }
+    __syncthreads();
+    kand = 0xffffffffu;
+    kor = 0u;
+#pragma unroll
+    for (int w = 0; w < kRadixThreads / kWave; ++w) {
+      kand &= wand[w];
+      kor |= wor[w];
+    }
+    int rem = m - 1;
+    const int free_bits = kand == kor ? 0 : 32 - __clz((int)(kand ^ kor));
+    uint32_t pmask = free_bits == 32 ? 0u : ~((1u << free_bits) - 1u);
+    uint32_t prefix = kand & pmask;
+    if (rem == 0) {
+      prefix = 0xffffffffu;  // no other block is kept
+      pmask = 0xffffffffu;
+    }
+    // radix select of the rem-th largest other key, most significant free digit first
 #pragma unroll 1
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
+    for (int shift = free_bits - 8; rem > 0 && shift > -8; shift -= 8) {
+      const int sh = shift < 0 ? 0 : shift;  // the last digit may repeat decided bits
       if (tid < 256) hist[tid] = 0;
       __syncthreads();
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        if (c0 + e < n && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255], 1);
+        if (c0 + e < cur && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> sh) & 255], 1);
       __syncthreads();
       if (wave == 0) {
         // lane l holds digits 4l..4l+3; count of matching keys with a higher digit
@@ -234,18 +267,19 @@ __global__ void __launch_bounds__(kRadixThreads) topk_radix_kernel(TopkArgs a) {
         }
       }
       __syncthreads();
-      prefix |= (uint32_t)pick[0] << shift;
-      pmask |= 0xffu << shift;
+      prefix |= (uint32_t)pick[0] << sh;
+      pmask |= 0xffu << sh;
       rem = pick[1];
       __syncthreads();
     }
-    // prefix is T; take every key above T and the first `rem` keys equal to T
+    // prefix is T; take the own block, every other key above T and the first
+    // `rem` other keys equal to T
     int gt = 0, eq = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const bool ok = c0 + e < n;
-      gt += ok && key[e] > prefix;
-      eq += ok && key[e] == prefix;
+      const int c = c0 + e;
+      gt += (c < cur && key[e] > prefix) || c == cur;
+      eq += c < cur && key[e] == prefix;
     }
     int ties_total;
     const int tie_rank = block_exclusive_scan(eq, wsum, &ties_total);
@@ -257,9 +291,9 @@ __global__ void __launch_bounds__(kRadixThreads) topk_radix_kernel(TopkArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int c = c0 + e;
-      if (c >= n) continue;
-      const bool tie = key[e] == prefix;
-      if (key[e] > prefix || (tie && took < take)) {
+      if (c > cur) continue;
+      const bool tie = c < cur && key[e] == prefix;
+      if (c == cur || (c < cur && key[e] > prefix) || (tie && took < take)) {
         dst[at++] = c;
         took += tie;
       }
