@@ -138,6 +138,30 @@ def test_topk_exact_against_oracle_on_same_scores(k, nblk, seed):
             assert np.array_equal(sel[0, hh, t], ref), (hh, t, sel[0, hh, t], ref)
 
 
+@pytest.mark.parametrize("k", [1, 9, 64])
+def test_topk_radix_rows_shorter_than_k(k):
+    """Few long rows (the work-group radix select): sequences whose causal
+    blocks number fewer than, equal to or more than k, on scores full of exact
+    ties; the selection must follow the (score desc, block asc) rule exactly."""
+    need_gpu()
+    nblk = 1100
+    lens = [nblk * 64, 1, 64, 65, 129, 4100, 64 * 9, 64 * 9 + 1]
+    w = DECODE_32x256K.shrink(batch=len(lens), seq_kv=nblk * 64, top_k=k)
+    g = torch.Generator().manual_seed(40 + k)
+    sc = torch.randint(-3, 4, (w.batch, w.n_kv_heads, 1, nblk), generator=g).float()
+    p = msa.Problem.from_workload(w)
+    sel = msa.msa_topk_blocks(p, sc.to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV))
+    sel = sel.cpu().numpy()
+    po = oprob(w)
+    for b, L in enumerate(lens):
+        cur = (L - 1) // 64
+        for hh in range(w.n_kv_heads):
+            row = sc[b, hh, 0].numpy().copy()
+            row[cur] = np.inf
+            ref = O.select_row(po, row, cur)
+            assert np.array_equal(sel[b, hh, 0], ref), (b, hh, sel[b, hh, 0], ref)
+
+
 @pytest.mark.parametrize("hkv", [4, 2, 1], ids=["hkv4", "hkv2", "hkv1"])
 def test_index_scores_decode_and_topk_ragged(hkv):
     # with fewer KV heads than index heads, a KV head's block score is the max
