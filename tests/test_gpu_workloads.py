@@ -82,3 +82,25 @@ def test_prefill_32k_shared_index_queries_sampled():
     w = PREFILL_32K_SHARED_IQ
     rows = PAR.sample_rows(w.seq_q, w.q_start, w.block_size, seed=33, n_uniform=1024)
     WC.check(w, False, rows, log=log)
+
+
+@pytest.mark.parametrize("w", [PREFILL_32K, CHUNK_1M], ids=lambda w: w.name)
+def test_forward_bit_identical_across_calls(w):
+    """The sparse prefill's K/V ring is filled and drained in an order that
+    depends on timing, but each row group walks its blocks in one fixed order:
+    two calls on the same inputs give the same bits (selection, output, LSE)."""
+    need_gpu()
+    inp = generate(w, "cuda")
+    p = msa.Problem.from_workload(w)
+    runs = []
+    for _ in range(2):
+        if w.seq_kv > 200000:
+            sel = msa.msa_index_topk_fused(p, inp.iq, inp.ik)
+        else:
+            sel = msa.msa_topk_blocks(p, msa.msa_index_block_scores(p, inp.iq, inp.ik))
+        lse = torch.empty((w.batch, w.n_q_heads, w.seq_q), dtype=torch.float32, device="cuda")
+        out = msa.msa_sparse_attn_prefill(p, inp.q, inp.k, inp.v, sel, lse=lse)
+        runs.append((sel, out, lse))
+    torch.cuda.synchronize()
+    for name, a, b in zip(("selection", "output", "lse"), runs[0], runs[1]):
+        assert torch.equal(a, b), f"{w.name}: {name} differs between two identical calls"
