@@ -57,6 +57,9 @@ PREFILL_SMALL = [
     ("g16_rowwise", dict(seq_q=400, seq_kv=900, q_start=500, n_q_heads=32, n_kv_heads=2, top_k=6)),
     ("g2_rowwise", dict(seq_q=300, seq_kv=300, q_start=0, n_q_heads=8, n_kv_heads=4, top_k=3)),
     ("g8_many_tiles", dict(seq_q=1500, seq_kv=4000, q_start=2500, n_q_heads=16, n_kv_heads=2, top_k=20)),
+    # rows past 512 causal blocks: the tile-union kernel's block windows roll over
+    ("g4_two_windows", dict(seq_q=300, seq_kv=40000, q_start=39700, n_q_heads=8, n_kv_heads=2, top_k=24)),
+    ("g8_two_windows", dict(seq_q=200, seq_kv=36000, q_start=35800, n_q_heads=16, n_kv_heads=2, top_k=24)),
 ]
 
 
