@@ -190,10 +190,11 @@ def test_index_scores_decode_and_topk_ragged(hkv):
             PAR.check_selection_row(sel_h[b, hh, 0], ref, cur, w.top_k, False, f"seq {b}")
 
 
+@pytest.mark.parametrize("heads", [(32, 4), (8, 2)], ids=["g8", "g4_hkv2"])
 @pytest.mark.parametrize("dense", [False, True], ids=["sparse", "dense"])
-def test_decode_attention_ragged(dense):
+def test_decode_attention_ragged(dense, heads):
     need_gpu()
-    w = DECODE_32x256K.shrink(batch=4, seq_kv=3000, top_k=11)
+    w = DECODE_32x256K.shrink(batch=4, seq_kv=3000, top_k=11, n_q_heads=heads[0], n_kv_heads=heads[1])
     lens = [3000, 65, 1, 2048]
     inp = generate(w, DEV, seed=5, seq_lens=lens)
     p = msa.Problem.from_workload(w)
