@@ -114,7 +114,10 @@ def test_prefill_pipeline_small(name, ov, integer):
 @pytest.mark.parametrize("k,nblk,seed", [(1, 40, 0), (5, 130, 1), (64, 700, 2), (200, 513, 3),
                                          (256, 256, 4), (8, 32, 5), (64, 1100, 6), (200, 1500, 7),
                                          (1, 1024, 8), (3, 4096, 9), (64, 5000, 10),
-                                         (128, 9000, 11), (256, 16384, 12)])
+                                         (128, 9000, 11), (256, 16384, 12),
+                                         # past 16384 candidates: the wide-row kernel
+                                         (64, 20000, 13), (128, 17000, 14), (200, 18000, 15),
+                                         (256, 16500, 16)])
 def test_topk_exact_against_oracle_on_same_scores(k, nblk, seed):
     """Top-k alone on synthetic scores full of exact ties (integers, -0/+0):
     the decision is taken on identical fp32 values, so it must be bit-exact."""
