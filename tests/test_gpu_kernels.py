@@ -117,7 +117,9 @@ def test_prefill_pipeline_small(name, ov, integer):
                                          (128, 9000, 11), (256, 16384, 12),
                                          # past 16384 candidates: the wide-row kernel
                                          (64, 20000, 13), (128, 17000, 14), (200, 18000, 15),
-                                         (256, 16500, 16)])
+                                         (256, 16500, 16),
+                                         # k of 129..192: the 320-entry list instances
+                                         (150, 700, 17), (150, 17500, 18)])
 def test_topk_exact_against_oracle_on_same_scores(k, nblk, seed):
     """Top-k alone on synthetic scores full of exact ties (integers, -0/+0):
     the decision is taken on identical fp32 values, so it must be bit-exact."""
@@ -260,6 +262,7 @@ FUSED_CASES = [
     ("multi_split_unaligned", dict(seq_q=300, seq_kv=12000, q_start=11650, n_q_heads=8, n_kv_heads=2, top_k=37)),
     ("k1", dict(seq_q=200, seq_kv=9000, q_start=8700, n_q_heads=4, n_kv_heads=1, top_k=1)),
     ("k256", dict(seq_q=130, seq_kv=20000, q_start=19800, n_q_heads=8, n_kv_heads=2, top_k=256)),
+    ("k150", dict(seq_q=150, seq_kv=14000, q_start=13850, n_q_heads=8, n_kv_heads=2, top_k=150)),
     ("short_rows", dict(seq_q=700, seq_kv=700, q_start=0, n_q_heads=8, n_kv_heads=2, top_k=6)),
 ]
 
