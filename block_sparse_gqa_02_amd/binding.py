@@ -23,7 +23,7 @@ STATUS = {0: "MSA_OK", 1: "MSA_ERR_INVALID_ARGUMENT", 2: "MSA_ERR_UNSUPPORTED",
           3: "MSA_ERR_WORKSPACE_TOO_SMALL", 4: "MSA_ERR_HIP"}
 OPS = {"index_block_scores": 0, "topk_blocks": 1, "index_topk_fused": 2,
        "sparse_attn_prefill": 3, "sparse_attn_decode": 4, "dense_attn_prefill": 5,
-       "dense_attn_decode": 6, "sparse_attn_prefill_backward": 7}
+       "dense_attn_decode": 6, "sparse_attn_prefill_backward": 7, "index_topk_fused_decode": 8}
 
 
 class MsaError(RuntimeError):
@@ -97,6 +97,8 @@ def lib():
                                              vp, sz, vp],
             "msa_sparse_attn_prefill_backward": [pr, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                  sz, vp],
+            "msa_sparse_attn_prefill_status_offset": [pr, P(sz)],
+            "msa_index_topk_fused_paged": [pr, vp, vp, vp, ctypes.c_int32, vp, vp, vp, sz, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -108,6 +110,8 @@ def lib():
         L.msa_last_error.restype = ctypes.c_char_p
         L.msa_abi_version.argtypes = []
         L.msa_abi_version.restype = ctypes.c_int
+        L.msa_set_wait_limit.argtypes = [ctypes.c_int32]
+        L.msa_set_wait_limit.restype = None
         _lib = L
     return _lib
 
@@ -145,11 +149,36 @@ def msa_workspace_bytes(p: Problem, op: str) -> int:
     return out.value
 
 
+# Operations whose workspace starts with arrival counters that must be zero
+# before the first call (each call leaves them zero).
+_ZEROED = {"index_topk_fused_decode"}
+
+
 def _workspace(p: Problem, op: str, ws, device):
     need = msa_workspace_bytes(p, op)
     if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        alloc = torch.zeros if op in _ZEROED else torch.empty
+        ws = alloc(max(need, 16), dtype=torch.uint8, device=device)
     return ws, ws.numel() * ws.element_size()
+
+
+def decode_workspace(p: Problem, dense: bool = False, device="cuda", op=None):
+    """A reusable workspace for msa_sparse_attn_decode (dense=False),
+    msa_dense_attn_decode (dense=True) or another op named by `op`, zero-filled
+    (the decode form of msa_index_topk_fused needs its counter region zero)."""
+    if op is None:
+        op = "dense_attn_decode" if dense else "sparse_attn_decode"
+    return torch.zeros(max(msa_workspace_bytes(p, op), 16), dtype=torch.uint8, device=device)
+
+
+def msa_sparse_attn_prefill_status_offset(p: Problem) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().msa_sparse_attn_prefill_status_offset(ctypes.byref(p.c()), ctypes.byref(out)))
+    return out.value
+
+
+def msa_set_wait_limit(polls: int) -> None:
+    lib().msa_set_wait_limit(int(polls))
 
 
 def msa_index_block_scores(p: Problem, iq, ik, seq_lens=None, block_scores=None, stream=None):
@@ -177,7 +206,8 @@ def msa_index_topk_fused(p: Problem, iq, ik, seq_lens=None, sel=None, workspace=
     if sel is None:
         sel = torch.empty((p.batch, p.n_kv_heads, p.seq_q, p.top_k), dtype=torch.int32,
                           device=iq.device)
-    ws, nbytes = _workspace(p, "index_topk_fused", workspace, iq.device)
+    op = "index_topk_fused" if seq_lens is None else "index_topk_fused_decode"
+    ws, nbytes = _workspace(p, op, workspace, iq.device)
     _check(lib().msa_index_topk_fused(ctypes.byref(p.c()), _ptr(iq, torch.bfloat16),
                                       _ptr(ik, torch.bfloat16), _ptr(seq_lens, torch.int32),
                                       _ptr(sel, torch.int32), _ptr(ws), nbytes, _stream(stream)))
@@ -242,6 +272,19 @@ def msa_index_block_scores_paged(p: Problem, iq, ik_pages, page_table, num_pages
         _ptr(page_table, torch.int32), int(num_pages), _ptr(seq_lens, torch.int32),
         _ptr(block_scores, torch.float32), _stream(stream)))
     return block_scores
+
+
+def msa_index_topk_fused_paged(p: Problem, iq, ik_pages, page_table, num_pages: int, seq_lens,
+                               sel=None, workspace=None, stream=None):
+    """Decode index scoring + top-k in one launch, index-K cache in pages."""
+    if sel is None:
+        sel = torch.empty((p.batch, p.n_kv_heads, 1, p.top_k), dtype=torch.int32, device=iq.device)
+    ws, nbytes = _workspace(p, "index_topk_fused_decode", workspace, iq.device)
+    _check(lib().msa_index_topk_fused_paged(
+        ctypes.byref(p.c()), _ptr(iq, torch.bfloat16), _ptr(ik_pages, torch.bfloat16),
+        _ptr(page_table, torch.int32), int(num_pages), _ptr(seq_lens, torch.int32),
+        _ptr(sel, torch.int32), _ptr(ws), nbytes, _stream(stream)))
+    return sel
 
 
 def msa_sparse_attn_decode_paged(p: Problem, q, k_pages, v_pages, page_table, num_pages: int,

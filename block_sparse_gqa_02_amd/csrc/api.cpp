@@ -61,6 +61,9 @@ msa_status check_problem(const msa_problem* p, Mode mode, bool need_k, msa::Shap
                 p->n_q_heads, p->n_kv_heads);
   if (!std::isfinite(p->softmax_scale))
     return fail(MSA_ERR_INVALID_ARGUMENT, "softmax_scale is not finite");
+  // the tiled kernels take the running max on unscaled scores
+  if (!(p->softmax_scale > 0.f))
+    return fail(MSA_ERR_UNSUPPORTED, "softmax_scale must be > 0");
   if (need_k && p->top_k < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "top_k must be >= 1");
   if (mode == Mode::kDecode && p->seq_q != 1)
     return fail(MSA_ERR_INVALID_ARGUMENT, "decode needs seq_q == 1 (got %d)", p->seq_q);
@@ -151,11 +154,36 @@ msa_status msa_topk_blocks(const msa_problem* p, const float* block_scores,
                   "msa_topk_blocks");
 }
 
+// Decode form of the fused index + top-k (contiguous or paged index-K cache).
+static msa_status index_topk_decode(const msa_problem* p, const void* iq, const void* ik,
+                                    const msa::Paging* pg, const int32_t* seq_lens, int32_t* sel,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                    const char* name) {
+  msa::Shape s;
+  msa_status st = check_problem(p, Mode::kDecode, true, &s);
+  if (st != MSA_OK) return st;
+  NEED_PTR(iq);
+  NEED_PTR(ik);
+  NEED_PTR4(seq_lens);
+  NEED_PTR4(sel);
+  NEED_PTR(workspace);
+  if (!msa::index_topk_decode_counters_fit(s))
+    return fail(MSA_ERR_UNSUPPORTED, "too many sequences for the arrival counters");
+  const size_t need = msa::index_topk_decode_workspace_bytes(s);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  return launched(msa::launch_index_topk_decode(s, iq, ik, seq_lens, sel, workspace,
+                                                workspace_bytes, stream, pg),
+                  name);
+}
+
 msa_status msa_index_topk_fused(const msa_problem* p, const void* iq, const void* ik,
                                 const int32_t* seq_lens, int32_t* sel, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
   msa::Shape s;
-  if (seq_lens) return fail(MSA_ERR_UNSUPPORTED, "msa_index_topk_fused: prefill positions only");
+  if (seq_lens)
+    return index_topk_decode(p, iq, ik, nullptr, seq_lens, sel, workspace, workspace_bytes, stream,
+                             "msa_index_topk_fused");
   msa_status st = check_problem(p, Mode::kPrefill, true, &s);
   if (st != MSA_OK) return st;
   NEED_PTR(iq);
@@ -213,7 +241,8 @@ static msa_status decode_common(const msa_problem* p, const void* q, const void*
   const size_t need = msa::decode_workspace_bytes(s, sel == nullptr);
   if (workspace_bytes < need)
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
-  return launched(msa::launch_attn_decode(s, q, k, v, seq_lens, sel, out, lse, workspace, stream),
+  return launched(msa::launch_attn_decode(s, q, k, v, seq_lens, sel, out, lse, workspace,
+                                          workspace_bytes, stream),
                   name);
 }
 
@@ -270,6 +299,17 @@ msa_status msa_index_block_scores_paged(const msa_problem* p, const void* iq,
                   "msa_index_block_scores_paged");
 }
 
+msa_status msa_index_topk_fused_paged(const msa_problem* p, const void* iq, const void* ik_pages,
+                                      const int32_t* page_table, int32_t num_pages,
+                                      const int32_t* seq_lens, int32_t* sel, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  NEED_PTR4(page_table);
+  if (num_pages < 1) return fail(MSA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+  const msa::Paging pg{page_table, num_pages};
+  return index_topk_decode(p, iq, ik_pages, &pg, seq_lens, sel, workspace, workspace_bytes, stream,
+                           "msa_index_topk_fused_paged");
+}
+
 msa_status msa_sparse_attn_decode_paged(const msa_problem* p, const void* q,
                                         const void* k_pages, const void* v_pages,
                                         const int32_t* page_table, int32_t num_pages,
@@ -294,7 +334,7 @@ msa_status msa_sparse_attn_decode_paged(const msa_problem* p, const void* q,
     return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
   const msa::Paging pg{page_table, num_pages};
   return launched(msa::launch_attn_decode(s, q, k_pages, v_pages, seq_lens, sel, out, lse,
-                                          workspace, stream, &pg),
+                                          workspace, workspace_bytes, stream, &pg),
                   "msa_sparse_attn_decode_paged");
 }
 
@@ -327,6 +367,19 @@ msa_status msa_sparse_attn_prefill_backward(const msa_problem* p, const void* q,
                   "msa_sparse_attn_prefill_backward");
 }
 
+msa_status msa_sparse_attn_prefill_status_offset(const msa_problem* p, size_t* offset) {
+  if (!offset) return fail(MSA_ERR_INVALID_ARGUMENT, "offset is NULL");
+  msa::Shape s;
+  msa_status st = check_problem(p, Mode::kPrefill, true, &s, true);
+  if (st != MSA_OK) return st;
+  if (s.bs != 64 || !msa::union_prefill_supported(s))
+    return fail(MSA_ERR_UNSUPPORTED, "this shape runs a kernel without bounded waits (no status word)");
+  *offset = msa::union_prefill_status_offset(s);
+  return ok();
+}
+
+void msa_set_wait_limit(int32_t polls) { msa::set_union_spin_limit(polls); }
+
 msa_status msa_workspace_bytes(const msa_problem* p, msa_op op, size_t* bytes) {
   if (!bytes) return fail(MSA_ERR_INVALID_ARGUMENT, "bytes is NULL");
   msa::Shape s;
@@ -356,6 +409,11 @@ msa_status msa_workspace_bytes(const msa_problem* p, msa_op op, size_t* bytes) {
       st = check_backward(s);
       if (st != MSA_OK) return st;
       *bytes = msa::sparse_bwd_workspace_bytes(s);
+      return ok();
+    case MSA_OP_INDEX_TOPK_FUSED_DECODE:
+      st = check_problem(p, Mode::kDecode, true, &s);
+      if (st != MSA_OK) return st;
+      *bytes = msa::index_topk_decode_workspace_bytes(s);
       return ok();
     case MSA_OP_SPARSE_ATTN_DECODE:
     case MSA_OP_DENSE_ATTN_DECODE:

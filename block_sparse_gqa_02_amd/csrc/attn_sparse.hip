@@ -12,7 +12,10 @@
 // the selection (or of all causal blocks for the dense baseline) and writes an
 // unnormalised partial (m, l, O); a merge kernel combines the splits by
 // log-sum-exp.  Splits keep enough waves in flight to stream K/V at HBM rate
-// when only B * Hkv = 128 (sequence, head) pairs exist.
+// when only B * Hkv = 128 (sequence, head) pairs exist.  (Merging in the same
+// launch, by the last work-group of each (sequence, KV head), measured slower:
+// handing the partials over inside a launch takes write-through stores and an
+// arrival atomic per work-group, which cost more than the merge launch.)
 #include "attn_block.h"
 #include "common.h"
 #include "kernels.h"
@@ -264,7 +267,8 @@ size_t decode_workspace_bytes(const Shape& s, bool dense) {
 
 hipError_t launch_attn_decode(const Shape& s, const void* q, const void* k, const void* v,
                               const int32_t* seq_lens, const int32_t* sel, void* out, float* lse,
-                              void* ws, hipStream_t st, const Paging* pg) {
+                              void* ws, size_t ws_bytes, hipStream_t st, const Paging* pg) {
+  if (ws_bytes < decode_workspace_bytes(s, sel == nullptr)) return hipErrorInvalidValue;
   const bool dense = sel == nullptr;
   const int nsplit = decode_nsplit(s, dense);
   const size_t cols = (size_t)s.B * s.Hkv * nsplit * s.G;

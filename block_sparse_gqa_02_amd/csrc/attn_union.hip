@@ -28,8 +28,8 @@
 // wave's loads return in issue order, so the tag lands after the data.  The
 // refiller never waits for its own fetch.  Waves that want none of a block
 // skip it without touching the ring.  Every wait is bounded: past the bound
-// the kernel stops waiting and stores NaN outputs (a caller-visible failure,
-// never a hang).
+// the kernel stops waiting, stores NaN outputs and sets the call's failure
+// word at the end of the workspace (a caller-visible failure, never a hang).
 //
 // V arrives transposed.  A pre-pass writes, for every context block, a 16 KiB
 // V^T tile: 128 dim rows of 64 keys, the keys of each 32-key half permuted so
@@ -44,6 +44,9 @@
 // chunk positions of a 256-byte bank line.
 #include "common.h"
 #include "kernels.h"
+#include "lds_ring.h"
+
+#include <atomic>
 
 namespace msa {
 namespace {
@@ -56,7 +59,8 @@ constexpr int kWaves = 8;          // waves per work-group (2 per SIMD)
 constexpr int kGPW = 3;            // row groups owned per wave
 constexpr int kNG = kWaves * kGPW; // row groups per tile
 constexpr int kRing = 4;           // K/V slots in the LDS ring
-constexpr int kSpinLimit = 1 << 22;
+constexpr int kDefaultSpinLimit = 1 << 22;  // tag polls before a wave gives up
+constexpr int kStatusBytes = 256;           // failure word at the end of the workspace
 constexpr int kBlockBytes = kBlock * kHeadDim * 2;  // one K or V block
 constexpr int kRsrcFlags = 0x00020000;              // raw buffer descriptor word 3
 
@@ -67,8 +71,10 @@ struct UnionArgs {
   const int32_t* sel;   // [B][Hkv][Sq][k]
   uint16_t* out;        // [B][Sq][Hq][128]
   float* lse;           // [B][Hq][Sq] or null
+  int32_t* status;      // failure word: set to 1 when a bounded wait gives up
   int Sq, Skv, q_start, Hq, Hkv, top_k, ntiles, nblk_ctx;
   float scale_log2;
+  int spin_limit;
 };
 
 // V^T tile of block c: position 32kv + 8g + i of dim row d holds V[64c + 32kv +
@@ -79,6 +85,7 @@ struct UnionArgs {
 struct VtArgs {
   const uint16_t* v;    // [B][Hkv][Skv][128]
   uint16_t* vt;         // [B][Hkv][nblk_ctx][128][64]
+  int32_t* status;      // the call's failure word, cleared here (runs before the sweep)
   int Skv, ctx, nblk_ctx;
 };
 
@@ -90,6 +97,7 @@ __global__ void __launch_bounds__(256) vt_kernel(VtArgs a) {
   const long long head = tl / a.nblk_ctx;
   const u32x4* src = reinterpret_cast<const u32x4*>(a.v + head * a.Skv * kHeadDim);
   const int tid = threadIdx.x;
+  if (tl == 0 && tid == 0) *a.status = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = i * 256 + tid;  // chunk q of the block: key q / 16, dim chunk q % 16
@@ -115,12 +123,6 @@ __global__ void __launch_bounds__(256) vt_kernel(VtArgs a) {
     dst[q] = w;
   }
 }
-
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-__device__ __forceinline__ int kswz(int row) { return row & 15; }
-
-__device__ __forceinline__ void cbarrier() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
@@ -444,7 +446,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
         if (lds_load_tag(&ready[sl]) != u) {
           int spins = 0;
           while (lds_load_tag(&ready[sl]) != u) {
-            if (++spins > kSpinLimit) {
+            if (++spins > a.spin_limit) {
               ok_run = false;
               break;
             }
@@ -486,6 +488,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
     __syncthreads();
     if (failed) ok_run = false;
   }
+  if (!ok_run && tid == 0) *a.status = 1;  // a vector store: visible to the caller after the call
 
   // epilogue: normalise and store this wave's groups; register r of o[j][mt] is
   // dim 16mt + 4g + r of this lane's column
@@ -517,9 +520,17 @@ bool union_prefill_supported(const Shape& s) { return s.G == 8 || s.G == 4; }
 
 static int context_blocks(const Shape& s) { return ceil_div(s.q_start + s.Sq, kBlock); }
 
-size_t union_prefill_workspace_bytes(const Shape& s) {
+static size_t vt_bytes(const Shape& s) {
   return (size_t)s.B * s.Hkv * context_blocks(s) * kBlockBytes;
 }
+
+size_t union_prefill_workspace_bytes(const Shape& s) { return vt_bytes(s) + kStatusBytes; }
+
+size_t union_prefill_status_offset(const Shape& s) { return vt_bytes(s); }
+
+static std::atomic<int> g_spin_limit{kDefaultSpinLimit};
+
+void set_union_spin_limit(int spins) { g_spin_limit.store(spins > 0 ? spins : kDefaultSpinLimit); }
 
 hipError_t launch_union_prefill(const Shape& s, const void* q, const void* k, const void* v,
                                 const int32_t* sel, void* out, float* lse, void* ws,
@@ -532,14 +543,16 @@ hipError_t launch_union_prefill(const Shape& s, const void* q, const void* k, co
   const long long tiles_vt = (long long)s.B * s.Hkv * nblk_ctx;
   const long long grid = (long long)ntiles * s.Hkv * s.B;
   if (grid > 0x7fffffffLL || tiles_vt > 0x7fffffffLL) return hipErrorInvalidValue;
-  VtArgs t{static_cast<const uint16_t*>(v), static_cast<uint16_t*>(ws), s.Skv, s.q_start + s.Sq,
-           nblk_ctx};
+  int32_t* status = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + vt_bytes(s));
+  VtArgs t{static_cast<const uint16_t*>(v), static_cast<uint16_t*>(ws), status, s.Skv,
+           s.q_start + s.Sq, nblk_ctx};
   vt_kernel<<<(unsigned)tiles_vt, 256, 0, st>>>(t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   UnionArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-              static_cast<const uint16_t*>(ws), sel, static_cast<uint16_t*>(out), lse,
-              s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.top_k, ntiles, nblk_ctx, s.scale * kLog2e};
+              static_cast<const uint16_t*>(ws), sel, static_cast<uint16_t*>(out), lse, status,
+              s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.top_k, ntiles, nblk_ctx, s.scale * kLog2e,
+              g_spin_limit.load()};
   if (s.G == 8) union_prefill_kernel<8><<<(unsigned)grid, kWaves * kWave, 0, st>>>(a);
   else if (s.G == 4) union_prefill_kernel<4><<<(unsigned)grid, kWaves * kWave, 0, st>>>(a);
   else return hipErrorInvalidValue;

@@ -105,4 +105,43 @@ __device__ __forceinline__ float halves_max(float a, float b) {
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Hand-over of data between the work-groups of one launch (the last one to
+// finish a unit of work consumes what the others wrote).  The data travels
+// through agent-scope coherent stores and loads, which write through / read
+// past the non-coherent copy in an XCD's L2, so the producer needs no L2
+// write-back (an agent-scope release fence writes back the whole L2, which
+// costs far more than the data when thousands of work-groups do it); a wait
+// for the producer's stores to complete orders them before its arrival count.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained), fenced against compiler
+// reordering: every store this wave issued has completed.
+__device__ __forceinline__ void wait_stores_done() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xf70);
+  asm volatile("" ::: "memory");
+}
+
+// Counts the calling work-group in on `counter` once every thread's
+// store_agent() data has completed; true, in every thread, for the work-group
+// that arrives last of `total`, which also puts the counter back to zero for
+// the next launch.  Nothing waits for another work-group.  flag: one int of LDS.
+__device__ __forceinline__ bool arrive_last(int32_t* counter, int total, int* flag) {
+  wait_stores_done();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int before = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    const int last = before == total - 1;
+    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
 }  // namespace msa

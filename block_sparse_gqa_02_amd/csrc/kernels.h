@@ -9,6 +9,14 @@
 
 namespace msa {
 
+// Launches that hand data over between their work-groups (the decode index
+// scoring with its in-launch top-k) keep their arrival counters in the first
+// kCounterBytes of their workspace, the same region for every shape: zero
+// before the first call on a workspace, and every call puts the counters it
+// used back to zero, so a workspace stays valid for any later call of any shape.
+constexpr size_t kCounterBytes = 1 << 20;
+constexpr int kMaxCounters = (int)(kCounterBytes / sizeof(int32_t));
+
 struct Shape {
   int B, Sq, Skv, q_start;
   int Hq, Hkv, G;     // query heads, KV heads, Hq / Hkv
@@ -30,6 +38,16 @@ struct Paging {
 hipError_t launch_index_block_scores(const Shape& s, const void* iq, const void* ik,
                                      const int32_t* seq_lens, float* scores, hipStream_t st,
                                      const Paging* pg = nullptr);
+
+// Decode index scoring and top-k in one launch: block scores into the workspace,
+// each sequence's selection by its last work-group.  Workspace: the fixed
+// arrival-counter region (zero before the first call on a buffer; every call
+// leaves it zero), then the block scores.
+size_t index_topk_decode_workspace_bytes(const Shape& s);
+bool index_topk_decode_counters_fit(const Shape& s);
+hipError_t launch_index_topk_decode(const Shape& s, const void* iq, const void* ik,
+                                    const int32_t* seq_lens, int32_t* sel, void* ws,
+                                    size_t ws_bytes, hipStream_t st, const Paging* pg = nullptr);
 
 // Per-KV-head top-k over block scores -> sel [B][Hkv][Sq][k].
 hipError_t launch_topk_blocks(const Shape& s, const float* scores, const int32_t* seq_lens,
@@ -58,14 +76,23 @@ hipError_t launch_sparse_attn_prefill(const Shape& s, const void* q, const void*
 // Tile-union schedule of the sparse prefill (used for G = 4 and 8).
 bool union_prefill_supported(const Shape& s);
 size_t union_prefill_workspace_bytes(const Shape& s);
+// Byte offset of the int32 failure word in the tile-union workspace.
+size_t union_prefill_status_offset(const Shape& s);
+// Polls of a ring tag before a wave gives up (<= 0 restores the default).
+void set_union_spin_limit(int spins);
 hipError_t launch_union_prefill(const Shape& s, const void* q, const void* k, const void* v,
                                 const int32_t* sel, void* out, float* lse, void* ws,
                                 hipStream_t st);
+// Decode workspace: the split partials (any content).
 size_t decode_workspace_bytes(const Shape& s, bool dense);
 // sel == NULL: dense; pg: k and v are pools of [num_pages][Hkv][64][128] pages.
 hipError_t launch_attn_decode(const Shape& s, const void* q, const void* k, const void* v,
                               const int32_t* seq_lens, const int32_t* sel, void* out, float* lse,
-                              void* ws, hipStream_t st, const Paging* pg = nullptr);
+                              void* ws, size_t ws_bytes, hipStream_t st,
+                              const Paging* pg = nullptr);
+// The library's own decode scratch on the current device (no allocation):
+// its address and size.  hipGetSymbolAddress runs once per device.
+hipError_t decode_scratch(void** ptr, size_t* bytes);
 
 // Token-level selection (block size 1, prefill positions): token scores
 // [B][Hkv][Sq][Skv] (entries j <= pos written), per-KV-head top-k over them,

@@ -86,15 +86,16 @@ __device__ __forceinline__ uint32_t wave_topm_regs(const uint32_t (&kr)[MAXE],
   int out = 0, eq_seen = 0;
 #pragma unroll
   for (int e = 0; e < MAXE; ++e) {
-    if (e * kWave >= n) break;
-    const bool gt = kr[e] > V;
-    const bool eq = kr[e] == V;
-    const uint64_t eqm = ballot(eq);
-    const bool keep = gt || (eq && eq_seen + prefix_count(eqm) < take_equal);
-    const uint64_t km = ballot(keep);
-    if (keep) put(out + prefix_count(km), kr[e], ir[e]);
-    out += __popcll(km);
-    eq_seen += __popcll(eqm);
+    if (e * kWave < n) {  // (a guard, not a break: the loop must unroll fully)
+      const bool gt = kr[e] > V;
+      const bool eq = kr[e] == V;
+      const uint64_t eqm = ballot(eq);
+      const bool keep = gt || (eq && eq_seen + prefix_count(eqm) < take_equal);
+      const uint64_t km = ballot(keep);
+      if (keep) put(out + prefix_count(km), kr[e], ir[e]);
+      out += __popcll(km);
+      eq_seen += __popcll(eqm);
+    }
   }
   __builtin_amdgcn_wave_barrier();
   return V;
@@ -158,6 +159,66 @@ __device__ __forceinline__ int wave_append(KP keys, IP idxs, int cnt, bool pass,
   }
   __builtin_amdgcn_wave_barrier();
   return cnt + (int)__popcll(mask);
+}
+
+constexpr int kStreamBatch = 16;  // 64-candidate chunks loaded together
+
+// Streams block scores [c_beg, c_end) of one row (src[c] is block c's score)
+// through a wave's running top-m list in LDS (keys, idxs; cnt entries, the
+// threshold thr), with the own block `cur` forced to the top key.  Up to
+// kStreamBatch chunks are loaded at once, so a row costs one memory latency per
+// batch, not per chunk.  The list keeps room for a full chunk after every
+// compaction (64 MAXE >= m + 64).
+template <int MAXE, bool AgentLoads = false>
+__device__ __forceinline__ void stream_candidates(const float* src, int c_beg, int c_end, int cur,
+                                                  int m, uint32_t* keys, int32_t* idxs, int& cnt,
+                                                  uint32_t& thr) {
+  constexpr int CAP = MAXE * kWave;
+  constexpr int NB = kStreamBatch;  // (a larger batch is no longer unrolled: its registers spill)
+  const int lane = lane_id();
+  for (int c0 = c_beg; c0 < c_end; c0 += NB * kWave) {
+    float v[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int c = c0 + i * kWave + lane;
+      if (AgentLoads) {
+        // unconditional (clamped) loads: a load under a branch gets its own wait
+        const float x = load_agent(src + min(c, c_end - 1));
+        v[i] = c < c_end ? x : 0.f;
+      } else {
+        v[i] = c < c_end ? src[c] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (c0 + i * kWave >= c_end) break;
+      const int c = c0 + i * kWave + lane;
+      const bool ok = c < c_end;
+      uint32_t key = 0;
+      if (ok) key = (c == cur) ? 0xffffffffu : score_key(v[i]);
+      cnt = wave_append(keys, idxs, cnt, ok && key > thr, key, c);
+      if (cnt > CAP - kWave) {
+        thr = wave_compact_topm<MAXE>(keys, idxs, cnt, m);
+        cnt = m;
+      }
+    }
+  }
+}
+
+// One row's whole selection into dst[0 .. k): the first min(k, cur+1) blocks
+// of [0, cur] by (score descending, block ascending), ascending, -1 padded.
+// AgentLoads: the scores were written by other work-groups of the launch.
+template <int MAXE, bool AgentLoads = false>
+__device__ __forceinline__ void select_row(const float* src, int cur, int k, uint32_t* keys,
+                                           int32_t* idxs, int32_t* dst) {
+  const int lane = lane_id();
+  const int m = min(k, cur + 1);
+  int cnt = 0;
+  uint32_t thr = 0;
+  stream_candidates<MAXE, AgentLoads>(src, 0, cur + 1, cur, m, keys, idxs, cnt, thr);
+  if (cnt > m) wave_compact_topm<MAXE>(keys, idxs, cnt, m);
+  for (int i = lane; i < k; i += kWave) dst[i] = i < m ? idxs[i] : -1;
+  __builtin_amdgcn_wave_barrier();
 }
 
 }  // namespace msa

@@ -23,47 +23,12 @@ struct TopkArgs {
 };
 
 constexpr int kWavesPerWG = 4;
-constexpr int kBatch = 16;  // 64-candidate chunks loaded together
-
-// Streams candidates [c_beg, c_end) of one row through the wave's running
-// top-m list (own block `cur` forced to the top key).  Up to kBatch chunks are
-// loaded at once, so a row costs one memory latency per batch, not per chunk.
-template <int MAXE>
-__device__ __forceinline__ void stream_candidates(const float* src, int c_beg, int c_end, int cur,
-                                                  int m, uint32_t* keys, int32_t* idxs, int& cnt,
-                                                  uint32_t& thr) {
-  constexpr int CAP = MAXE * kWave;
-  const int lane = lane_id();
-  for (int c0 = c_beg; c0 < c_end; c0 += kBatch * kWave) {
-    float v[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int c = c0 + i * kWave + lane;
-      v[i] = c < c_end ? src[c] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      if (c0 + i * kWave >= c_end) break;
-      const int c = c0 + i * kWave + lane;
-      const bool ok = c < c_end;
-      uint32_t key = 0;
-      if (ok) key = (c == cur) ? 0xffffffffu : score_key(v[i]);
-      cnt = wave_append(keys, idxs, cnt, ok && key > thr, key, c);
-      if (cnt > CAP - kWave) {
-        thr = wave_compact_topm<MAXE>(keys, idxs, cnt, m);
-        cnt = m;
-      }
-    }
-  }
-}
-
 template <int MAXE>
 __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
   constexpr int CAP = MAXE * kWave;
   __shared__ uint32_t skeys[kWavesPerWG][CAP];
   __shared__ int32_t sidx[kWavesPerWG][CAP];
   const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
   uint32_t* keys = skeys[wave];
   int32_t* idxs = sidx[wave];
   const long long stride = (long long)gridDim.x * kWavesPerWG;
@@ -72,15 +37,7 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
     const int b = (int)(row / ((long long)a.Sq * a.Hkv));
     const int pos = a.seq_lens ? min(max(a.seq_lens[b], 1), a.Skv) - 1 : a.q_start + t;
     const int cur = pos / kBlock;
-    const int m = min(a.k, cur + 1);
-    const float* src = a.scores + row * a.nblk;
-    int cnt = 0;
-    uint32_t thr = 0;
-    stream_candidates<MAXE>(src, 0, cur + 1, cur, m, keys, idxs, cnt, thr);
-    if (cnt > m) wave_compact_topm<MAXE>(keys, idxs, cnt, m);
-    int32_t* dst = a.sel + row * a.k;
-    for (int i = lane; i < a.k; i += kWave) dst[i] = i < m ? idxs[i] : -1;
-    __builtin_amdgcn_wave_barrier();
+    select_row<MAXE>(a.scores + row * a.nblk, cur, a.k, keys, idxs, a.sel + row * a.k);
   }
 }
 

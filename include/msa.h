@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 4
+#define MSA_ABI_VERSION 5
 
 typedef enum {
   MSA_OK = 0,
@@ -95,8 +95,20 @@ typedef struct {
   int32_t block_size;     /* 64; or 1 = token-level selection (see below) */
   int32_t top_k;          /* 1..256 blocks per KV head per query (own block included);
                              1..65536 tokens at block_size 1 */
-  float softmax_scale;    /* scale of q.k in the main branch, e.g. 1/sqrt(128) */
+  float softmax_scale;    /* scale of q.k in the main branch, e.g. 1/sqrt(128); must be
+                             finite and > 0 (<= 0: MSA_ERR_UNSUPPORTED) */
 } msa_problem;
+
+/* Arrival-counter region.  Launches whose work-groups hand data to each other
+ * (the decode forms of msa_index_topk_fused and msa_index_topk_fused_paged,
+ * where the last work-group of a sequence to finish selects its blocks) count
+ * arrivals in int32 counters in the first MSA_COUNTER_REGION_BYTES of their
+ * workspace.
+ * That region must be zero before the first call on a workspace (e.g. a
+ * zero-filled allocation); every call puts the counters it used back to zero,
+ * so a workspace stays valid for every later call of any shape it is large
+ * enough for.  Calls that share a workspace must not run concurrently. */
+#define MSA_COUNTER_REGION_BYTES (1u << 20)
 
 /* Operation ids for msa_workspace_bytes. */
 typedef enum {
@@ -107,7 +119,8 @@ typedef enum {
   MSA_OP_SPARSE_ATTN_DECODE = 4,
   MSA_OP_DENSE_ATTN_PREFILL = 5,
   MSA_OP_DENSE_ATTN_DECODE = 6,
-  MSA_OP_SPARSE_ATTN_PREFILL_BACKWARD = 7
+  MSA_OP_SPARSE_ATTN_PREFILL_BACKWARD = 7,
+  MSA_OP_INDEX_TOPK_FUSED_DECODE = 8   /* msa_index_topk_fused / _paged with seq_lens */
 } msa_op;
 
 /* Index branch: block scores.  For every sequence b, KV head h, row t and
@@ -135,15 +148,24 @@ msa_status msa_topk_blocks(const msa_problem* p, const float* block_scores,
                            const int32_t* seq_lens, int32_t* sel, hipStream_t stream);
 
 /* Index scoring and top-k in one pass: the same sel as msa_index_block_scores
- * followed by msa_topk_blocks, but block scores stream through a running
+ * followed by msa_topk_blocks.
+ * Prefill positions (seq_lens == NULL): block scores stream through a running
  * top-k and are never written to memory (needed at 1M-token contexts, where
- * they would take gigabytes).  Prefill positions only (seq_lens must be NULL);
+ * they would take gigabytes).  workspace: msa_workspace_bytes(p,
+ * MSA_OP_INDEX_TOPK_FUSED) bytes, any content; it holds per-split candidate
+ * lists.
+ * Decode positions (seq_lens != NULL): one launch scores every sequence's
+ * index-K cache and selects its blocks (the work-groups of a sequence count
+ * themselves in after writing its block scores; the last one selects).
+ * workspace: msa_workspace_bytes(p, MSA_OP_INDEX_TOPK_FUSED_DECODE) bytes: the
+ * arrival-counter region (see below), then the block scores [B][Hkv][nblk]
+ * fp32.  Sequences times (1 + ceil(nblk / 512)) must not exceed the 262144
+ * counters of the region (MSA_ERR_UNSUPPORTED).
  * iq and ik must be finite, as for msa_index_block_scores.
- * workspace: msa_workspace_bytes(p, MSA_OP_INDEX_TOPK_FUSED) bytes, any
- * content; it holds per-split candidate lists.
  * Source: as msa_index_block_scores and msa_topk_blocks; the 1M-token window
  * is named in the talk summary, section "MiniMax M3 combines agentic coding,
- * long context, and native multimodality". */
+ * long context, and native multimodality"; decode speed-ups in the news
+ * write-up, paragraph 7. */
 msa_status msa_index_topk_fused(const msa_problem* p, const void* iq, const void* ik,
                                 const int32_t* seq_lens, int32_t* sel, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
@@ -161,7 +183,15 @@ msa_status msa_index_topk_fused(const msa_problem* p, const void* iq, const void
  * content (may be NULL when that is 0).  For n_q_heads / n_kv_heads of 4 or 8
  * at block_size 64 it receives a transposed copy of V's context blocks,
  * B * n_kv_heads * ceil((q_start + seq_q) / 64) * 16 KiB, which the kernel
- * streams instead of V.
+ * streams instead of V, followed by a 256-byte status block.
+ * Failure mode: the work-groups of that kernel share K/V blocks through an LDS
+ * ring with bounded waits; a wait that exceeds its bound (never expected; it
+ * exists so that a fault elsewhere cannot hang the GPU) ends the call early
+ * and normally: the affected rows get NaN outputs and LSE, and the int32 word
+ * at msa_sparse_attn_prefill_status_offset() in the workspace reads 1 once the
+ * call has completed on the stream (0 after a complete call; the call clears
+ * it before its sweep).  The return value is MSA_OK either way, since nothing
+ * is known on the host when the call returns.
  * Source: topic page "MiniMax稀疏注意力", summary paragraph (exact attention
  * only over the selected blocks). */
 msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const void* k,
@@ -171,7 +201,8 @@ msa_status msa_sparse_attn_prefill(const msa_problem* p, const void* q, const vo
 /* Main branch, decode: as msa_sparse_attn_prefill for the single query of
  * each sequence at seq_lens[b] - 1, with the selected blocks split over
  * several work-groups whose partial softmax states are merged by
- * log-sum-exp.  workspace: msa_workspace_bytes(p, MSA_OP_SPARSE_ATTN_DECODE).
+ * log-sum-exp.  workspace: msa_workspace_bytes(p, MSA_OP_SPARSE_ATTN_DECODE)
+ * bytes, any content (it receives the split partials).
  * Source: as msa_sparse_attn_prefill; decode speed-ups over full attention are
  * reported in the news write-up, paragraph 7. */
 msa_status msa_sparse_attn_decode(const msa_problem* p, const void* q, const void* k_cache,
@@ -179,14 +210,19 @@ msa_status msa_sparse_attn_decode(const msa_problem* p, const void* q, const voi
                                   const int32_t* sel, void* out, float* lse, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
-/* Dense causal GQA attention over every key j <= pos(t) (the full-attention
- * baseline every speed-up on the pages is quoted against).  top_k is ignored. */
+/* Dense causal GQA attention over every key j <= pos(t): the full-attention
+ * baseline that the pages quote every speed-up against (news write-up,
+ * paragraph 7: about 9x prefill and 15x decode; topic page "MiniMax稀疏注意力",
+ * summary paragraph: 14.2x prefill and 7.6x decode over full attention on
+ * H800).  top_k is ignored; the workspace is unused (may be NULL). */
 msa_status msa_dense_attn_prefill(const msa_problem* p, const void* q, const void* k,
                                   const void* v, void* out, float* lse, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
 /* Dense decode: every key j < seq_lens[b], split over work-groups and merged by
- * log-sum-exp.  workspace: msa_workspace_bytes(p, MSA_OP_DENSE_ATTN_DECODE). */
+ * log-sum-exp; the full-attention baseline of the decode speed-ups (news
+ * write-up, paragraph 7; topic page "MiniMax稀疏注意力", summary paragraph).
+ * workspace: msa_workspace_bytes(p, MSA_OP_DENSE_ATTN_DECODE), any content. */
 msa_status msa_dense_attn_decode(const msa_problem* p, const void* q, const void* k_cache,
                                  const void* v_cache, const int32_t* seq_lens, void* out,
                                  float* lse, void* workspace, size_t workspace_bytes,
@@ -214,7 +250,14 @@ msa_status msa_index_block_scores_paged(const msa_problem* p, const void* iq,
                                         int32_t num_pages, const int32_t* seq_lens,
                                         float* block_scores, hipStream_t stream);
 
-/* workspace: msa_workspace_bytes(p, MSA_OP_SPARSE_ATTN_DECODE). */
+/* The decode form of msa_index_topk_fused on a paged index-K cache (same
+ * workspace and counter rules; pages as for msa_index_block_scores_paged). */
+msa_status msa_index_topk_fused_paged(const msa_problem* p, const void* iq, const void* ik_pages,
+                                      const int32_t* page_table, int32_t num_pages,
+                                      const int32_t* seq_lens, int32_t* sel, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/* workspace: as msa_sparse_attn_decode. */
 msa_status msa_sparse_attn_decode_paged(const msa_problem* p, const void* q,
                                         const void* k_pages, const void* v_pages,
                                         const int32_t* page_table, int32_t num_pages,
@@ -248,6 +291,18 @@ msa_status msa_sparse_attn_prefill_backward(const msa_problem* p, const void* q,
                                             const float* lse, const void* dout, float* dq,
                                             float* dk, float* dv, void* workspace,
                                             size_t workspace_bytes, hipStream_t stream);
+
+/* Byte offset, inside the workspace of msa_sparse_attn_prefill for problem p,
+ * of the int32 status word described there (0: complete; 1: a bounded wait
+ * gave up).  MSA_ERR_UNSUPPORTED for shapes whose kernel has no bounded wait
+ * (group sizes other than 4 and 8, block_size 1).  Host only. */
+msa_status msa_sparse_attn_prefill_status_offset(const msa_problem* p, size_t* offset);
+
+/* Testing only: the number of polls of a ring tag after which a wave of the
+ * sparse prefill gives up (process-wide; <= 0 restores the default, 2^22).
+ * A tiny bound forces the failure path above with every kernel still
+ * exiting normally. */
+void msa_set_wait_limit(int32_t polls);
 
 /* Workspace bytes an operation needs for problem p (0 if none).  Host only. */
 msa_status msa_workspace_bytes(const msa_problem* p, msa_op op, size_t* bytes);

@@ -69,18 +69,38 @@ def assert_attention_close(gpu, ref, what=""):
     return mx, mean
 
 
+def boundary_blocks(seq_q: int, q_start: int, block: int, n_log: int) -> list[int]:
+    """At least n_log distinct query blocks (absolute block ids) past the
+    first two blocks of the rows, log-spaced over the rest of the range (all
+    of them when fewer exist).  Block ids are drawn directly, so rounding
+    never collapses two positions into one block."""
+    first = q_start // block
+    last = (q_start + seq_q - 1) // block
+    lo = first + 2
+    n_cand = last - lo + 1
+    if n_cand <= 0:
+        return []
+    if n_cand <= n_log:
+        return list(range(lo, last + 1))
+    n = n_log
+    while True:
+        xs = np.unique(np.round(np.geomspace(1, n_cand, n)).astype(np.int64))
+        if len(xs) >= n_log:
+            return [lo + int(x) - 1 for x in xs]
+        n += 1
+
+
 def sample_rows(seq_q: int, q_start: int, block: int, seed: int, n_uniform: int = 2048,
                 n_log: int = 32) -> np.ndarray:
     """Stratified row sample: all rows of the first two blocks, the last 64
-    rows, rows with pos % 64 in {0, 63} at >= n_log log-spaced positions, and
-    n_uniform uniform random rows."""
+    rows, both boundary rows (pos % 64 in {0, 63}) of >= n_log distinct
+    log-spaced blocks, and n_uniform uniform random rows."""
     rng = np.random.default_rng(seed)
-    rows = set(range(min(seq_q, 2 * block)))
+    rows = set(range(min(seq_q, 2 * block - q_start % block)))
     rows |= set(range(max(0, seq_q - 64), seq_q))
-    for x in np.unique(np.geomspace(1, max(seq_q - 1, 1), n_log).astype(np.int64)):
-        base = ((q_start + int(x)) // block) * block - q_start
-        for t in (base, base + block - 1):
+    for c in boundary_blocks(seq_q, q_start, block, n_log):
+        for t in (c * block - q_start, c * block + block - 1 - q_start):
             if 0 <= t < seq_q:
                 rows.add(t)
-    rows |= set(rng.integers(0, seq_q, size=min(n_uniform, seq_q)).tolist())
+    rows |= set(rng.choice(seq_q, size=min(n_uniform, seq_q), replace=False).tolist())
     return np.array(sorted(rows), dtype=np.int64)

@@ -20,7 +20,7 @@ NULL = None
 
 def declared():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:msa_status|const char\s*\*|int)\s+(msa_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:msa_status|const char\s*\*|int|void)\s+(msa_\w+)\s*\(",
                                  src, re.M)))
 
 
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = binding.lib()
-    assert L.msa_abi_version() == 4
+    assert L.msa_abi_version() == 5
     for code, name in binding.STATUS.items():
         assert L.msa_status_string(code).decode() == name
 
@@ -125,7 +125,9 @@ def test_paged_decode_rules():
 
 def test_fused_rules():
     p = prob(CHUNK_1M)
-    assert call("msa_index_topk_fused", P(p), A, A, A4, A4, A, 1 << 40, NULL)[0] == 2  # decode
+    # seq_lens selects the decode form, which needs a decode problem (seq_q == 1)
+    st, msg = call("msa_index_topk_fused", P(p), A, A, A4, A4, A, 1 << 40, NULL)
+    assert st == 1 and "decode" in msg, msg
     need = ctypes.c_size_t()
     assert call("msa_workspace_bytes", P(p), 2, ctypes.byref(need))[0] == 0
     if need.value:
@@ -133,11 +135,34 @@ def test_fused_rules():
         assert st == 3, msg
 
 
+def test_fused_decode_rules():
+    """Decode form of the fused index + top-k: block scores, then B arrival
+    counters at the end of the workspace; pointers and size checked first."""
+    d = prob(DECODE_32x256K)
+    need = ctypes.c_size_t()
+    assert call("msa_workspace_bytes", P(d), 8, ctypes.byref(need))[0] == 0
+    assert need.value == (1 << 20) + 32 * 4 * 4096 * 4
+    st, msg = call("msa_index_topk_fused", P(d), A, A, A4, A4, A, need.value - 1, NULL)
+    assert st == 3 and "workspace" in msg, msg
+    st, msg = call("msa_index_topk_fused", P(d), A, A, A4, A4, NULL, need.value, NULL)
+    assert st == 1, msg
+    st, msg = call("msa_index_topk_fused_paged", P(d), A, A, A4, 0, A4, A4, A, need.value, NULL)
+    assert st == 1 and "num_pages" in msg, msg
+    st, msg = call("msa_index_topk_fused_paged", P(d), A, A, NULL, 5, A4, A4, A, need.value, NULL)
+    assert st == 1, msg
+    # more sequences than the fixed counter region holds
+    big = prob(DECODE_32x256K, batch=65535)  # 9 counters per sequence
+    st, msg = call("msa_index_topk_fused", P(big), A, A, A4, A4, A, 1 << 60, NULL)
+    assert st == 2 and "counters" in msg, msg
+    # prefill problems have no decode workspace
+    assert call("msa_workspace_bytes", P(prob(PREFILL_32K)), 8, ctypes.byref(need))[0] != 0
+
+
 def test_workspace_bytes_every_op_and_workload():
     for w in ALL:
         p = prob(w)
-        for op in range(8):
-            is_decode_op = op in (4, 6)
+        for op in range(9):
+            is_decode_op = op in (4, 6, 8)
             out = ctypes.c_size_t(12345)
             st, msg = call("msa_workspace_bytes", P(p), op, ctypes.byref(out))
             if is_decode_op and not w.decode:
@@ -156,17 +181,42 @@ def test_sparse_prefill_workspace_rules():
     p = prob()  # 128K, G = 8
     need = ctypes.c_size_t()
     assert call("msa_workspace_bytes", P(p), 3, ctypes.byref(need))[0] == 0
-    assert need.value == 1 * 4 * (131072 // 64) * 16384
+    assert need.value == 1 * 4 * (131072 // 64) * 16384 + 256
+    off = ctypes.c_size_t()
+    assert call("msa_sparse_attn_prefill_status_offset", P(p), ctypes.byref(off))[0] == 0
+    assert off.value == need.value - 256 and off.value % 256 == 0
     st, msg = call("msa_sparse_attn_prefill", P(p), A, A, A, A4, A, NULL, A, need.value - 1, NULL)
     assert st == 3 and "workspace" in msg, msg
     st, msg = call("msa_sparse_attn_prefill", P(p), A, A, A, A4, A, NULL, NULL, need.value, NULL)
     assert st == 1, msg
     chunk = prob(CHUNK_1M)  # context = q_start + seq_q = 1048576 tokens
     assert call("msa_workspace_bytes", P(chunk), 3, ctypes.byref(need))[0] == 0
-    assert need.value == 4 * (1048576 // 64) * 16384
+    assert need.value >= 4 * (1048576 // 64) * 16384 + 256
     for kw in (dict(n_q_heads=8), dict(block_size=1, top_k=4096)):  # G = 2; tokens
         assert call("msa_workspace_bytes", P(prob(**kw)), 3, ctypes.byref(need))[0] == 0
         assert need.value == 0, kw
+        st, msg = call("msa_sparse_attn_prefill_status_offset", P(prob(**kw)), ctypes.byref(off))
+        assert st == 2 and "bounded" in msg, msg
+    assert call("msa_sparse_attn_prefill_status_offset", P(p), NULL)[0] == 1
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.088, float("-inf"), float("nan")])
+def test_softmax_scale_must_be_positive(scale):
+    """A scale <= 0 is rejected before launch by every entry point (the tiled
+    kernels take the running max on unscaled scores); non-finite is invalid."""
+    p = prob(softmax_scale=scale)
+    code = 2 if scale == scale and abs(scale) != float("inf") else 1
+    st, msg = call("msa_sparse_attn_prefill", P(p), A, A, A, A4, A, NULL, A, 1 << 40, NULL)
+    assert st == code and "softmax_scale" in msg, (st, msg)
+    d = prob(DECODE_32x256K, softmax_scale=scale)
+    st, msg = call("msa_sparse_attn_decode", P(d), A, A, A, A4, A4, A, NULL, A, 1 << 40, NULL)
+    assert st == code and "softmax_scale" in msg, (st, msg)
+
+
+def test_wait_limit_knob_is_host_only():
+    L = binding.lib()
+    L.msa_set_wait_limit(5)
+    L.msa_set_wait_limit(0)  # back to the default
 
 
 def test_token_level_rules():

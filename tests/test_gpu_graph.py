@@ -1,8 +1,9 @@
-"""The decode step (index block scores -> top-k -> split-K sparse attention and
-its merge) captured once as a HIP graph and replayed, the serving form of the
-step: one launch per step and no host work.  The library allocates,
-synchronises and clears nothing itself, so the captured kernels are exactly
-the eager ones.  Every replay, with eager library work on other inputs between
+"""The decode step (index scoring with its in-launch top-k -> split-K sparse
+attention and its merge) captured once as a HIP graph and replayed, the
+serving form of the step: one launch per step and no host work.  The library
+allocates, synchronises and clears nothing itself (the index launch's arrival
+counters are put back to zero by the kernel that counts them), so the
+captured kernels are exactly the eager ones.  Every replay, with eager library work on other inputs between
 replays, must give the eager step's selection, output and LSE bit for bit, and
 the output must match the oracle."""
 import numpy as np
@@ -32,17 +33,20 @@ def test_decode_step_graph_replays_match_eager():
     sel = torch.empty((w.batch, w.n_kv_heads, 1, w.top_k), dtype=torch.int32, device=DEV)
     out = torch.empty_like(inp.q)
     lse = torch.empty((w.batch, w.n_q_heads, 1), dtype=torch.float32, device=DEV)
-    ws = torch.empty(msa.msa_workspace_bytes(p, "sparse_attn_decode"), dtype=torch.uint8,
-                     device=DEV)
+    ws = msa.decode_workspace(p, device=DEV)  # arrival counters zero; every call leaves them zero
 
-    def step(x):
-        msa.msa_index_block_scores(p, x.iq, x.ik, x.seq_lens, bs)
-        msa.msa_topk_blocks(p, bs, x.seq_lens, sel)
+    ws_i = msa.decode_workspace(p, op="index_topk_fused_decode", device=DEV)
+
+    def step(x):  # the two-launch step: index + top-k, attention + merge
+        msa.msa_index_topk_fused(p, x.iq, x.ik, x.seq_lens, sel, ws_i)
         msa.msa_sparse_attn_decode(p, x.q, x.k, x.v, x.seq_lens, sel, out, lse, ws)
 
     step(inp)
     torch.cuda.synchronize()
     want = (sel.clone(), out.clone(), lse.clone())
+    # the same selection as block scores + top-k
+    assert torch.equal(want[0], msa.msa_topk_blocks(p, msa.msa_index_block_scores(
+        p, inp.iq, inp.ik, inp.seq_lens, bs), inp.seq_lens))
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -61,6 +65,8 @@ def test_decode_step_graph_replays_match_eager():
         assert torch.equal(sel, want[0]), f"replay {r}: selection"
         assert torch.equal(out.view(torch.int16), want[1].view(torch.int16)), f"replay {r}: output"
         assert torch.equal(lse, want[2]), f"replay {r}: lse"
+    counters = ws_i[:1 << 20].view(torch.int32)  # the index launch's arrival counters
+    assert int(counters.abs().sum().item()) == 0, "arrival counters not left at zero"
     po = O.Problem(w.batch, 1, w.seq_kv, 0, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_idx_heads,
                    w.idx_head_dim, w.block_size, w.top_k, True, w.softmax_scale)
     q, k, v = bf16_bits(inp.q), bf16_bits(inp.k), bf16_bits(inp.v)

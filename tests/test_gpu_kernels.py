@@ -320,3 +320,36 @@ def test_prefill_ignores_cache_rows_past_the_context(heads):
     assert torch.isfinite(a.float()).all()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(lse_a, lse_b)
+
+
+def test_sparse_prefill_bounded_wait_failure_is_reported():
+    """The tile-union kernel's ring waits are bounded.  With the bound forced
+    down to one poll from the host, waves give up early: every kernel still
+    exits normally, the affected rows hold NaN and the workspace's status word
+    reads 1.  With the default bound restored the same call is complete (word
+    0) and equals a call made before the knob was touched."""
+    need_gpu()
+    w = PREFILL_32K.shrink(seq_q=4096, seq_kv=4096)
+    inp = generate(w, DEV)
+    p = msa.Problem.from_workload(w)
+    sel = msa.msa_topk_blocks(p, msa.msa_index_block_scores(p, inp.iq, inp.ik))
+    off = msa.msa_sparse_attn_prefill_status_offset(p)
+    ws = torch.full((msa.msa_workspace_bytes(p, "sparse_attn_prefill"),), 7, dtype=torch.uint8,
+                    device=DEV)
+    word = lambda: int(ws[off:off + 4].view(torch.int32).item())
+    ref = msa.msa_sparse_attn_prefill(p, inp.q, inp.k, inp.v, sel, workspace=ws)
+    torch.cuda.synchronize()
+    assert word() == 0 and bool(torch.isfinite(ref.float()).all())
+    try:
+        msa.msa_set_wait_limit(1)
+        bad = msa.msa_sparse_attn_prefill(p, inp.q, inp.k, inp.v, sel, workspace=ws)
+        torch.cuda.synchronize()
+        nan_rows = int(torch.isnan(bad.float()).any(dim=3).any(dim=2).sum().item())  # [B][Sq]
+        print(f"forced give-up: status word {word()}, rows with NaN {nan_rows} of {w.seq_q}",
+              flush=True)
+        assert word() == 1 and nan_rows > 0
+    finally:
+        msa.msa_set_wait_limit(0)
+    again = msa.msa_sparse_attn_prefill(p, inp.q, inp.k, inp.v, sel, workspace=ws)
+    torch.cuda.synchronize()
+    assert word() == 0 and torch.equal(again, ref)

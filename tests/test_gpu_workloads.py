@@ -40,6 +40,7 @@ def test_prefill_32k_sampled():
     WC.check(w, False, rows, log=log)
 
 
+@pytest.mark.timeout(900)
 def test_prefill_128k_sampled():
     need_gpu()
     w = PREFILL_128K
@@ -52,10 +53,11 @@ def test_decode_32x256k_all_rows():
     WC.check(DECODE_32x256K, False, log=log)
 
 
+@pytest.mark.timeout(1200)
 def test_chunk_prefill_1m_fused_sampled():
     need_gpu()
     w = CHUNK_1M
-    rows = PAR.sample_rows(w.seq_q, w.q_start, w.block_size, seed=1024, n_uniform=384, n_log=16)
+    rows = PAR.sample_rows(w.seq_q, w.q_start, w.block_size, seed=1024, n_uniform=2048, n_log=32)
     WC.check(w, True, rows, log=log)
 
 
