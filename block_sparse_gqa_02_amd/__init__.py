@@ -14,4 +14,5 @@ from .binding import (Problem, MsaError, abi_version, decode_workspace,  # noqa:
                       msa_sparse_attn_prefill_backward,
                       msa_sparse_attn_decode_paged, msa_sparse_attn_prefill, msa_topk_blocks,
                       msa_sparse_attn_prefill_status_offset, msa_set_wait_limit,
+                      msa_sparse_attn_decode_static,
                       msa_workspace_bytes)

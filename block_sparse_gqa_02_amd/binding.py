@@ -99,6 +99,7 @@ def lib():
                                                  sz, vp],
             "msa_sparse_attn_prefill_status_offset": [pr, P(sz)],
             "msa_index_topk_fused_paged": [pr, vp, vp, vp, ctypes.c_int32, vp, vp, vp, sz, vp],
+            "msa_sparse_attn_decode_static": [pr, vp, vp, vp, vp, vp, vp, vp, vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -258,6 +259,18 @@ def msa_sparse_attn_decode(p: Problem, q, k_cache, v_cache, seq_lens, sel, out=N
                                         _ptr(sel, torch.int32), _ptr(out, torch.bfloat16),
                                         _ptr(lse, torch.float32), _ptr(ws), nbytes,
                                         _stream(stream)))
+    return out
+
+
+def msa_sparse_attn_decode_static(p: Problem, q, k_cache, v_cache, seq_lens, sel, out=None,
+                                  lse=None, stream=None):
+    """msa_sparse_attn_decode with the library's own scratch (no workspace)."""
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().msa_sparse_attn_decode_static(
+        ctypes.byref(p.c()), _ptr(q, torch.bfloat16), _ptr(k_cache, torch.bfloat16),
+        _ptr(v_cache, torch.bfloat16), _ptr(seq_lens, torch.int32), _ptr(sel, torch.int32),
+        _ptr(out, torch.bfloat16), _ptr(lse, torch.float32), _stream(stream)))
     return out
 
 

@@ -255,6 +255,36 @@ msa_status msa_sparse_attn_decode(const msa_problem* p, const void* q, const voi
                        workspace_bytes, stream, "msa_sparse_attn_decode");
 }
 
+msa_status msa_sparse_attn_decode_static(const msa_problem* p, const void* q, const void* k_cache,
+                                         const void* v_cache, const int32_t* seq_lens,
+                                         const int32_t* sel, void* out, float* lse,
+                                         hipStream_t stream) {
+  msa::Shape s;
+  msa_status st = check_problem(p, Mode::kDecode, true, &s);
+  if (st != MSA_OK) return st;
+  NEED_PTR(q);
+  NEED_PTR(k_cache);
+  NEED_PTR(v_cache);
+  NEED_PTR4(seq_lens);
+  NEED_PTR4(sel);
+  NEED_PTR(out);
+  if (lse && !aligned(lse, 4)) return fail(MSA_ERR_INVALID_ARGUMENT, "lse is not 4-byte aligned");
+  const size_t need = msa::decode_workspace_bytes(s, false);
+  if (need > msa::decode_scratch_bytes())
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL,
+                "this problem needs %zu bytes of scratch; the library's static decode scratch "
+                "holds %zu (use msa_sparse_attn_decode with a workspace)",
+                need, msa::decode_scratch_bytes());
+  void* scratch = nullptr;
+  const hipError_t e = msa::decode_scratch(&scratch);
+  if (e != hipSuccess)
+    return fail(MSA_ERR_HIP, "msa_sparse_attn_decode_static: scratch address: %s",
+                hipGetErrorString(e));
+  return launched(msa::launch_attn_decode(s, q, k_cache, v_cache, seq_lens, sel, out, lse, scratch,
+                                          msa::decode_scratch_bytes(), stream),
+                  "msa_sparse_attn_decode_static");
+}
+
 msa_status msa_dense_attn_prefill(const msa_problem* p, const void* q, const void* k,
                                   const void* v, void* out, float* lse, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {

@@ -20,6 +20,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <mutex>
+
 namespace msa {
 namespace {
 
@@ -258,6 +260,34 @@ hipError_t launch_dense_attn_prefill_rowwise(const Shape& s, const void* q, cons
                                              const void* v, void* out, float* lse,
                                              hipStream_t st) {
   return launch_sparse_attn_prefill(s, q, k, v, nullptr, out, lse, nullptr, st);
+}
+
+// The decode partials of msa_sparse_attn_decode_static, for callers that
+// cannot allocate: one copy per GPU the library runs on, held until the
+// process ends.  In host code `scratch` only names the symbol; its device
+// address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = 16u << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* dev_ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with device `dev` current
+    if (e != hipSuccess) return e;
+    dev_ptr[dev] = p;
+  }
+  *ptr = dev_ptr[dev];
+  return hipSuccess;
 }
 
 size_t decode_workspace_bytes(const Shape& s, bool dense) {

@@ -85,6 +85,10 @@ hipError_t launch_union_prefill(const Shape& s, const void* q, const void* k, co
                                 hipStream_t st);
 // Decode workspace: the split partials (any content).
 size_t decode_workspace_bytes(const Shape& s, bool dense);
+// The library's static decode scratch on the current device: its size, and
+// its device address (hipGetSymbolAddress on the first call per device).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** ptr);
 // sel == NULL: dense; pg: k and v are pools of [num_pages][Hkv][64][128] pages.
 hipError_t launch_attn_decode(const Shape& s, const void* q, const void* k, const void* v,
                               const int32_t* seq_lens, const int32_t* sel, void* out, float* lse,

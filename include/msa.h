@@ -210,6 +210,25 @@ msa_status msa_sparse_attn_decode(const msa_problem* p, const void* q, const voi
                                   const int32_t* sel, void* out, float* lse, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
+/* msa_sparse_attn_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and results, with the split partials in a
+ * scratch array of 16 MiB that the library itself holds on every GPU it runs
+ * on until the process ends, instead of a caller's workspace.  The call
+ * allocates nothing.  The scratch is that of the device current on the calling
+ * thread (stream must belong to it); its address is looked up on the first
+ * call on a device.  A problem that needs more than 16 MiB of partials
+ * (msa_workspace_bytes(p, MSA_OP_SPARSE_ATTN_DECODE) > 16 MiB; 32 sequences of
+ * 4 KV heads at top_k 64 need 4.3 MB) returns MSA_ERR_WORKSPACE_TOO_SMALL
+ * and launches nothing.  Every call on a GPU shares that GPU's one scratch:
+ * calls that overlap on one GPU (other streams, other threads) race and must
+ * be serialised by the caller.  Each call overwrites what it uses and needs
+ * no clearing. */
+msa_status msa_sparse_attn_decode_static(const msa_problem* p, const void* q, const void* k_cache,
+                                         const void* v_cache, const int32_t* seq_lens,
+                                         const int32_t* sel, void* out, float* lse,
+                                         hipStream_t stream);
+
 /* Dense causal GQA attention over every key j <= pos(t): the full-attention
  * baseline that the pages quote every speed-up against (news write-up,
  * paragraph 7: about 9x prefill and 15x decode; topic page "MiniMax稀疏注意力",

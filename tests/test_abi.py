@@ -213,6 +213,19 @@ def test_softmax_scale_must_be_positive(scale):
     assert st == code and "softmax_scale" in msg, (st, msg)
 
 
+def test_static_decode_rules():
+    """The allocation-free decode validates like msa_sparse_attn_decode and
+    refuses, before touching the GPU, problems whose partials exceed its 16 MiB."""
+    d = prob(DECODE_32x256K)
+    assert call("msa_sparse_attn_decode_static", P(d), NULL, A, A, A4, A4, A, NULL, NULL)[0] == 1
+    assert call("msa_sparse_attn_decode_static", P(d), A, A, A, A4, NULL, A, NULL, NULL)[0] == 1
+    big = prob(DECODE_32x256K, batch=4096)
+    st, msg = call("msa_sparse_attn_decode_static", P(big), A, A, A, A4, A4, A, NULL, NULL)
+    assert st == 3 and "scratch" in msg, msg
+    st, msg = call("msa_sparse_attn_decode_static", P(prob()), A, A, A, A4, A4, A, NULL, NULL)
+    assert st == 1 and "seq_q" in msg, msg  # a prefill problem
+
+
 def test_wait_limit_knob_is_host_only():
     L = binding.lib()
     L.msa_set_wait_limit(5)
