@@ -404,7 +404,7 @@ msa_status msa_sparse_attn_prefill_status_offset(const msa_problem* p, size_t* o
   if (st != MSA_OK) return st;
   if (s.bs != 64 || !msa::union_prefill_supported(s))
     return fail(MSA_ERR_UNSUPPORTED, "this shape runs a kernel without bounded waits (no status word)");
-  *offset = msa::union_prefill_status_offset(s);
+  *offset = msa::sparse_prefill_status_offset(s);
   return ok();
 }
 

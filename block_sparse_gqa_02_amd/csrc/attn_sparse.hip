@@ -238,7 +238,13 @@ int decode_nsplit(const Shape& s, bool dense) {
 }  // namespace
 
 size_t sparse_prefill_workspace_bytes(const Shape& s) {
-  return union_prefill_supported(s) ? union_prefill_workspace_bytes(s) : 0;
+  if (!union_prefill_supported(s)) return 0;
+  return kvs_prefill_preferred(s) ? kvs_prefill_workspace_bytes(s)
+                                  : union_prefill_workspace_bytes(s);
+}
+
+size_t sparse_prefill_status_offset(const Shape& s) {
+  return kvs_prefill_preferred(s) ? 0 : union_prefill_status_offset(s);
 }
 
 hipError_t launch_sparse_attn_prefill(const Shape& s, const void* q, const void* k, const void* v,
@@ -248,8 +254,10 @@ hipError_t launch_sparse_attn_prefill(const Shape& s, const void* q, const void*
                 static_cast<const uint16_t*>(v), sel, static_cast<uint16_t*>(out), lse,
                 s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.G, s.top_k, s.scale * kLog2e,
                 (long long)s.B * s.Hkv * s.Sq};
-  if (sel && union_prefill_supported(s))
+  if (sel && union_prefill_supported(s)) {
+    if (kvs_prefill_preferred(s)) return launch_kvs_prefill(s, q, k, v, sel, out, lse, ws, st);
     return launch_union_prefill(s, q, k, v, sel, out, lse, ws, st);
+  }
   const long long grid = (a.units + kAttnWaves - 1) / kAttnWaves;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   sparse_prefill_kernel<<<(unsigned)grid, 256, 0, st>>>(a);

@@ -532,6 +532,17 @@ static std::atomic<int> g_spin_limit{kDefaultSpinLimit};
 
 void set_union_spin_limit(int spins) { g_spin_limit.store(spins > 0 ? spins : kDefaultSpinLimit); }
 
+hipError_t launch_vt_tiles(const Shape& s, const void* v, void* ws, hipStream_t st) {
+  const int nblk_ctx = context_blocks(s);
+  const long long tiles_vt = (long long)s.B * s.Hkv * nblk_ctx;
+  if (tiles_vt > 0x7fffffffLL) return hipErrorInvalidValue;
+  int32_t* status = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + vt_bytes(s));
+  VtArgs t{static_cast<const uint16_t*>(v), static_cast<uint16_t*>(ws), status, s.Skv,
+           s.q_start + s.Sq, nblk_ctx};
+  vt_kernel<<<(unsigned)tiles_vt, 256, 0, st>>>(t);
+  return hipGetLastError();
+}
+
 hipError_t launch_union_prefill(const Shape& s, const void* q, const void* k, const void* v,
                                 const int32_t* sel, void* out, float* lse, void* ws,
                                 hipStream_t st) {
@@ -544,10 +555,7 @@ hipError_t launch_union_prefill(const Shape& s, const void* q, const void* k, co
   const long long grid = (long long)ntiles * s.Hkv * s.B;
   if (grid > 0x7fffffffLL || tiles_vt > 0x7fffffffLL) return hipErrorInvalidValue;
   int32_t* status = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + vt_bytes(s));
-  VtArgs t{static_cast<const uint16_t*>(v), static_cast<uint16_t*>(ws), status, s.Skv,
-           s.q_start + s.Sq, nblk_ctx};
-  vt_kernel<<<(unsigned)tiles_vt, 256, 0, st>>>(t);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_vt_tiles(s, v, ws, st);
   if (e != hipSuccess) return e;
   UnionArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
               static_cast<const uint16_t*>(ws), sel, static_cast<uint16_t*>(out), lse, status,

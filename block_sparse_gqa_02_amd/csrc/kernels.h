@@ -70,6 +70,8 @@ hipError_t launch_index_topk_fused(const Shape& s, const void* iq, const void* i
 // Sparse attention.  ws: sparse_prefill_workspace_bytes(s) bytes (the
 // tile-union kernel's transposed V tiles; unused by the row-wise kernel).
 size_t sparse_prefill_workspace_bytes(const Shape& s);
+// Byte offset of the int32 status word in that workspace (tiled schedules).
+size_t sparse_prefill_status_offset(const Shape& s);
 hipError_t launch_sparse_attn_prefill(const Shape& s, const void* q, const void* k,
                                       const void* v, const int32_t* sel, void* out, float* lse,
                                       void* ws, hipStream_t st);
@@ -83,6 +85,17 @@ void set_union_spin_limit(int spins);
 hipError_t launch_union_prefill(const Shape& s, const void* q, const void* k, const void* v,
                                 const int32_t* sel, void* out, float* lse, void* ws,
                                 hipStream_t st);
+// The transposed V tiles of the context (start of ws), and the status word
+// after them cleared; shared by both tiled schedules.
+hipError_t launch_vt_tiles(const Shape& s, const void* v, void* ws, hipStream_t st);
+// KV-block-stationary schedule of the sparse prefill (G = 4 and 8), used when a
+// tile-union tile's rows would select fewer blocks than the context holds.
+// Its workspace starts with the 256-byte status word.
+bool kvs_prefill_preferred(const Shape& s);
+size_t kvs_prefill_workspace_bytes(const Shape& s);
+hipError_t launch_kvs_prefill(const Shape& s, const void* q, const void* k, const void* v,
+                              const int32_t* sel, void* out, float* lse, void* ws,
+                              hipStream_t st);
 // Decode workspace: the split partials (any content).
 size_t decode_workspace_bytes(const Shape& s, bool dense);
 // The library's static decode scratch on the current device: its size, and

@@ -60,6 +60,14 @@ PREFILL_SMALL = [
     # rows past 512 causal blocks: the tile-union kernel's block windows roll over
     ("g4_two_windows", dict(seq_q=300, seq_kv=40000, q_start=39700, n_q_heads=8, n_kv_heads=2, top_k=24)),
     ("g8_two_windows", dict(seq_q=200, seq_kv=36000, q_start=35800, n_q_heads=16, n_kv_heads=2, top_k=24)),
+    # a tile's rows select fewer blocks than the context holds (48 k < 625 for
+    # groups of 8, 96 k < 625 for groups of 4): the KV-block-stationary schedule
+    ("g8_kvs", dict(seq_q=310, seq_kv=40000, q_start=39690, n_q_heads=16, n_kv_heads=2, top_k=8)),
+    ("g4_kvs", dict(seq_q=250, seq_kv=40000, q_start=39750, n_q_heads=8, n_kv_heads=2, top_k=5)),
+    ("g8_kvs_batch2_k1", dict(batch=2, seq_q=130, seq_kv=20000, q_start=19870, n_q_heads=32,
+                              n_kv_heads=4, top_k=1)),
+    ("g8_kvs_batch2", dict(batch=2, seq_q=200, seq_kv=20000, q_start=19800, n_q_heads=32,
+                           n_kv_heads=4, top_k=6)),
 ]
 
 
