@@ -376,3 +376,95 @@ int oracle_attend_backward(const oracle_problem* p, const double* q, const doubl
   free(o);
   return rc;
 }
+
+/* Index-branch KL loss and its gradient (see msa_oracle.h).  Per row (b, t)
+ * and index head i with KV head h = i mod Hkv, over the tokens T that h
+ * attends: P = the main branch's softmax over T averaged over h's query heads
+ * (a target: nothing flows back into q or k), Q = softmax over T of the raw
+ * index dot products, loss = sum_j P_j (log P_j - log Q_j); the loss's
+ * derivative by index score j is Q_j - P_j. */
+int oracle_index_kl(const oracle_problem* p, const double* q, const double* k, const double* iq,
+                    const double* ik, const int32_t* seq_lens, const int32_t* sel_all,
+                    double* loss, double* diq, double* dik) {
+  if (!problem_ok(p) || !q || !k || !iq || !ik || !sel_all || !loss || !diq || !dik)
+    return ORACLE_EBADARG;
+  const int32_t D = p->head_dim, Di = p->idx_head_dim, K = p->top_k;
+  const int32_t Hq = p->n_q_heads, Hkv = p->n_kv_heads, Hi = p->n_idx_heads;
+  const int32_t G = Hq / Hkv;
+  for (int64_t x = 0; x < (int64_t)p->batch * p->seq_q * Hi; ++x) loss[x] = 0.0;
+  for (int64_t x = 0; x < (int64_t)p->batch * p->seq_q * Hi * Di; ++x) diq[x] = 0.0;
+  for (int64_t x = 0; x < (int64_t)p->batch * p->seq_kv * Di; ++x) dik[x] = 0.0;
+  const size_t cap = (size_t)K * p->block_size;
+  int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * cap);
+  double* P = (double*)malloc(sizeof(double) * cap);
+  double* w = (double*)malloc(sizeof(double) * cap);
+  double* Q = (double*)malloc(sizeof(double) * cap);
+  if (!tok || !P || !w || !Q) { free(tok); free(P); free(w); free(Q); return ORACLE_ENOMEM; }
+  int rc = ORACLE_OK;
+  for (int32_t b = 0; b < p->batch && rc == ORACLE_OK; ++b) {
+    for (int32_t t = 0; t < p->seq_q && rc == ORACLE_OK; ++t) {
+      const int32_t pos = oracle_position(p, seq_lens, b, t);
+      if (pos < 0) { rc = ORACLE_EBADARG; break; }
+      const int32_t* sel_row = sel_all + ((int64_t)b * p->seq_q + t) * Hkv * K;
+      for (int32_t i = 0; i < Hi; ++i) {
+        const int32_t h = i % Hkv;
+        const int32_t n = selected_tokens(p, sel_row + (int64_t)h * K, pos, tok);
+        if (n < 0) { rc = ORACLE_EBADARG; break; }
+        if (n == 0) continue;
+        const int64_t kvbase = ((int64_t)b * Hkv + h) * p->seq_kv;
+        /* P: the G query heads' softmax weights, averaged */
+        for (int32_t a = 0; a < n; ++a) P[a] = 0.0;
+        for (int32_t hq = h * G; hq < (h + 1) * G; ++hq) {
+          const double* qv = q + (((int64_t)b * p->seq_q + t) * Hq + hq) * D;
+          double zmax = -INFINITY;
+          for (int32_t a = 0; a < n; ++a) {
+            const double* kv = k + (kvbase + tok[a]) * D;
+            double s = 0.0;
+            for (int32_t d = 0; d < D; ++d) s += qv[d] * kv[d];
+            w[a] = p->softmax_scale * s;
+            if (w[a] > zmax) zmax = w[a];
+          }
+          double l = 0.0;
+          for (int32_t a = 0; a < n; ++a) { w[a] = exp(w[a] - zmax); l += w[a]; }
+          for (int32_t a = 0; a < n; ++a) P[a] += w[a] / l / G;
+        }
+        /* Q: softmax of the raw index dot products */
+        const double* iv = iq + (((int64_t)b * p->seq_q + t) * Hi + i) * Di;
+        double smax = -INFINITY;
+        for (int32_t a = 0; a < n; ++a) {
+          const double* kv = ik + ((int64_t)b * p->seq_kv + tok[a]) * Di;
+          double s = 0.0;
+          for (int32_t d = 0; d < Di; ++d) s += iv[d] * kv[d];
+          Q[a] = s;
+          if (s > smax) smax = s;
+        }
+        double lq = 0.0;
+        for (int32_t a = 0; a < n; ++a) lq += exp(Q[a] - smax);
+        const double lse = smax + log(lq);
+        double kl = 0.0;
+        for (int32_t a = 0; a < n; ++a) {
+          const double logq = Q[a] - lse;
+          Q[a] = exp(logq);
+          if (P[a] > 0.0) kl += P[a] * (log(P[a]) - logq);
+        }
+        loss[((int64_t)b * p->seq_q + t) * Hi + i] = kl;
+        /* d loss / d score_j = Q_j - P_j, into both factors of the dot product */
+        double* dq_row = diq + (((int64_t)b * p->seq_q + t) * Hi + i) * Di;
+        for (int32_t a = 0; a < n; ++a) {
+          const double g = Q[a] - P[a];
+          const double* kv = ik + ((int64_t)b * p->seq_kv + tok[a]) * Di;
+          double* dk_row = dik + ((int64_t)b * p->seq_kv + tok[a]) * Di;
+          for (int32_t d = 0; d < Di; ++d) {
+            dq_row[d] += g * kv[d];
+            dk_row[d] += g * iv[d];
+          }
+        }
+      }
+    }
+  }
+  free(tok);
+  free(P);
+  free(w);
+  free(Q);
+  return rc;
+}

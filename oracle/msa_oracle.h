@@ -1,6 +1,7 @@
 /*
  * msa_oracle.h — plain, slow, single-threaded CPU oracle of the MiniMax Sparse
- * Attention (MSA) forward pass, and the gradient of its main branch.
+ * Attention (MSA) forward pass, the gradient of its main branch, and the
+ * index branch's KL training signal with its gradient.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
  * load or call this code: only the test suite, the smoke check and the CPU
@@ -128,6 +129,28 @@ int oracle_attend_row_f64(const oracle_problem* p, const double* q, const double
 int oracle_attend_backward(const oracle_problem* p, const double* q, const double* k,
                            const double* v, const double* dout, const int32_t* seq_lens,
                            const int32_t* sel_all, double* dq, double* dk, double* dv);
+
+/* Index-branch training signal ([A] section "MSA uses a lightweight index
+ * branch before sparse attention": the index branch is trained with a KL
+ * divergence to follow the main branch's attention).  The pages give neither
+ * the direction, the distributions compared nor any scale; this oracle reads
+ * them plainly.  For row (b, t) and index head i, whose KV head is
+ * h = i mod Hkv, over the tokens T that KV head attends (the selected blocks
+ * of sel_all, keys j <= pos; layout as for oracle_attend_backward):
+ *   P_j = (1/G) sum over the G query heads hq of h of
+ *         softmax_j(softmax_scale q_hq . k_j)   (the main branch, a target),
+ *   Q_j = softmax_j(iq_i . ik_j)                (raw index dot products, as
+ *                                                the selection uses them),
+ *   loss[b][t][i] = KL(P || Q) = sum_j P_j (log P_j - log Q_j).
+ * Gradients of the summed loss (double, overwritten):
+ *   diq [B][Sq][Hi][Di]: sum over j in T of (Q_j - P_j) ik_j;
+ *   dik [B][Skv][Di]:    sum over (t, i) attending j of (Q_j - P_j) iq_i
+ *                        (zero for keys nothing attends).
+ * q [B][Sq][Hq][D], k [B][Hkv][Skv][D], iq [B][Sq][Hi][Di], ik [B][Skv][Di]
+ * as double.  A row with no attended token contributes nothing. */
+int oracle_index_kl(const oracle_problem* p, const double* q, const double* k, const double* iq,
+                    const double* ik, const int32_t* seq_lens, const int32_t* sel_all,
+                    double* loss, double* diq, double* dik);
 
 #ifdef __cplusplus
 }

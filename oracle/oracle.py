@@ -101,8 +101,9 @@ def _bind(L):
     L.oracle_attend_row_f64.argtypes = [prob, f64, f64, f64, i32, i32, ctypes.c_int32,
                                         ctypes.c_int32, f64, f64]
     L.oracle_attend_backward.argtypes = [prob, f64, f64, f64, f64, i32, i32, f64, f64, f64]
+    L.oracle_index_kl.argtypes = [prob, f64, f64, f64, f64, i32, i32, f64, f64, f64]
     for name in ("oracle_block_scores_row", "oracle_select_row", "oracle_attend_row",
-                 "oracle_dense_row", "oracle_forward_rows", "oracle_attend_row_f64",
+                 "oracle_dense_row", "oracle_forward_rows", "oracle_attend_row_f64", "oracle_index_kl",
                  "oracle_attend_backward"):
         getattr(L, name).restype = ctypes.c_int
     return L
@@ -267,3 +268,25 @@ def attend_backward(p: Problem, q, k, v, dout, seq_lens, sel_all, L=None):
                                     _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double)),
            "attend_backward")
     return dq, dk, dv
+
+
+def index_kl(p: Problem, q, k, iq, ik, seq_lens, sel_all, L=None):
+    """The index branch's KL training signal (oracle_index_kl): loss
+    [B][Sq][Hi], diq [B][Sq][Hi][Di], dik [B][Skv][Di], all fp64, over the
+    selection sel_all [B][Sq][Hkv][top_k]; inputs fp64 (bf16 values as exact
+    doubles)."""
+    L = L or lib()
+    q, k, iq, ik = _f64(q), _f64(k), _f64(iq), _f64(ik)
+    s = np.ascontiguousarray(sel_all, dtype=np.int32)
+    assert s.shape == (p.batch, p.seq_q, p.n_kv_heads, p.top_k)
+    sl = None if seq_lens is None else np.ascontiguousarray(seq_lens, dtype=np.int32)
+    loss = np.empty((p.batch, p.seq_q, p.n_idx_heads), dtype=np.float64)
+    diq = np.empty((p.batch, p.seq_q, p.n_idx_heads, p.idx_head_dim), dtype=np.float64)
+    dik = np.empty((p.batch, p.seq_kv, p.idx_head_dim), dtype=np.float64)
+    _check(L.oracle_index_kl(ctypes.byref(p.c()), _ptr(q, ctypes.c_double),
+                             _ptr(k, ctypes.c_double), _ptr(iq, ctypes.c_double),
+                             _ptr(ik, ctypes.c_double), _ptr(sl, ctypes.c_int32),
+                             _ptr(s, ctypes.c_int32), _ptr(loss, ctypes.c_double),
+                             _ptr(diq, ctypes.c_double), _ptr(dik, ctypes.c_double)),
+           "index_kl")
+    return loss, diq, dik

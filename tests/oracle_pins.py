@@ -28,7 +28,12 @@ What pins what:
   * gradient          -> central differences of the fp64 forward, torch
                          autograd of dense causal attention (all blocks kept),
                          and the sum rules over keys (sum of dk = 0, sum of
-                         dv = sum of dout over the rows reading the head).
+                         dv = sum of dout over the rows reading the head);
+  * index KL          -> central differences of the loss, torch autograd of
+                         the definition written with library softmaxes, zero
+                         loss and gradient when the distributions agree (and
+                         at one attended token), the key sum rule and the
+                         invariance of the loss under a shift of every key.
 """
 from __future__ import annotations
 
@@ -470,6 +475,117 @@ def check_backward_invariants(L):
         assert not np.any(a), "zero cotangent, nonzero gradient"
 
 
+# ----------------------------------------------------------------- index KL
+def _kl_inputs(p, rng):
+    q = rng.standard_normal((p.batch, p.seq_q, p.n_q_heads, p.head_dim))
+    k = rng.standard_normal((p.batch, p.n_kv_heads, p.seq_kv, p.head_dim))
+    iq = rng.standard_normal((p.batch, p.seq_q, p.n_idx_heads, p.idx_head_dim))
+    ik = rng.standard_normal((p.batch, p.seq_kv, p.idx_head_dim))
+    return q, k, iq, ik
+
+
+def check_index_kl_finite_differences(L):
+    """Gradients of the summed KL loss against central differences of the
+    loss itself, on sampled coordinates of iq and ik (two index heads per KV
+    head, a ragged last block, two sequences, random selections)."""
+    p = problem(B=2, Sq=11, Skv=13, q_start=2, Hq=4, Hkv=2, D=8, Hi=4, Di=6, bs=4, k=2)
+    rng = np.random.default_rng(31)
+    q, k, iq, ik = _kl_inputs(p, rng)
+    sel = _random_selection(p, rng)
+    loss, diq, dik = O.index_kl(p, q, k, iq, ik, None, sel, L=L)
+    h = 1e-6
+    for name, x, gx in (("iq", iq, diq), ("ik", ik, dik)):
+        for _ in range(16):
+            idx = tuple(int(rng.integers(0, n)) for n in x.shape)
+            x0 = x[idx]
+            x[idx] = x0 + h
+            lp = O.index_kl(p, q, k, iq, ik, None, sel, L=L)[0].sum()
+            x[idx] = x0 - h
+            lm = O.index_kl(p, q, k, iq, ik, None, sel, L=L)[0].sum()
+            x[idx] = x0
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - gx[idx]) <= 1e-6 * (1.0 + abs(fd)), \
+                f"d{name}{idx}: analytic {gx[idx]:.9e} vs central difference {fd:.9e}"
+
+
+def check_index_kl_vs_autograd(L):
+    """The loss and both gradients against the definition written with torch
+    operations in float64 (masked softmaxes over the attended tokens, the
+    group-averaged main-branch distribution as a constant target, KL through
+    log_softmax) and differentiated by torch autograd."""
+    p = problem(B=1, Sq=14, Skv=18, q_start=4, Hq=6, Hkv=2, D=8, Hi=4, Di=5, bs=4, k=2)
+    rng = np.random.default_rng(32)
+    q, k, iq, ik = _kl_inputs(p, rng)
+    sel = _random_selection(p, rng)
+    loss, diq, dik = O.index_kl(p, q, k, iq, ik, None, sel, L=L)
+    G = p.n_q_heads // p.n_kv_heads
+    tiq = torch.tensor(iq).requires_grad_()
+    tik = torch.tensor(ik).requires_grad_()
+    total = torch.zeros((), dtype=torch.float64)
+    want_loss = np.zeros_like(loss)
+    for t in range(p.seq_q):
+        pos = p.q_start + t
+        for i in range(p.n_idx_heads):
+            h = i % p.n_kv_heads
+            allowed = torch.zeros(p.seq_kv, dtype=torch.bool)
+            for c in sel[0, t, h]:
+                if c >= 0:
+                    allowed[c * p.block_size: min((c + 1) * p.block_size, pos + 1)] = True
+            z = torch.tensor(q[0, t, h * G:(h + 1) * G]) @ torch.tensor(k[0, h]).T  # [G][Skv]
+            z = (z * p.softmax_scale).masked_fill(~allowed, float("-inf"))
+            P = torch.softmax(z, dim=-1).mean(dim=0)
+            s = (tik[0] @ tiq[0, t, i]).masked_fill(~allowed, float("-inf"))
+            logq = torch.log_softmax(s, dim=-1)
+            m = allowed & (P > 0)
+            kl = (P[m] * (torch.log(P[m]) - logq[m])).sum()
+            want_loss[0, t, i] = kl.item()
+            total = total + kl
+    total.backward()
+    close(loss, want_loss, 1e-12, "kl loss")
+    close(diq, tiq.grad.numpy(), 1e-12, "kl diq")
+    close(dik, tik.grad.numpy(), 1e-12, "kl dik")
+
+
+def check_index_kl_zero_when_distributions_agree(L):
+    """When the index scores are exactly the main branch's scaled scores and
+    the group's query heads agree, Q == P: the loss and every gradient vanish
+    (up to rounding).  Rows at position 0 (one attended token) have Q == P == 1
+    whatever the inputs."""
+    p = problem(B=1, Sq=12, Skv=12, Hq=4, Hkv=2, D=8, Hi=2, Di=8, bs=4, k=2)
+    rng = np.random.default_rng(33)
+    G = p.n_q_heads // p.n_kv_heads
+    iq = rng.standard_normal((p.batch, p.seq_q, p.n_idx_heads, p.idx_head_dim))
+    ik = rng.standard_normal((p.batch, p.seq_kv, p.idx_head_dim))
+    q = np.repeat(iq, G, axis=2) / p.softmax_scale  # head hq = h G + g reads index head h
+    k = np.repeat(ik[:, None], p.n_kv_heads, axis=1)
+    sel = _random_selection(p, rng)
+    loss, diq, dik = O.index_kl(p, q, k, iq, ik, None, sel, L=L)
+    close(loss, np.zeros_like(loss), 1e-12, "agreeing loss")
+    close(diq, np.zeros_like(diq), 1e-10, "agreeing diq")
+    close(dik, np.zeros_like(dik), 1e-10, "agreeing dik")
+    # position 0: a single attended token
+    q2, k2, iq2, ik2 = _kl_inputs(p, rng)
+    loss2, diq2, _ = O.index_kl(p, q2, k2, iq2, ik2, None, sel, L=L)
+    close(loss2[0, 0], np.zeros(p.n_idx_heads), 1e-14, "single-token loss")
+    close(diq2[0, 0], np.zeros((p.n_idx_heads, p.idx_head_dim)), 1e-14, "single-token diq")
+    assert np.all(loss2 >= -1e-12) and loss2[0, 5:].max() > 1e-3, "KL must be >= 0 and not all 0"
+
+
+def check_index_kl_invariants(L):
+    """Q - P sums to zero over a row's tokens: the key gradient summed over all
+    keys vanishes, and shifting every index key by one vector (every score of a
+    row moves by the same amount) leaves the loss unchanged."""
+    p = problem(B=2, Sq=20, Skv=25, q_start=5, Hq=8, Hkv=2, D=8, Hi=4, Di=6, bs=4, k=3)
+    rng = np.random.default_rng(34)
+    q, k, iq, ik = _kl_inputs(p, rng)
+    sel = _random_selection(p, rng)
+    loss, diq, dik = O.index_kl(p, q, k, iq, ik, None, sel, L=L)
+    close(dik.sum(axis=1), np.zeros((p.batch, p.idx_head_dim)), 1e-10, "sum of dik")
+    shift = rng.standard_normal(p.idx_head_dim)
+    loss_s = O.index_kl(p, q, k, iq, ik + shift, None, sel, L=L)[0]
+    close(loss_s, loss, 1e-10, "shifted index keys")
+
+
 # ----------------------------------------------------------------- token level
 def check_token_level_block_size_one(L):
     """Block size 1 (token-level selection, the ablation the pages contrast
@@ -523,4 +639,6 @@ ALL_CHECKS = [check_dense_vs_library, check_attend_vs_masked_library,
               check_planted_winners_per_kv_head, check_select_brute_force,
               check_select_edge_cases, check_golden_hand_example,
               check_backward_finite_differences, check_backward_dense_vs_autograd,
-              check_backward_invariants, check_token_level_block_size_one]
+              check_backward_invariants, check_token_level_block_size_one,
+              check_index_kl_finite_differences, check_index_kl_vs_autograd,
+              check_index_kl_zero_when_distributions_agree, check_index_kl_invariants]

@@ -61,6 +61,18 @@ MUTANTS = [
     ("bwd_tokens_not_causal", "for (int32_t j = c * bs; j <= pos && j < (c + 1) * bs; ++j) tok[n++] = j;",
      "for (int32_t j = c * bs; j < (c + 1) * bs && j < p->seq_kv; ++j) tok[n++] = j;"),
     ("f64_forward_unscaled", "z[a] = s * p->softmax_scale;", "z[a] = s;"),
+    # the index branch's KL signal
+    ("kl_target_not_averaged", "P[a] += w[a] / l / G;", "P[a] += w[a] / l;"),
+    ("kl_gradient_sign", "const double g = Q[a] - P[a];", "const double g = P[a] - Q[a];"),
+    ("kl_index_scaled", "Q[a] = s;\n          if (s > smax) smax = s;",
+     "Q[a] = p->softmax_scale * s;\n          if (p->softmax_scale * s > smax) smax = p->softmax_scale * s;"),
+    ("kl_diq_reads_iq", "dq_row[d] += g * kv[d];", "dq_row[d] += g * iv[d];"),
+    ("kl_dik_reads_ik", "dk_row[d] += g * iv[d];", "dk_row[d] += g * kv[d];"),
+    ("kl_head_attribution", "const int32_t h = i % Hkv;", "const int32_t h = i / (Hi / Hkv);"),
+    ("kl_target_unscaled", "            w[a] = p->softmax_scale * s;", "            w[a] = s;"),
+    ("kl_lse_missing_max", "const double lse = smax + log(lq);", "const double lse = log(lq);"),
+    ("kl_reversed_direction", "if (P[a] > 0.0) kl += P[a] * (log(P[a]) - logq);",
+     "if (P[a] > 0.0) kl += Q[a] * (logq - log(P[a]));"),
 ]
 
 
