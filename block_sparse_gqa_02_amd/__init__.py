@@ -10,7 +10,8 @@ from .binding import (Problem, MsaError, abi_version, decode_workspace,  # noqa:
                       msa_dense_attn_decode,
                       msa_dense_attn_prefill, msa_index_block_scores,
                       msa_index_block_scores_paged, msa_index_topk_fused,
-                      msa_index_topk_fused_paged, msa_sparse_attn_decode,
+                      msa_index_kl_backward, msa_index_topk_fused_paged,
+                      msa_sparse_attn_decode,
                       msa_sparse_attn_prefill_backward,
                       msa_sparse_attn_decode_paged, msa_sparse_attn_prefill, msa_topk_blocks,
                       msa_sparse_attn_prefill_status_offset, msa_set_wait_limit,

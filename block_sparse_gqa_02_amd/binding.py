@@ -23,7 +23,8 @@ STATUS = {0: "MSA_OK", 1: "MSA_ERR_INVALID_ARGUMENT", 2: "MSA_ERR_UNSUPPORTED",
           3: "MSA_ERR_WORKSPACE_TOO_SMALL", 4: "MSA_ERR_HIP"}
 OPS = {"index_block_scores": 0, "topk_blocks": 1, "index_topk_fused": 2,
        "sparse_attn_prefill": 3, "sparse_attn_decode": 4, "dense_attn_prefill": 5,
-       "dense_attn_decode": 6, "sparse_attn_prefill_backward": 7, "index_topk_fused_decode": 8}
+       "dense_attn_decode": 6, "sparse_attn_prefill_backward": 7, "index_topk_fused_decode": 8,
+       "index_kl_backward": 9}
 
 
 class MsaError(RuntimeError):
@@ -97,6 +98,7 @@ def lib():
                                              vp, sz, vp],
             "msa_sparse_attn_prefill_backward": [pr, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                  sz, vp],
+            "msa_index_kl_backward": [pr, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "msa_sparse_attn_prefill_status_offset": [pr, P(sz)],
             "msa_index_topk_fused_paged": [pr, vp, vp, vp, ctypes.c_int32, vp, vp, vp, sz, vp],
             "msa_sparse_attn_decode_static": [pr, vp, vp, vp, vp, vp, vp, vp, vp],
@@ -246,6 +248,27 @@ def msa_sparse_attn_prefill_backward(p: Problem, q, k, v, sel, out, lse, dout, d
         _ptr(lse, torch.float32), _ptr(dout, torch.bfloat16), _ptr(dq, torch.float32),
         _ptr(dk, torch.float32), _ptr(dv, torch.float32), _ptr(ws), nbytes, _stream(stream)))
     return dq, dk, dv
+
+
+def msa_index_kl_backward(p: Problem, q, k, iq, ik, sel, lse, loss=None, diq=None, dik=None,
+                          workspace=None, stream=None):
+    """The index branch's KL loss (loss [B][Sq][4]) and its gradients (diq
+    [B][Sq][4][64], dik [B][Skv][64]), fp32, over the selection sel, with the
+    main branch's weights taken from msa_sparse_attn_prefill's lse."""
+    f32 = dict(dtype=torch.float32, device=q.device)
+    if loss is None:
+        loss = torch.empty(iq.shape[:3], **f32)
+    if diq is None:
+        diq = torch.empty(iq.shape, **f32)
+    if dik is None:
+        dik = torch.empty(ik.shape, **f32)
+    ws, nbytes = _workspace(p, "index_kl_backward", workspace, q.device)
+    _check(lib().msa_index_kl_backward(
+        ctypes.byref(p.c()), _ptr(q, torch.bfloat16), _ptr(k, torch.bfloat16),
+        _ptr(iq, torch.bfloat16), _ptr(ik, torch.bfloat16), _ptr(sel, torch.int32),
+        _ptr(lse, torch.float32), _ptr(loss, torch.float32), _ptr(diq, torch.float32),
+        _ptr(dik, torch.float32), _ptr(ws), nbytes, _stream(stream)))
+    return loss, diq, dik
 
 
 def msa_sparse_attn_decode(p: Problem, q, k_cache, v_cache, seq_lens, sel, out=None, lse=None,

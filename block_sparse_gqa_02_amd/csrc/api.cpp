@@ -121,6 +121,19 @@ msa_status check_backward(const msa::Shape& s) {
   return MSA_OK;
 }
 
+// Index-KL-specific limits on top of check_problem and check_backward.
+msa_status check_index_kl(const msa::Shape& s) {
+  msa_status st = check_backward(s);
+  if (st != MSA_OK) return st;
+  if (!msa::index_kl_supported(s))
+    return fail(MSA_ERR_UNSUPPORTED,
+                "index KL gradient needs n_q_heads / n_kv_heads in {4, 8, 16} and at most 8 "
+                "(row, index head) pairs per 16 query columns: (16 / G) * (4 / n_kv_heads) <= 8");
+  if ((size_t)3 * 1024 * 16 + (size_t)s.nblk * 4 > 160 * 1024)
+    return fail(MSA_ERR_UNSUPPORTED, "index KL gradient needs seq_kv <= 1310720");
+  return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -397,6 +410,33 @@ msa_status msa_sparse_attn_prefill_backward(const msa_problem* p, const void* q,
                   "msa_sparse_attn_prefill_backward");
 }
 
+msa_status msa_index_kl_backward(const msa_problem* p, const void* q, const void* k,
+                                 const void* iq, const void* ik, const int32_t* sel,
+                                 const float* lse, float* loss, float* diq, float* dik,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  msa::Shape s;
+  msa_status st = check_problem(p, Mode::kPrefill, true, &s);
+  if (st != MSA_OK) return st;
+  st = check_index_kl(s);
+  if (st != MSA_OK) return st;
+  NEED_PTR(q);
+  NEED_PTR(k);
+  NEED_PTR(iq);
+  NEED_PTR(ik);
+  NEED_PTR4(sel);
+  NEED_PTR4(lse);
+  NEED_PTR4(loss);
+  NEED_PTR(diq);
+  NEED_PTR(dik);
+  NEED_PTR(workspace);
+  const size_t need = msa::index_kl_workspace_bytes(s);
+  if (workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  return launched(msa::launch_index_kl_backward(s, q, k, iq, ik, sel, lse, loss, diq, dik,
+                                                workspace, stream),
+                  "msa_index_kl_backward");
+}
+
 msa_status msa_sparse_attn_prefill_status_offset(const msa_problem* p, size_t* offset) {
   if (!offset) return fail(MSA_ERR_INVALID_ARGUMENT, "offset is NULL");
   msa::Shape s;
@@ -439,6 +479,13 @@ msa_status msa_workspace_bytes(const msa_problem* p, msa_op op, size_t* bytes) {
       st = check_backward(s);
       if (st != MSA_OK) return st;
       *bytes = msa::sparse_bwd_workspace_bytes(s);
+      return ok();
+    case MSA_OP_INDEX_KL_BACKWARD:
+      st = check_problem(p, Mode::kPrefill, true, &s);
+      if (st != MSA_OK) return st;
+      st = check_index_kl(s);
+      if (st != MSA_OK) return st;
+      *bytes = msa::index_kl_workspace_bytes(s);
       return ok();
     case MSA_OP_INDEX_TOPK_FUSED_DECODE:
       st = check_problem(p, Mode::kDecode, true, &s);

@@ -33,13 +33,13 @@
 // Score-side operand layouts follow attn_block.h; the products with a transposed
 // tile (dQ^T += K^T dS^T, dV^T += dO^T P, dK^T += Q^T dS) use pv_tr below.
 #include "attn_block.h"
+#include "bwd_tiles.h"
 #include "common.h"
 #include "kernels.h"
 
 namespace msa {
 namespace {
 
-constexpr float kLog2eB = 1.4426950408889634f;
 constexpr int kBatchRows = 64;  // rows per inverse-list batch (one bit each)
 
 struct BwdArgs {
@@ -65,18 +65,6 @@ __device__ __forceinline__ float wave_sum64(float v) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
   return v;
-}
-
-// LDS tiles of the tiled gradient kernels: 64 rows x 128 bf16, chunk c (16
-// bytes) of row r at chunk c ^ (r & 15), so the 16 rows of a 16-byte operand
-// read (one chunk column) hit 16 distinct chunks.
-__device__ __forceinline__ int swz_slot(int row, int ch) { return row * 16 + (ch ^ (row & 15)); }
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
-
-__device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
 // acc += T^T P^T over one tile T (swz_slot layout; its 64 rows are the
@@ -288,14 +276,6 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdArgs a) {
   }
   if (col_ok) store_tr_f32(acc, a.dq + (((long long)b * a.Sq + t) * a.Hq + hq0 + n) * kHeadDim,
                            a.scale);
-}
-
-// s_waitcnt vmcnt(0) with a compiler fence: the LDS-bound loads of the
-// staged columns are complete (for this wave) before anything below.
-__device__ __forceinline__ void wait_all_loads() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xf70);  // vmcnt 0; expcnt, lgkmcnt unconstrained
-  asm volatile("" ::: "memory");
 }
 
 // dK and dV of one block: work-group per (block, KV head, sequence), wave w
@@ -572,38 +552,46 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
 
 }  // namespace
 
-size_t sparse_bwd_workspace_bytes(const Shape& s) {
+namespace {
+char* align256(char* p) { return reinterpret_cast<char*>(((uintptr_t)p + 255) & ~(uintptr_t)255); }
+}  // namespace
+
+size_t inverse_lists_bytes(const Shape& s) {
   const size_t nbatch = (size_t)ceil_div(s.Sq, kBatchRows);
   size_t bytes = 0;
-  bytes += (size_t)s.B * s.Hq * s.Sq * 4;                   // dsum
   bytes += (size_t)s.B * s.Hkv * nbatch * s.nblk * 4;       // batch counts / offsets
   bytes += ((size_t)s.B * s.Hkv * s.nblk + 1) * 4;          // list starts
   bytes += (size_t)s.B * s.Hkv * s.Sq * s.top_k * 4;        // row lists
-  return bytes + 4 * 256;                                    // alignment slack
+  return bytes + 3 * 256;                                    // alignment slack
 }
 
-hipError_t launch_sparse_attn_backward(const Shape& s, const void* q, const void* k, const void* v,
-                                       const int32_t* sel, const void* out, const float* lse,
-                                       const void* dout, float* dq, float* dk, float* dv, void* ws,
-                                       hipStream_t st) {
-  if (s.G > 64 || 64 % s.G != 0) return hipErrorInvalidValue;
+hipError_t launch_inverse_lists(const Shape& s, const int32_t* sel, void* ws,
+                                const int32_t** base_out, const int32_t** lists_out,
+                                hipStream_t st) {
   const int nbatch = ceil_div(s.Sq, kBatchRows);
   const size_t bm_bytes = (size_t)s.nblk * 8;
   if (bm_bytes > 160 * 1024) return hipErrorInvalidValue;
-  auto align = [](char* p) { return reinterpret_cast<char*>(((uintptr_t)p + 255) & ~(uintptr_t)255); };
-  char* p = align(static_cast<char*>(ws));
-  float* dsum = reinterpret_cast<float*>(p);
-  p = align(p + (size_t)s.B * s.Hq * s.Sq * 4);
+  char* p = align256(static_cast<char*>(ws));
   int32_t* bcnt = reinterpret_cast<int32_t*>(p);
-  p = align(p + (size_t)s.B * s.Hkv * nbatch * s.nblk * 4);
+  p = align256(p + (size_t)s.B * s.Hkv * nbatch * s.nblk * 4);
   int32_t* base = reinterpret_cast<int32_t*>(p);
-  p = align(p + ((size_t)s.B * s.Hkv * s.nblk + 1) * 4);
+  p = align256(p + ((size_t)s.B * s.Hkv * s.nblk + 1) * 4);
   int32_t* lists = reinterpret_cast<int32_t*>(p);
-  BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-            static_cast<const uint16_t*>(v), sel, static_cast<const uint16_t*>(out), lse,
-            static_cast<const uint16_t*>(dout), dq, dk, dv, dsum, bcnt, base, lists,
-            s.B, s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.G, s.top_k, s.nblk, nbatch,
-            s.scale, s.scale * kLog2eB};
+  BwdArgs a{};
+  a.sel = sel;
+  a.bcnt = bcnt;
+  a.base = base;
+  a.lists = lists;
+  a.B = s.B;
+  a.Sq = s.Sq;
+  a.Skv = s.Skv;
+  a.q_start = s.q_start;
+  a.Hq = s.Hq;
+  a.Hkv = s.Hkv;
+  a.G = s.G;
+  a.top_k = s.top_k;
+  a.nblk = s.nblk;
+  a.nbatch = nbatch;
   hipError_t e;
   if (bm_bytes > 64 * 1024) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&inverse_kernel<false>),
@@ -613,12 +601,40 @@ hipError_t launch_sparse_attn_backward(const Shape& s, const void* q, const void
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bm_bytes);
     if (e != hipSuccess) return e;
   }
-  const long long nrows = (long long)s.B * s.Sq * s.Hq;
-  dsum_kernel<<<(unsigned)((nrows + 3) / 4), 256, 0, st>>>(a);
   inverse_kernel<false><<<dim3(nbatch, s.Hkv, s.B), 256, bm_bytes, st>>>(a);
   batch_scan_kernel<<<dim3(ceil_div(s.nblk, 256), s.B * s.Hkv), 256, 0, st>>>(a);
   base_scan_kernel<<<1, 256, 0, st>>>(a);
   inverse_kernel<true><<<dim3(nbatch, s.Hkv, s.B), 256, bm_bytes, st>>>(a);
+  *base_out = base;
+  *lists_out = lists;
+  return hipGetLastError();
+}
+
+size_t sparse_bwd_workspace_bytes(const Shape& s) {
+  return (size_t)s.B * s.Hq * s.Sq * 4 + 256 + inverse_lists_bytes(s);  // dsum, then the lists
+}
+
+hipError_t launch_sparse_attn_backward(const Shape& s, const void* q, const void* k, const void* v,
+                                       const int32_t* sel, const void* out, const float* lse,
+                                       const void* dout, float* dq, float* dk, float* dv, void* ws,
+                                       hipStream_t st) {
+  if (s.G > 64 || 64 % s.G != 0) return hipErrorInvalidValue;
+  char* p = align256(static_cast<char*>(ws));
+  float* dsum = reinterpret_cast<float*>(p);
+  p += (size_t)s.B * s.Hq * s.Sq * 4;
+  const int32_t* base = nullptr;
+  const int32_t* lists = nullptr;
+  BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+            static_cast<const uint16_t*>(v), sel, static_cast<const uint16_t*>(out), lse,
+            static_cast<const uint16_t*>(dout), dq, dk, dv, dsum, nullptr, nullptr, nullptr,
+            s.B, s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.G, s.top_k, s.nblk,
+            ceil_div(s.Sq, kBatchRows), s.scale, s.scale * kLog2eB};
+  const long long nrows = (long long)s.B * s.Sq * s.Hq;
+  dsum_kernel<<<(unsigned)((nrows + 3) / 4), 256, 0, st>>>(a);
+  hipError_t e = launch_inverse_lists(s, sel, p, &base, &lists, st);
+  if (e != hipSuccess) return e;
+  a.base = const_cast<int32_t*>(base);
+  a.lists = const_cast<int32_t*>(lists);
   if (s.G == 4 || s.G == 8) {
     const size_t dq_lds = (size_t)4 * kBlock * 16 * 16 + (size_t)s.nblk * 4;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dq_tile_kernel),

@@ -1,0 +1,37 @@
+// bwd_tiles.h — LDS tile helpers shared by the gradient kernels (main branch
+// and index branch): the 256-byte-row tile swizzle, transposed LDS reads, and
+// the load wait that orders LDS-bound global loads.
+#pragma once
+
+#include "common.h"
+
+namespace msa {
+
+constexpr float kLog2eB = 1.4426950408889634f;
+
+// LDS tiles of 64 rows x 128 bf16: chunk c (16 bytes) of row r at chunk
+// c ^ (r & 15), so the 16 rows of a 16-byte operand read (one chunk column)
+// hit 16 distinct chunks.
+__device__ __forceinline__ int swz_slot(int row, int ch) { return row * 16 + (ch ^ (row & 15)); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+__device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// ds_read_b64_tr_b16 at LDS byte address `addr`.
+__device__ __forceinline__ s16x4 lds_read_tr(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)addr);
+}
+
+// s_waitcnt vmcnt(0) with a compiler fence: the LDS-bound loads of the
+// staged columns are complete (for this wave) before anything below.
+__device__ __forceinline__ void wait_all_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xf70);  // vmcnt 0; expcnt, lgkmcnt unconstrained
+  asm volatile("" ::: "memory");
+}
+
+}  // namespace msa

@@ -64,6 +64,22 @@ hipError_t launch_sparse_attn_backward(const Shape& s, const void* q, const void
                                        const int32_t* sel, const void* out, const float* lse,
                                        const void* dout, float* dq, float* dk, float* dv, void* ws,
                                        hipStream_t st);
+// The rows that selected each (sequence, KV head, block), ascending, built
+// from sel [B][Hkv][Sq][top_k] in ws (inverse_lists_bytes(s) bytes): list
+// starts base[(b * Hkv + h) * nblk + c] (then the total) into lists.
+size_t inverse_lists_bytes(const Shape& s);
+hipError_t launch_inverse_lists(const Shape& s, const int32_t* sel, void* ws,
+                                const int32_t** base, const int32_t** lists, hipStream_t st);
+
+// Index-branch KL gradient (prefill): loss [B][Sq][4], diq [B][Sq][4][64],
+// dik [B][Skv][64] in fp32 from q, k, iq, ik (bf16), the selection and the
+// forward's log-sum-exp ([B][Hq][Sq]).
+bool index_kl_supported(const Shape& s);
+size_t index_kl_workspace_bytes(const Shape& s);
+hipError_t launch_index_kl_backward(const Shape& s, const void* q, const void* k, const void* iq,
+                                    const void* ik, const int32_t* sel, const float* lse,
+                                    float* loss, float* diq, float* dik, void* ws,
+                                    hipStream_t st);
 hipError_t launch_index_topk_fused(const Shape& s, const void* iq, const void* ik, int32_t* sel,
                                    void* ws, hipStream_t st);
 

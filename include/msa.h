@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define MSA_ABI_VERSION 5
+#define MSA_ABI_VERSION 6
 
 typedef enum {
   MSA_OK = 0,
@@ -120,7 +120,8 @@ typedef enum {
   MSA_OP_DENSE_ATTN_PREFILL = 5,
   MSA_OP_DENSE_ATTN_DECODE = 6,
   MSA_OP_SPARSE_ATTN_PREFILL_BACKWARD = 7,
-  MSA_OP_INDEX_TOPK_FUSED_DECODE = 8   /* msa_index_topk_fused / _paged with seq_lens */
+  MSA_OP_INDEX_TOPK_FUSED_DECODE = 8,  /* msa_index_topk_fused / _paged with seq_lens */
+  MSA_OP_INDEX_KL_BACKWARD = 9
 } msa_op;
 
 /* Index branch: block scores.  For every sequence b, KV head h, row t and
@@ -310,6 +311,35 @@ msa_status msa_sparse_attn_prefill_backward(const msa_problem* p, const void* q,
                                             const float* lse, const void* dout, float* dq,
                                             float* dk, float* dv, void* workspace,
                                             size_t workspace_bytes, hipStream_t stream);
+
+/* Index-branch training signal and its gradient, prefill (talk summary "How
+ * MiniMax M3 Was Built", section "MSA uses a lightweight index branch before
+ * sparse attention": the index branch is trained with a KL divergence to
+ * follow the main branch's attention; the pages give no formula, and this is
+ * the plain reading).  For row t and index head i, with KV head h = i mod Hkv,
+ * over the tokens T that h attends in sel (its selected blocks, keys j <= pos):
+ *   P_j = mean over the G query heads hq of h of exp(softmax_scale q_hq.k_j
+ *         - lse[hq][t])   (the main branch's weights; a target, no gradient),
+ *   Q_j = softmax over T of s_j = iq_i . ik_j   (raw index dot products),
+ *   loss[b][t][i] = KL(P || Q) = sum_j P_j (log P_j - log Q_j),
+ *   diq[b][t][i][:] = sum_j (Q_j - P_j) ik_j,
+ *   dik[b][j][:] = sum over (t, i) attending j of (Q_j - P_j) iq_i
+ * (the gradients of the summed loss; zero for keys nothing attends; a row
+ * that attends nothing gets loss 0 and diq 0).
+ * Inputs (device): q [B][Sq][Hq][128], k [B][Hkv][Skv][128], iq [B][Sq][4][64],
+ * ik [B][Skv][64] bf16; sel [B][Hkv][Sq][top_k] as for msa_sparse_attn_prefill,
+ * each block at most once per list; lse (fp32, [B][Hq][Sq], natural log) as
+ * msa_sparse_attn_prefill returned it for this selection.  Outputs (device,
+ * fp32, fully overwritten): loss [B][Sq][4], diq [B][Sq][4][64], dik
+ * [B][Skv][64].  Hq / Hkv must be 4, 8 or 16 with (16 / G) (4 / Hkv) <= 8;
+ * seq_kv at most 1310720.  workspace: msa_workspace_bytes(p,
+ * MSA_OP_INDEX_KL_BACKWARD) bytes, any contents.  bf16 products (P, the index
+ * softmax numerators and Q - P rounded to bf16), fp32 accumulation and
+ * softmax statistics; deterministic (no floating-point atomics). */
+msa_status msa_index_kl_backward(const msa_problem* p, const void* q, const void* k,
+                                 const void* iq, const void* ik, const int32_t* sel,
+                                 const float* lse, float* loss, float* diq, float* dik,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Byte offset, inside the workspace of msa_sparse_attn_prefill for problem p,
  * of the int32 status word described there (0: complete; 1: a bounded wait

@@ -30,7 +30,8 @@ def test_header_declares_entry_points():
               "msa_sparse_attn_prefill", "msa_sparse_attn_decode", "msa_dense_attn_prefill",
               "msa_dense_attn_decode", "msa_workspace_bytes", "msa_status_string",
               "msa_last_error", "msa_abi_version", "msa_index_block_scores_paged",
-              "msa_sparse_attn_decode_paged", "msa_sparse_attn_prefill_backward"]:
+              "msa_sparse_attn_decode_paged", "msa_sparse_attn_prefill_backward",
+              "msa_index_kl_backward"]:
         assert n in names
 
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = binding.lib()
-    assert L.msa_abi_version() == 5
+    assert L.msa_abi_version() == 6
     for code, name in binding.STATUS.items():
         assert L.msa_status_string(code).decode() == name
 
@@ -261,6 +262,47 @@ def test_token_level_rules():
     # pointers are still checked
     assert call("msa_topk_blocks", P(p), NULL, NULL, A4, NULL)[0] == 1
     assert call("msa_sparse_attn_prefill", P(p), A, A, A, NULL, A, NULL, NULL, 0, NULL)[0] == 1
+
+
+def test_index_kl_rules():
+    """Host-side checks of the index KL gradient entry: workspace size, missing
+    or misaligned pointers, the supported group sizes and index-head spreads,
+    caches too long for the LDS block mask, rows past the cache."""
+    p = prob()
+    need = ctypes.c_size_t()
+    assert call("msa_workspace_bytes", P(p), 9, ctypes.byref(need))[0] == 0
+    # the index log-sum-exp (B * 4 * Sq fp32) plus the inverse row lists
+    assert need.value >= 4 * 4 * 131072 + 4 * 131072 * 64 * 4
+    args = [A, A, A, A, A4, A4, A4, A, A]
+    st, msg = call("msa_index_kl_backward", P(p), *args, A, need.value - 1, NULL)
+    assert st == 3, msg
+    st, msg = call("msa_index_kl_backward", P(p), *args, NULL, need.value, NULL)
+    assert st == 1, msg
+    for i in range(len(args)):
+        a = list(args)
+        a[i] = NULL
+        assert call("msa_index_kl_backward", P(p), *a, A, need.value, NULL)[0] == 1, i
+    # diq must be 16-byte aligned (vector stores)
+    a = list(args)
+    a[7] = A4
+    assert call("msa_index_kl_backward", P(p), *a, A, need.value, NULL)[0] == 1
+    # G = 2 (8 query heads over 4 KV heads) is not implemented
+    st, msg = call("msa_index_kl_backward", P(prob(n_q_heads=8)), *args, A, 1 << 40, NULL)
+    assert st == 2 and "index KL" in msg, msg
+    # G = 4 with one KV head: 4 rows x 4 index heads per 16 columns is too many
+    st, msg = call("msa_index_kl_backward", P(prob(n_q_heads=4, n_kv_heads=1)), *args, A,
+                   1 << 40, NULL)
+    assert st == 2 and "index KL" in msg, msg
+    # ... while G = 4 over 2 KV heads, and G = 16, are accepted
+    assert call("msa_workspace_bytes", P(prob(n_q_heads=8, n_kv_heads=2)), 9,
+                ctypes.byref(need))[0] == 0
+    assert call("msa_workspace_bytes", P(prob(n_q_heads=16, n_kv_heads=1)), 9,
+                ctypes.byref(need))[0] == 0
+    # the block mask of 2M cached tokens does not fit LDS
+    big = prob(CHUNK_1M, seq_kv=2 * 1048576)
+    assert call("msa_workspace_bytes", P(big), 9, ctypes.byref(need))[0] == 2
+    # rows past the cache; decode positions are not accepted
+    assert call("msa_workspace_bytes", P(prob(q_start=1)), 9, ctypes.byref(need))[0] == 1
 
 
 def test_binding_raises_with_detail():
