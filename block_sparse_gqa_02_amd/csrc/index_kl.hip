@@ -20,17 +20,20 @@
 //   kl_row_kernel  a work-group per 16 rows of one (sequence, KV head) walks the
 //                  union of the rows' selected blocks, each block's K and index
 //                  K fetched once into double-buffered LDS tiles.  A row group
-//                  (16 / G rows) owns 16 main-branch columns (row, query head)
-//                  and 16 index columns: column q < 8 is (row q / nih, index
-//                  head q % nih) of the group (nih = index heads per KV head),
-//                  and column q + 8 repeats it.  Per block: S^T = K Q^T gives
-//                  P per head, summed over the row's heads; the index scores of
-//                  the columns; an online log-sum-exp of the index scores; and
-//                  one product over the block's index-key rows whose first 8
-//                  columns weigh them by e^{s - m} (U, rescaled as m grows) and
-//                  whose last 8 by P (V), so that diq = U / l - V comes out of
-//                  one sweep.  The loss is gathered from sum P log P, sum P s
-//                  and sum P.  Writes loss, diq and the index log-sum-exp.
+//                  (16 / G rows) owns 16 main-branch columns (row, query head),
+//                  each row a segment of G lanes, and 16 index columns laid in
+//                  the same segments: lane e < nih of a row's segment is (row,
+//                  index head e) (nih = index heads per KV head), lane
+//                  nih <= e < 2 nih repeats (row, e - nih).  Per block: S^T =
+//                  K Q^T gives P per head, summed over the row's segment (DPP
+//                  lane swaps, so every lane of the row holds its P); the index
+//                  scores of the columns; an online log-sum-exp of the index
+//                  scores; and one product over the block's index-key rows
+//                  whose first copy of each column weighs them by e^{s - m}
+//                  (U, rescaled as m grows) and whose second by P (V), so that
+//                  diq = U / l - V comes out of one sweep.  The loss is
+//                  gathered from sum P log P, sum P s and sum P.  Writes loss,
+//                  diq and the index log-sum-exp.
 //   kl_key_kernel  a work-group per (block, sequence); wave w owns keys
 //                  16w..16w+15.  For each KV head the rows that selected the
 //                  block come in chunks of 64 / G rows (64 main-branch columns,
@@ -108,6 +111,19 @@ __device__ __forceinline__ void pv_idx(const f32x4 (&w)[2 * KV], const u32x4* ti
   }
 }
 
+// Sum over the G-lane segment of each 16-lane row (G = 4, 8, 16), in every
+// lane of the segment: DPP swaps of neighbours and of pairs (quads), then
+// the half-row mirror (the other quad of 8 lanes) and the row mirror (the
+// other 8 of 16).
+template <int G>
+__device__ __forceinline__ float segment_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  if (G >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  if (G >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
 __device__ __forceinline__ float max16(const f32x4 (&v)[4]) {
   float m = v[0][0];
 #pragma unroll
@@ -144,18 +160,21 @@ __global__ void __launch_bounds__(512) kl_row_kernel(KlArgs a) {
     if (c >= 0 && c <= (a.q_start + t0 + i) / kBlock) atomicOr(&rmask[c], 1u << i);
   }
   __syncthreads();
-  // this lane's main column and index column in each of the wave's two groups
-  const int qcol = n & 7;
+  // this lane's main column (row rloc, head n % G) and index column (the same
+  // row, index head h + Hkv m) in each of the wave's two groups
+  const int e = n % G;
+  const bool is_u = e < nih;                        // U copy of the index column
+  const int mloc = is_u ? e : e - nih;
   bf16x8 qf[2][4], iqf[2][2];
   float lse2[2];
-  int pos[2], rloc[2], iloc[2], ihead[2], src[2];
+  int pos[2], rloc[2], ihead[2];
   bool ivalid[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int grp = 2 * wave + j;
     rloc[j] = grp * RPG + n / G;
     const bool ok = rloc[j] < rows;
-    const int t = t0 + (ok ? rloc[j] : 0), hq = h * G + n % G;
+    const int t = t0 + (ok ? rloc[j] : 0), hq = h * G + e;
     const u32x4* qs = reinterpret_cast<const u32x4*>(a.q + (((long long)b * a.Sq + t) * a.Hq + hq) * kHeadDim);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -165,14 +184,10 @@ __global__ void __launch_bounds__(512) kl_row_kernel(KlArgs a) {
     }
     lse2[j] = ok ? a.lse[((long long)b * a.Hq + hq) * a.Sq + t] * kLog2eB : 0.f;
     pos[j] = ok ? a.q_start + t : -1;
-    // index column: row qcol / nih of the group, index head h + Hkv (qcol % nih)
-    const int rg = min(qcol / nih, RPG - 1);
-    iloc[j] = grp * RPG + rg;
-    ihead[j] = h + a.Hkv * (qcol % nih);
-    ivalid[j] = qcol < RPG * nih && iloc[j] < rows;
-    src[j] = g * 16 + rg * G;  // a lane holding the row's P
+    ihead[j] = h + a.Hkv * (mloc < nih ? mloc : 0);
+    ivalid[j] = ok && e < 2 * nih;
     const u32x4* is = reinterpret_cast<const u32x4*>(
-        a.iq + (((long long)b * a.Sq + t0 + (ivalid[j] ? iloc[j] : 0)) * kIdxHeads + ihead[j]) * kIdxDim);
+        a.iq + (((long long)b * a.Sq + t) * kIdxHeads + ihead[j]) * kIdxDim);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       u32x4 v = {0, 0, 0, 0};
@@ -180,7 +195,6 @@ __global__ void __launch_bounds__(512) kl_row_kernel(KlArgs a) {
       iqf[j][ks] = as_bf16x8(v);
     }
   }
-  const int ipos0 = a.q_start + t0;
   f32x4 acc[2][4];
   float m[2], l[2], A2[2], B2[2], Ps[2];
 #pragma unroll
@@ -239,8 +253,7 @@ __global__ void __launch_bounds__(512) kl_row_kernel(KlArgs a) {
       const int grp = 2 * wave + j;
       if (((msk >> (grp * RPG)) & ((1u << RPG) - 1u)) == 0u) continue;  // wave-uniform
       const bool wants = (msk >> rloc[j]) & 1u;
-      const bool iwants = ivalid[j] && ((msk >> iloc[j]) & 1u);
-      const int ipos = ipos0 + iloc[j];
+      const bool iwants = ivalid[j] && wants;
       f32x4 sv[4], si[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -253,20 +266,18 @@ __global__ void __launch_bounds__(512) kl_row_kernel(KlArgs a) {
         for (int ks = 0; ks < 2; ++ks)
           si[mt] = mfma16(as_bf16x8(it[islot(16 * mt + n, 4 * ks + g)]), iqf[j][ks], si[mt]);
       }
-      // P of the main column, summed over the row's G heads, then carried to
-      // the index column's lane; index scores in the log2 domain, masked
+      // P of the main column, averaged over the row's G heads (every lane of
+      // the row's segment); index scores in the log2 domain, masked
       f32x4 pr[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = c * kBlock + 16 * mt + 4 * g + r;
-          float p = (wants && key <= pos[j]) ? exp2f(sv[mt][r] * a.scale_log2 - lse2[j]) : 0.f;
-#pragma unroll
-          for (int o = 1; o < G; o <<= 1) p += __shfl_xor(p, o);
-          pr[mt][r] = __shfl(p * invG, src[j]);
-          const bool ok = iwants && key <= ipos;
-          si[mt][r] = ok ? si[mt][r] * kLog2eB : -__builtin_huge_valf();
+          const bool att = key <= pos[j];
+          const float p = (wants && att) ? exp2f(sv[mt][r] * a.scale_log2 - lse2[j]) : 0.f;
+          pr[mt][r] = segment_sum<G>(p) * invG;
+          si[mt][r] = (iwants && att) ? si[mt][r] * kLog2eB : -__builtin_huge_valf();
         }
       const float mb = wave_max_xor16_32(max16(si));
       const float mn = fmaxf(m[j], mb);
@@ -280,25 +291,25 @@ __global__ void __launch_bounds__(512) kl_row_kernel(KlArgs a) {
         for (int r = 0; r < 4; ++r) {
           const float s2 = si[mt][r];
           const bool ok = s2 != -__builtin_huge_valf();
-          const float e = ok ? exp2f(s2 - mn) : 0.f;
+          const float ev = ok ? exp2f(s2 - mn) : 0.f;
           const float p = pr[mt][r];
-          ls += e;
+          ls += ev;
           ps += p;
           if (p > 0.f) {  // p > 0 only at attended keys, where s2 is finite
             a2 += p * __log2f(p);
             b2 += p * s2;
           }
-          w[mt][r] = n < 8 ? e : p;
+          w[mt][r] = is_u ? ev : p;
         }
       l[j] = l[j] * alpha + ls;
       A2[j] += a2;
       B2[j] += b2;
       Ps[j] += ps;
-      if (n < 8) {
+      if (is_u) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) acc[j][mt] *= alpha;
       }
-      pv_idx<2>(w, it, acc[j]);  // U (columns < 8) and V (columns >= 8)
+      pv_idx<2>(w, it, acc[j]);  // U (first copies) and V (second copies)
     }
     __syncthreads();  // tiles bf free for the block after cn
     c = cn;
@@ -314,9 +325,9 @@ __global__ void __launch_bounds__(512) kl_row_kernel(KlArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vv[mt][r] = __shfl_xor(acc[j][mt][r], 8);
-    if (n < 8 && ivalid[j]) {
-      const int t = t0 + iloc[j];
+      for (int r = 0; r < 4; ++r) vv[mt][r] = __shfl(acc[j][mt][r], lane + nih);  // V copy
+    if (is_u && ivalid[j]) {
+      const int t = t0 + rloc[j];
       const bool any = lt > 0.f;
       const float inv = any ? 1.f / lt : 0.f;
       float* dst = a.diq + (((long long)b * a.Sq + t) * kIdxHeads + ihead[j]) * kIdxDim;

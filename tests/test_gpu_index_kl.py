@@ -131,3 +131,90 @@ def test_index_kl_empty_selection_rows():
         assert not torch.any(loss[:, rows.cuda(), i])
         assert not torch.any(diq[:, rows.cuda(), i])
     check(w, got, ref)
+
+
+def _row_oracle_kl(w, inp, sel, t, h):
+    """The oracle's loss and diq of row t for the index heads of KV head h,
+    and its dik over the row's attended tokens, from a compact one-KV-head
+    problem: the row's selected blocks of head h (ascending, own block last)
+    with the row at the same offset inside its own block attends exactly the
+    row's tokens.  Returns (index heads, loss, diq, dik, token ids)."""
+    bs = w.block_size
+    pos = w.q_start + t
+    m = min(w.top_k, pos // bs + 1)
+    blocks = sel[0, h, t, :m].long()
+    tok = (blocks.unsqueeze(-1) * bs + torch.arange(bs, device=blocks.device)).reshape(-1)
+    tok = tok.clamp(max=w.seq_kv - 1)
+    G = w.group
+    heads = [i for i in range(w.n_idx_heads) if i % w.n_kv_heads == h]
+    kk = inp.k[0, h].index_select(0, tok)[None, None]                  # [1][1][m*64][D]
+    ikk = inp.ik[0].index_select(0, tok)[None]                          # [1][m*64][Di]
+    qq = inp.q[:, t:t + 1, h * G:(h + 1) * G]                           # [1][1][G][D]
+    iqq = inp.iq[:, t:t + 1, heads]                                     # [1][1][nih][Di]
+    p = O.Problem(1, 1, m * bs, (m - 1) * bs + pos % bs, G, 1, w.head_dim, len(heads),
+                  w.idx_head_dim, bs, m, False, w.softmax_scale)
+    s = np.arange(m, dtype=np.int32).reshape(1, 1, 1, m)
+    loss, diq, dik = O.index_kl(p, f64(qq), f64(kk), f64(iqq), f64(ikk), None, s)
+    return heads, loss[0, 0], diq[0, 0], dik[0], tok.cpu().numpy()
+
+
+def test_index_kl_128k_sampled_rows_last_block_and_identities():
+    """The 128K workload at full size.  loss and diq of a stratified row
+    sample against the oracle (compact per-row problems).  dik of every key of
+    the last block, which exactly the last 64 rows attend (their own block),
+    summed from the oracle over those rows and all KV heads.  And two
+    identities of the whole output, which tie the key pass to the row pass:
+    sum_j dik_j = 0 (each row's Q - P sums to zero) and
+    sum_j dik_j . ik_j = sum_(t,i) diq_(t,i) . iq_(t,i) (both are the sum of
+    (Q_j - P_j) s_j over every attended triple).  Their residuals come from
+    the bf16 rounding of the products' weights; a dropped or misplaced term
+    leaves a residual of order one.  Bound: 2e-3 of the sum of magnitudes."""
+    need_gpu()
+    from block_sparse_gqa_02_amd.configs import PREFILL_128K as w
+    import parity as PAR
+    print(f"[index_kl] {w.name} full size", flush=True)
+    inp = generate(w, "cuda")
+    p = msa.Problem.from_workload(w)
+    sel = msa.msa_topk_blocks(p, msa.msa_index_block_scores(p, inp.iq, inp.ik))
+    lse = torch.empty((w.batch, w.n_q_heads, w.seq_q), dtype=torch.float32, device="cuda")
+    msa.msa_sparse_attn_prefill(p, inp.q, inp.k, inp.v, sel, lse=lse)
+    loss, diq, dik = msa.msa_index_kl_backward(p, inp.q, inp.k, inp.iq, inp.ik, sel, lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(loss).all() and torch.isfinite(diq).all() and torch.isfinite(dik).all()
+    # identities over the whole output
+    s1 = dik.double().sum(dim=1).abs().max().item()
+    a1 = dik.double().abs().sum(dim=1).max().item()
+    lhs = (dik.double() * inp.ik.double()).sum().item()
+    per_row = (diq.double() * inp.iq.double()).sum(dim=-1)              # [B][Sq][4]
+    rhs = per_row.sum().item()
+    r1, r2 = s1 / a1, abs(lhs - rhs) / per_row.abs().sum().item()
+    print(f"  |sum dik| / sum |dik| = {r1:.2e}; |sum dik.ik - sum diq.iq| / sum |diq.iq| = "
+          f"{r2:.2e} ({lhs:.4e} vs {rhs:.4e})", flush=True)
+    assert r1 <= 2e-3 and r2 <= 2e-3, (r1, r2)
+    # sampled rows: loss and diq
+    rows = PAR.sample_rows(w.seq_q, w.q_start, w.block_size, seed=11, n_uniform=48, n_log=8)
+    rows = rows[np.random.default_rng(11).permutation(len(rows))[:96]]
+    gl, gq = f64(loss[0]), f64(diq[0])
+    rl, rq, ql, qq = [], [], [], []
+    for t in rows:
+        for h in range(w.n_kv_heads):
+            heads, l_, q_, _, _ = _row_oracle_kl(w, inp, sel, int(t), h)
+            rl.append(l_)
+            rq.append(q_)
+            ql.append(gl[t, heads])
+            qq.append(gq[t, heads])
+    err = float(np.abs(np.concatenate(ql) - np.concatenate(rl)).max())
+    mx, mn = rel_errors(np.concatenate(qq), np.concatenate(rq))
+    print(f"  {len(rows)} rows: loss max abs {err:.2e}; diq max {mx:.2e} mean {mn:.2e}", flush=True)
+    assert err <= LOSS_ABS and mx <= MAX_REL and mn <= MEAN_REL, (err, mx, mn)
+    # the last block's keys: exactly the last 64 rows attend them
+    c = (w.seq_kv - 1) // w.block_size
+    ref = np.zeros((w.seq_kv - c * w.block_size, w.idx_head_dim))
+    for t in range(c * w.block_size - w.q_start, w.seq_q):
+        for h in range(w.n_kv_heads):
+            _, _, _, dk_, tok = _row_oracle_kl(w, inp, sel, t, h)
+            own = tok >= c * w.block_size
+            np.add.at(ref, tok[own] - c * w.block_size, dk_[own])
+    mx, mn = rel_errors(f64(dik[0, c * w.block_size:]), ref)
+    print(f"  dik of the last block: max {mx:.2e} mean {mn:.2e}", flush=True)
+    assert mx <= MAX_REL and mn <= MEAN_REL, (mx, mn)
