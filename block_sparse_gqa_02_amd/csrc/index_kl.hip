@@ -54,6 +54,16 @@ namespace {
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kKlTileRows = 16;  // rows per work-group of the row pass
+// A block's job list (chunks of rows over every KV head) is cut into up to
+// kKeySplits work-groups of at least kKeyMinJobs jobs: a block early in the
+// context is a candidate for every later row, so its list runs to several
+// times the mean, and one work-group per block would leave a long tail.
+constexpr int kKeySplits = 8;
+constexpr int kKeyMinJobs = 64;
+
+__device__ __forceinline__ int key_splits(int total) {
+  return max(1, min(kKeySplits, total / kKeyMinJobs));
+}
 
 struct KlArgs {
   const uint16_t* q;     // [B][Sq][Hq][128]
@@ -66,6 +76,7 @@ struct KlArgs {
   float* diq;            // [B][Sq][4][64]
   float* dik;            // [B][Skv][64]
   float* lse_idx;        // workspace [B][4][Sq]: index log-sum-exp, log2 domain
+  float* dikp;           // workspace [B][nblk][kKeySplits][64][64]: split partials of dik
   const int32_t* base;   // inverse lists: starts per (sequence, KV head, block), then the total
   const int32_t* lists;  // rows
   int B, Sq, Skv, q_start, Hq, Hkv, G, top_k, nblk, nih;
@@ -343,8 +354,11 @@ __global__ void __launch_bounds__(512) kl_row_kernel(KlArgs a) {
   }
 }
 
-// Key pass.  Work-group (block, sequence), 4 waves; wave w owns keys
-// 64c + 16w .. +15.  A chunk is R = 64 / G rows of one KV head's list: main
+// Key pass.  Work-group (block, sequence, split), 4 waves; wave w owns keys
+// 64c + 16w .. +15.  Split s of a block with n splits takes jobs
+// [s total / n, (s+1) total / n); with one split it writes dik itself, with
+// more each writes its partial and kl_dik_merge_kernel adds them in split
+// order (deterministic).  A chunk is R = 64 / G rows of one KV head's list: main
 // columns (row i / G, head i % G), i < 64, and index columns (row i / nih,
 // index head h + Hkv (i % nih)), i < R nih <= 32.
 template <int G>
@@ -456,13 +470,17 @@ __global__ void __launch_bounds__(256) kl_key_kernel(KlArgs a) {
   };
   bf16x8 kf[4];  // main-branch K operand of the wave's keys for the current head
   int kf_head = -1;
-  if (total > 0) {
-    fetch_rows(0);
-    stage(0, 0);
-    if (total > 1) fetch_rows(1);
+  const int nsplit = key_splits(total), split = blockIdx.z;
+  if (split >= nsplit) return;  // uniform over the work-group
+  const int j0 = (int)((long long)split * total / nsplit);
+  const int j1 = (int)((long long)(split + 1) * total / nsplit);
+  if (j0 < j1) {
+    fetch_rows(j0);
+    stage(j0, 0);
+    if (j0 + 1 < j1) fetch_rows(j0 + 1);
   }
-  for (int j = 0; j < total; ++j) {
-    const int buf = j & 1;
+  for (int j = j0; j < j1; ++j) {
+    const int buf = (j - j0) & 1;
     int chunk;
     const int h = head_of(j, chunk);
     if (h != kf_head) {  // uniform; loads complete at the wait below
@@ -485,9 +503,9 @@ __global__ void __launch_bounds__(256) kl_key_kernel(KlArgs a) {
       ipos[buf][tid - 64] = mp;
     }
     __syncthreads();
-    if (j + 1 < total) {
+    if (j + 1 < j1) {
       stage(j + 1, buf ^ 1);
-      if (j + 2 < total) fetch_rows(j + 2);
+      if (j + 2 < j1) fetch_rows(j + 2);
     }
     // X = Q K^T: M = main columns (16mt + 4g + r), N = the wave's keys
     f32x4 x[4];
@@ -539,10 +557,41 @@ __global__ void __launch_bounds__(256) kl_key_kernel(KlArgs a) {
     __syncthreads();                  // buffers buf free for job j + 2
   }
   if (n < nkeys) {
-    float* dst = a.dik + ((long long)b * a.Skv + key) * kIdxDim;
+    float* dst = nsplit == 1
+                     ? a.dik + ((long long)b * a.Skv + key) * kIdxDim
+                     : a.dikp + ((((long long)b * a.nblk + c) * kKeySplits + split) * kBlock +
+                                 16 * wave + n) * kIdxDim;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * g) = dka[mt];
   }
+}
+
+// dik of the blocks whose list was split: the splits' partials added in split
+// order.  Work-group (block, sequence); thread = (key, 16-dim quarter).
+__global__ void __launch_bounds__(256) kl_dik_merge_kernel(KlArgs a) {
+  const int c = blockIdx.x, b = blockIdx.y;
+  int total = 0;
+  for (int h = 0; h < a.Hkv; ++h) {
+    const long long e = ((long long)b * a.Hkv + h) * a.nblk + c;
+    total += (a.base[e + 1] - a.base[e] + 64 / a.G - 1) / (64 / a.G);
+  }
+  const int nsplit = key_splits(total);
+  if (nsplit == 1) return;
+  const int kl = threadIdx.x / 4, d0 = 16 * (threadIdx.x % 4);
+  const int key = c * kBlock + kl;
+  if (key >= a.Skv) return;
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; ++s) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(
+        a.dikp + ((((long long)b * a.nblk + c) * kKeySplits + s) * kBlock + kl) * kIdxDim + d0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += src[i];
+  }
+  f32x4* dst = reinterpret_cast<f32x4*>(a.dik + ((long long)b * a.Skv + key) * kIdxDim + d0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i] = acc[i];
 }
 
 char* align256(char* p) { return reinterpret_cast<char*>(((uintptr_t)p + 255) & ~(uintptr_t)255); }
@@ -555,7 +604,9 @@ bool index_kl_supported(const Shape& s) {
 }
 
 size_t index_kl_workspace_bytes(const Shape& s) {
-  return (size_t)s.B * kIdxHeads * s.Sq * 4 + 256 + inverse_lists_bytes(s);
+  return (size_t)s.B * kIdxHeads * s.Sq * 4 + 256 +                       // index log-sum-exp
+         (size_t)s.B * s.nblk * kKeySplits * kBlock * kIdxDim * 4 + 256 +  // dik split partials
+         inverse_lists_bytes(s);
 }
 
 namespace {
@@ -568,7 +619,8 @@ hipError_t launch_kl(const Shape& s, const KlArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   constexpr int waves = G / 2;  // G row groups, two per wave
   kl_row_kernel<G><<<dim3(ceil_div(s.Sq, kKlTileRows), s.Hkv, s.B), waves * kWave, lds, st>>>(a);
-  kl_key_kernel<G><<<dim3(s.nblk, s.B), 256, 0, st>>>(a);
+  kl_key_kernel<G><<<dim3(s.nblk, s.B, kKeySplits), 256, 0, st>>>(a);
+  kl_dik_merge_kernel<<<dim3(s.nblk, s.B), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 }  // namespace
@@ -580,14 +632,16 @@ hipError_t launch_index_kl_backward(const Shape& s, const void* q, const void* k
   if (!index_kl_supported(s)) return hipErrorInvalidValue;
   char* p = align256(static_cast<char*>(ws));
   float* lse_idx = reinterpret_cast<float*>(p);
-  p += (size_t)s.B * kIdxHeads * s.Sq * 4;
+  p = align256(p + (size_t)s.B * kIdxHeads * s.Sq * 4);
+  float* dikp = reinterpret_cast<float*>(p);
+  p += (size_t)s.B * s.nblk * kKeySplits * kBlock * kIdxDim * 4;
   const int32_t* base = nullptr;
   const int32_t* lists = nullptr;
   hipError_t e = launch_inverse_lists(s, sel, p, &base, &lists, st);
   if (e != hipSuccess) return e;
   KlArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
            static_cast<const uint16_t*>(iq), static_cast<const uint16_t*>(ik), sel, lse, loss,
-           diq, dik, lse_idx, base, lists, s.B, s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.G,
+           diq, dik, lse_idx, dikp, base, lists, s.B, s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.G,
            s.top_k, s.nblk, kIdxHeads / s.Hkv, s.scale * kLog2eB};
   switch (s.G) {
     case 4: return launch_kl<4>(s, a, st);

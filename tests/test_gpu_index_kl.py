@@ -7,8 +7,9 @@ Cases cover query groups of 4, 8 and 16 heads, one, two and four index heads
 per KV head (index head i drives KV head i mod Hkv), ragged last row tiles and
 blocks, rows with short lists (fewer causal blocks than k), a chunk whose rows
 start past 0 in a longer cache (keys no row attends: dik exactly zero), two
-sequences, and rows whose selection for one KV head is empty (loss and diq
-exactly zero for that head's index heads).
+sequences, rows whose selection for one KV head is empty (loss and diq
+exactly zero for that head's index heads), and the 2K workload, whose early
+blocks' row lists are split over several work-groups of the key pass.
 
 Tolerance, from the arithmetic: scores and softmax statistics are fp32 from
 exact bf16 products, so the loss carries only fp32 rounding (max abs error
@@ -47,6 +48,9 @@ CASES = {
     # G = 16: one row per 16 query columns
     "g16_hkv2": TINY_PREFILL_2K.shrink(name="kl_g16", seq_q=400, seq_kv=900, q_start=500,
                                        n_q_heads=32, n_kv_heads=2, top_k=6),
+    # the 2K workload: early blocks' row lists are long enough that the key
+    # pass splits them over several work-groups and merges the dik partials
+    "tiny_2k": TINY_PREFILL_2K,
 }
 
 
