@@ -3,9 +3,9 @@ oracle's gradient (oracle_attend_backward) on the GPU's own selection and the
 same bf16 inputs, every element compared.  Sizes span several 64-row batches
 and 64-key blocks with ragged tails, rows that precede k blocks (short, padded
 lists), a chunk whose rows start past 0 with a cache longer than the rows
-(blocks no row reads: their dk, dv must be exactly zero), and query groups of
+(blocks no row reads: their dk, dv must be exactly zero), query groups of
 2, 4, 8 and 16 heads (4 and 8 take the tile-union dq kernel, the others the
-per-row one).
+per-row one), and row lists of hundreds of 64-column chunks.
 
 Tolerance, per tensor, from the arithmetic: the kernels round P and dS to
 bf16 (as the forward rounds P) and take Dsum from the bf16 forward output, so
@@ -40,6 +40,10 @@ CASES = {
                                          n_kv_heads=4, top_k=3),
     "g16_rowwise": TINY_PREFILL_2K.shrink(name="bwd_g16", seq_q=400, seq_kv=900, q_start=500,
                                           n_q_heads=32, n_kv_heads=2, top_k=6),
+    # 1536 rows of one KV head at G = 16 (4 rows per 64-column chunk): the
+    # first blocks' row lists run to hundreds of chunks in the dK/dV pass
+    "g16_long_lists": TINY_PREFILL_2K.shrink(name="bwd_g16s", seq_q=1536, seq_kv=1536, n_q_heads=16,
+                                        n_kv_heads=1, top_k=8),
 }
 
 
