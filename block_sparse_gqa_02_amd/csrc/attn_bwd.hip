@@ -57,6 +57,7 @@ struct BwdArgs {
   int32_t* bcnt;         // workspace [B][Hkv][nbatch][nblk]: counts, then offsets in the list
   int32_t* base;         // workspace [B*Hkv*nblk + 1]: list starts (exclusive scan)
   int32_t* lists;        // workspace [B*Hkv*Sq*top_k]: rows per (sequence, KV head, block)
+  int32_t* slotpos;      // optional [B][Hkv][Sq][top_k]: list position of each entry, or -1
   int B, Sq, Skv, q_start, Hq, Hkv, G, top_k, nblk, nbatch;
   float scale, scale_log2;
 };
@@ -125,7 +126,8 @@ __global__ void __launch_bounds__(256) dsum_kernel(BwdArgs a) {
 }
 
 // Inverse lists, pass 1 (FILL = false: per-batch counts) and pass 3 (FILL =
-// true: rows written at their offsets).  One work-group per (sequence, KV
+// true: rows written at their offsets; with slotpos, also the position in its
+// block's list of every selection entry, -1 for entries that attend nothing).  One work-group per (sequence, KV
 // head, batch of 64 rows); the bitmap (one 64-bit word per block, dynamic LDS)
 // marks which rows of the batch selected each block.  A selection entry
 // counts when 0 <= c <= the row's own block, the blocks the forward attends.
@@ -159,6 +161,19 @@ __global__ void __launch_bounds__(256) inverse_kernel(BwdArgs a) {
         m &= m - 1;
         *dst++ = t0 + i;
       }
+    }
+  }
+  if (FILL && a.slotpos) {
+    // row i of the batch sits after the batch's earlier rows that chose c
+    int32_t* sp = a.slotpos + (hb * a.Sq + t0) * a.top_k;
+    for (int idx = threadIdx.x; idx < rows * a.top_k; idx += 256) {
+      const int i = idx / a.top_k;
+      const int c = srow[idx];
+      const int cur = (a.q_start + t0 + i) / kBlock;
+      int32_t pos = -1;
+      if (c >= 0 && c <= cur)
+        pos = a.base[hb * a.nblk + c] + cnt[c] + __popcll(bm[c] & ((1ull << i) - 1ull));
+      sp[idx] = pos;
     }
   }
 }
@@ -567,7 +582,7 @@ size_t inverse_lists_bytes(const Shape& s) {
 
 hipError_t launch_inverse_lists(const Shape& s, const int32_t* sel, void* ws,
                                 const int32_t** base_out, const int32_t** lists_out,
-                                hipStream_t st) {
+                                hipStream_t st, int32_t* slotpos) {
   const int nbatch = ceil_div(s.Sq, kBatchRows);
   const size_t bm_bytes = (size_t)s.nblk * 8;
   if (bm_bytes > 160 * 1024) return hipErrorInvalidValue;
@@ -582,6 +597,7 @@ hipError_t launch_inverse_lists(const Shape& s, const int32_t* sel, void* ws,
   a.bcnt = bcnt;
   a.base = base;
   a.lists = lists;
+  a.slotpos = slotpos;
   a.B = s.B;
   a.Sq = s.Sq;
   a.Skv = s.Skv;
@@ -627,7 +643,7 @@ hipError_t launch_sparse_attn_backward(const Shape& s, const void* q, const void
   BwdArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
             static_cast<const uint16_t*>(v), sel, static_cast<const uint16_t*>(out), lse,
             static_cast<const uint16_t*>(dout), dq, dk, dv, dsum, nullptr, nullptr, nullptr,
-            s.B, s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.G, s.top_k, s.nblk,
+            nullptr, s.B, s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.G, s.top_k, s.nblk,
             ceil_div(s.Sq, kBatchRows), s.scale, s.scale * kLog2eB};
   const long long nrows = (long long)s.B * s.Sq * s.Hq;
   dsum_kernel<<<(unsigned)((nrows + 3) / 4), 256, 0, st>>>(a);

@@ -14,36 +14,29 @@
 // d loss / d s_j = Q_j - P_j, so diq_i = sum_j (Q_j - P_j) ik_j and
 // dik_j = sum over the (t, i) attending j of (Q_j - P_j) iq_i.
 //
-// Kernels, in launch order:
-//   inverse lists  (shared with the main-branch gradient) the ascending rows
-//                  that selected each (sequence, KV head, block).
-//   kl_row_kernel  a work-group per 16 rows of one (sequence, KV head) walks the
-//                  union of the rows' selected blocks, each block's K and index
-//                  K fetched once into double-buffered LDS tiles.  A row group
-//                  (16 / G rows) owns 16 main-branch columns (row, query head),
-//                  each row a segment of G lanes, and 16 index columns laid in
-//                  the same segments: lane e < nih of a row's segment is (row,
-//                  index head e) (nih = index heads per KV head), lane
-//                  nih <= e < 2 nih repeats (row, e - nih).  Per block: S^T =
-//                  K Q^T gives P per head, summed over the row's segment (DPP
-//                  lane swaps, so every lane of the row holds its P); the index
-//                  scores of the columns; an online log-sum-exp of the index
-//                  scores; and one product over the block's index-key rows
-//                  whose first copy of each column weighs them by e^{s - m}
-//                  (U, rescaled as m grows) and whose second by P (V), so that
-//                  diq = U / l - V comes out of one sweep.  The loss is
-//                  gathered from sum P log P, sum P s and sum P.  Writes loss,
-//                  diq and the index log-sum-exp.
-//   kl_key_kernel  a work-group per (block, sequence); wave w owns keys
-//                  16w..16w+15.  For each KV head the rows that selected the
-//                  block come in chunks of 64 / G rows (64 main-branch columns,
-//                  staged with the matching index-query columns by LDS-bound
-//                  loads, the next chunk's while one is computed): X = Q K^T
-//                  gives P per row, the index scores and the saved log-sum-exp
-//                  give Q, and dik^T += iq^T (Q - P)^T.  Each key's gradient is
-//                  written once (zero for keys no row attends): deterministic,
-//                  no atomics.
-// Products take bf16 operands (P, e^{s-m} and Q - P rounded to bf16) with fp32
+// Every step runs block-stationary: each selected (sequence, KV head, block)
+// is read once, by the work-group that owns the block, for every row that
+// selected it, and per-row results are gathered from per-(list entry) partials
+// in slot order.  Kernels, in launch order:
+//   inverse lists        (shared with the main-branch gradient) the ascending
+//                        rows that selected each (sequence, KV head, block),
+//                        and the list position of every selection entry.
+//   kl_lse_kernel        per (list entry, index head), over the block's keys
+//                        the row attends: the max of the index scores and the
+//                        sum of 2^(s - max).
+//   kl_lse_merge_kernel  the index log-sum-exp per (row, index head), its
+//                        entries combined in slot order.
+//   kl_key_kernel        per chunk of a block's rows: P from the forward's
+//                        log-sum-exp, Q from the index log-sum-exp, C = Q - P;
+//                        per (list entry, index head) the loss partial and the
+//                        diq partial (sums over the block's keys), and per key
+//                        dik (a sum over the block's rows).  Long lists are
+//                        split over work-groups.
+//   kl_dik_merge_kernel  dik of split blocks, partials added in split order.
+//   kl_merge_kernel      loss and diq per (row, index head), partials added in
+//                        slot order.
+// Nothing uses floating-point atomics: results are bit-identical from call to
+// call.  Products take bf16 operands (C rounded to bf16) with fp32
 // accumulation; softmax statistics are fp32.
 #include "bwd_tiles.h"
 #include "common.h"
@@ -53,7 +46,6 @@ namespace msa {
 namespace {
 
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kKlTileRows = 16;  // rows per work-group of the row pass
 // A block's job list (chunks of rows over every KV head) is cut into up to
 // kKeySplits work-groups of at least kKeyMinJobs jobs: a block early in the
 // context is a candidate for every later row, so its list runs to several
@@ -66,19 +58,23 @@ __device__ __forceinline__ int key_splits(int total) {
 }
 
 struct KlArgs {
-  const uint16_t* q;     // [B][Sq][Hq][128]
-  const uint16_t* k;     // [B][Hkv][Skv][128]
-  const uint16_t* iq;    // [B][Sq][4][64]
-  const uint16_t* ik;    // [B][Skv][64]
-  const int32_t* sel;    // [B][Hkv][Sq][top_k]
-  const float* lse;      // [B][Hq][Sq], natural log
-  float* loss;           // [B][Sq][4]
-  float* diq;            // [B][Sq][4][64]
-  float* dik;            // [B][Skv][64]
-  float* lse_idx;        // workspace [B][4][Sq]: index log-sum-exp, log2 domain
-  float* dikp;           // workspace [B][nblk][kKeySplits][64][64]: split partials of dik
-  const int32_t* base;   // inverse lists: starts per (sequence, KV head, block), then the total
-  const int32_t* lists;  // rows
+  const uint16_t* q;       // [B][Sq][Hq][128]
+  const uint16_t* k;       // [B][Hkv][Skv][128]
+  const uint16_t* iq;      // [B][Sq][4][64]
+  const uint16_t* ik;      // [B][Skv][64]
+  const int32_t* sel;      // [B][Hkv][Sq][top_k]
+  const float* lse;        // [B][Hq][Sq], natural log
+  float* loss;             // [B][Sq][4]
+  float* diq;              // [B][Sq][4][64]
+  float* dik;              // [B][Skv][64]
+  float* lse_idx;          // workspace [B][4][Sq]: index log-sum-exp, log2 domain
+  float* dikp;             // workspace [B][nblk][kKeySplits][64][64]: split partials of dik
+  const int32_t* slotpos;  // workspace [B][Hkv][Sq][top_k]: list position of an entry, or -1
+  f32x2* part_ml;          // workspace [entries][nih]: block max and sum (log2 domain)
+  float* part_q;           // workspace [entries][nih][64]: diq partials
+  float* part_l;           // workspace [entries][nih]: loss partials
+  const int32_t* base;     // inverse lists: starts per (sequence, KV head, block), then the total
+  const int32_t* lists;    // rows
   int B, Sq, Skv, q_start, Hq, Hkv, G, top_k, nblk, nih;
   float scale_log2;
 };
@@ -144,240 +140,13 @@ __device__ __forceinline__ float max16(const f32x4 (&v)[4]) {
   return m;
 }
 
-// Row pass.  Work-group (tile, KV head, sequence), 16 / G row groups of 16 / G
-// rows, two groups per wave.
-template <int G>
-__global__ void __launch_bounds__(512) kl_row_kernel(KlArgs a) {
-  extern __shared__ u32x4 kl_lds[];
-  u32x4* ktiles = kl_lds;                   // [2][1024]: K of the current / next block
-  u32x4* itiles = kl_lds + 2 * 1024;        // [2][512]: its index-key rows
-  uint32_t* rmask = reinterpret_cast<uint32_t*>(kl_lds + 3 * 1024);  // [cmax + 1]
+// Work-group setup shared by the two block passes: every KV head's list for
+// block c (start, length and job count, jobs of `per` rows, in LDS) and the
+// block's 64 index keys in LDS (islot layout; rows past the cache repeat the
+// last key, masked by position).  Leaves the index-key loads in flight.
+__device__ __forceinline__ void block_setup(const KlArgs& a, int b, int c, int per, int* lbeg,
+                                            int* llen, int* lnj, u32x4* itile) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int nwaves = blockDim.x / kWave;
-  const int n = lane % 16, g = lane / 16;
-  const int h = blockIdx.y, b = blockIdx.z;
-  constexpr int RPG = 16 / G;
-  const int nih = a.nih;
-  const int t0 = blockIdx.x * kKlTileRows;
-  const int rows = min(kKlTileRows, a.Sq - t0);
-  const int cmax = (a.q_start + t0 + rows - 1) / kBlock;
-  const long long hb = (long long)b * a.Hkv + h;
-  for (int c = tid; c <= cmax; c += blockDim.x) rmask[c] = 0u;
-  __syncthreads();
-  const int32_t* srow = a.sel + (hb * a.Sq + t0) * a.top_k;
-  for (int idx = tid; idx < rows * a.top_k; idx += blockDim.x) {
-    const int i = idx / a.top_k;
-    const int c = srow[idx];
-    if (c >= 0 && c <= (a.q_start + t0 + i) / kBlock) atomicOr(&rmask[c], 1u << i);
-  }
-  __syncthreads();
-  // this lane's main column (row rloc, head n % G) and index column (the same
-  // row, index head h + Hkv m) in each of the wave's two groups
-  const int e = n % G;
-  const bool is_u = e < nih;                        // U copy of the index column
-  const int mloc = is_u ? e : e - nih;
-  bf16x8 qf[2][4], iqf[2][2];
-  float lse2[2];
-  int pos[2], rloc[2], ihead[2];
-  bool ivalid[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int grp = 2 * wave + j;
-    rloc[j] = grp * RPG + n / G;
-    const bool ok = rloc[j] < rows;
-    const int t = t0 + (ok ? rloc[j] : 0), hq = h * G + e;
-    const u32x4* qs = reinterpret_cast<const u32x4*>(a.q + (((long long)b * a.Sq + t) * a.Hq + hq) * kHeadDim);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 qv = {0, 0, 0, 0};
-      if (ok) qv = qs[4 * ks + g];
-      qf[j][ks] = as_bf16x8(qv);
-    }
-    lse2[j] = ok ? a.lse[((long long)b * a.Hq + hq) * a.Sq + t] * kLog2eB : 0.f;
-    pos[j] = ok ? a.q_start + t : -1;
-    ihead[j] = h + a.Hkv * (mloc < nih ? mloc : 0);
-    ivalid[j] = ok && e < 2 * nih;
-    const u32x4* is = reinterpret_cast<const u32x4*>(
-        a.iq + (((long long)b * a.Sq + t) * kIdxHeads + ihead[j]) * kIdxDim);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 v = {0, 0, 0, 0};
-      if (ivalid[j]) v = is[4 * ks + g];
-      iqf[j][ks] = as_bf16x8(v);
-    }
-  }
-  f32x4 acc[2][4];
-  float m[2], l[2], A2[2], B2[2], Ps[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[j] = -__builtin_huge_valf();
-    l[j] = A2[j] = B2[j] = Ps[j] = 0.f;
-  }
-  const float invG = 1.f / (float)G;
-  // first block >= from with a nonzero mask (cmax + 1 if none); same in every wave
-  auto next_block = [&](int from) {
-    for (int base = from; base <= cmax; base += kWave) {
-      const int c = base + lane;
-      const uint64_t bal = ballot(c <= cmax && rmask[c] != 0u);
-      if (bal != 0ull) return base + (int)__builtin_ctzll(bal);
-    }
-    return cmax + 1;
-  };
-  // LDS-bound loads of block c's K (16 instructions of 4 rows) and index-key
-  // rows (8 instructions of 8 rows) into tiles bf; rows past the cache re-read
-  // the last row (masked: they lie past every position)
-  auto fetch = [&](int c, int bf) {
-    const long long koff = (hb * a.Skv + (long long)c * kBlock) * kHeadDim;
-    for (int inst = wave; inst < 24; inst += nwaves) {
-      const int slot = (inst & 15) * kWave + lane;
-      if (inst < 16) {
-        const int key = slot >> 4;
-        const int ch = (slot & 15) ^ (key & 15);
-        const int krow = min(c * kBlock + key, a.Skv - 1);
-        __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const void*>(a.k + koff + (long long)(krow - c * kBlock) * kHeadDim + 8 * ch),
-            (__attribute__((address_space(3))) void*)(ktiles + bf * 1024 + inst * kWave), 16, 0, 0);
-      } else {
-        const int key = slot >> 3;
-        const int ch = (slot & 7) ^ (key & 7);
-        const int krow = min(c * kBlock + key, a.Skv - 1);
-        __builtin_amdgcn_global_load_lds(
-            reinterpret_cast<const void*>(a.ik + ((long long)b * a.Skv + krow) * kIdxDim + 8 * ch),
-            (__attribute__((address_space(3))) void*)(itiles + bf * 512 + (inst - 16) * kWave), 16, 0, 0);
-      }
-    }
-  };
-  int c = next_block(0), bf = 0;
-  if (c <= cmax) fetch(c, 0);
-  while (c <= cmax) {
-    const int cn = next_block(c + 1);
-    wait_all_loads();
-    __syncthreads();  // block c's tiles complete in every wave
-    if (cn <= cmax) fetch(cn, bf ^ 1);
-    const uint32_t msk = rmask[c];
-    const u32x4* kt = ktiles + bf * 1024;
-    const u32x4* it = itiles + bf * 512;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int grp = 2 * wave + j;
-      if (((msk >> (grp * RPG)) & ((1u << RPG) - 1u)) == 0u) continue;  // wave-uniform
-      const bool wants = (msk >> rloc[j]) & 1u;
-      const bool iwants = ivalid[j] && wants;
-      f32x4 sv[4], si[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        sv[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        si[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          sv[mt] = mfma16(as_bf16x8(kt[swz_slot(16 * mt + n, 4 * ks + g)]), qf[j][ks], sv[mt]);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          si[mt] = mfma16(as_bf16x8(it[islot(16 * mt + n, 4 * ks + g)]), iqf[j][ks], si[mt]);
-      }
-      // P of the main column, averaged over the row's G heads (every lane of
-      // the row's segment); index scores in the log2 domain, masked
-      f32x4 pr[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = c * kBlock + 16 * mt + 4 * g + r;
-          const bool att = key <= pos[j];
-          const float p = (wants && att) ? exp2f(sv[mt][r] * a.scale_log2 - lse2[j]) : 0.f;
-          pr[mt][r] = segment_sum<G>(p) * invG;
-          si[mt][r] = (iwants && att) ? si[mt][r] * kLog2eB : -__builtin_huge_valf();
-        }
-      const float mb = wave_max_xor16_32(max16(si));
-      const float mn = fmaxf(m[j], mb);
-      const float alpha = (mn == -__builtin_huge_valf()) ? 1.f : exp2f(m[j] - mn);
-      m[j] = mn;
-      float ls = 0.f, a2 = 0.f, b2 = 0.f, ps = 0.f;
-      f32x4 w[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float s2 = si[mt][r];
-          const bool ok = s2 != -__builtin_huge_valf();
-          const float ev = ok ? exp2f(s2 - mn) : 0.f;
-          const float p = pr[mt][r];
-          ls += ev;
-          ps += p;
-          if (p > 0.f) {  // p > 0 only at attended keys, where s2 is finite
-            a2 += p * __log2f(p);
-            b2 += p * s2;
-          }
-          w[mt][r] = is_u ? ev : p;
-        }
-      l[j] = l[j] * alpha + ls;
-      A2[j] += a2;
-      B2[j] += b2;
-      Ps[j] += ps;
-      if (is_u) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[j][mt] *= alpha;
-      }
-      pv_idx<2>(w, it, acc[j]);  // U (first copies) and V (second copies)
-    }
-    __syncthreads();  // tiles bf free for the block after cn
-    c = cn;
-    bf ^= 1;
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const float lt = wave_sum_xor16_32(l[j]);
-    const float a2 = wave_sum_xor16_32(A2[j]);
-    const float b2 = wave_sum_xor16_32(B2[j]);
-    const float ps = wave_sum_xor16_32(Ps[j]);
-    f32x4 vv[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vv[mt][r] = __shfl(acc[j][mt][r], lane + nih);  // V copy
-    if (is_u && ivalid[j]) {
-      const int t = t0 + rloc[j];
-      const bool any = lt > 0.f;
-      const float inv = any ? 1.f / lt : 0.f;
-      float* dst = a.diq + (((long long)b * a.Sq + t) * kIdxHeads + ihead[j]) * kIdxDim;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * g) = any ? acc[j][mt] * inv - vv[mt] : f32x4{0.f, 0.f, 0.f, 0.f};
-      if (g == 0) {
-        const float lse_i = any ? m[j] + __log2f(lt) : -__builtin_huge_valf();
-        a.loss[((long long)b * a.Sq + t) * kIdxHeads + ihead[j]] = any ? kLn2 * (a2 - b2 + lse_i * ps) : 0.f;
-        a.lse_idx[((long long)b * kIdxHeads + ihead[j]) * a.Sq + t] = lse_i;
-      }
-    }
-  }
-}
-
-// Key pass.  Work-group (block, sequence, split), 4 waves; wave w owns keys
-// 64c + 16w .. +15.  Split s of a block with n splits takes jobs
-// [s total / n, (s+1) total / n); with one split it writes dik itself, with
-// more each writes its partial and kl_dik_merge_kernel adds them in split
-// order (deterministic).  A chunk is R = 64 / G rows of one KV head's list: main
-// columns (row i / G, head i % G), i < 64, and index columns (row i / nih,
-// index head h + Hkv (i % nih)), i < R nih <= 32.
-template <int G>
-__global__ void __launch_bounds__(256) kl_key_kernel(KlArgs a) {
-  constexpr int R = 64 / G;
-  __shared__ u32x4 qtile[2][kBlock * 16];  // 64 main columns x 128 dims, swz_slot layout
-  __shared__ u32x4 iqtile[2][32 * 8];      // 32 index columns x 64 dims, islot layout
-  __shared__ float clse[2][64], ilse[2][32];
-  __shared__ int cpos[2][64], ipos[2][32];
-  __shared__ float ptab[4][16][17];        // per wave: P of chunk row x the wave's keys
-  __shared__ int lbeg[4], llen[4], lnch[4];
-  const int c = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int n = lane % 16, g = lane / 16;
-  const int nih = a.nih, NI = R * nih;
-  const int key0 = c * kBlock + 16 * wave;
-  const int nkeys = max(0, min(16, a.Skv - key0));
-  const int key = key0 + n;
-  // every KV head's list for this block, in (head, chunk) order
   if (tid < 4) {
     const bool hv = tid < a.Hkv;
     const long long e = ((long long)b * a.Hkv + (hv ? tid : 0)) * a.nblk + c;
@@ -385,9 +154,157 @@ __global__ void __launch_bounds__(256) kl_key_kernel(KlArgs a) {
     const int ln = hv ? a.base[e + 1] - bg : 0;
     lbeg[tid] = bg;
     llen[tid] = ln;
-    lnch[tid] = (ln + R - 1) / R;
+    lnj[tid] = (ln + per - 1) / per;
   }
-  // index-key operand (N = the wave's keys), zero past the cache
+  for (int inst = wave; inst < 8; inst += 4) {  // 8 loads of 64 lanes cover the 8 KiB
+    const int slot = inst * kWave + lane;
+    const int key = slot >> 3, ch = (slot & 7) ^ (key & 7);
+    const int krow = min(c * kBlock + key, a.Skv - 1);
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const void*>(a.ik + ((long long)b * a.Skv + krow) * kIdxDim + 8 * ch),
+        (__attribute__((address_space(3))) void*)(itile + inst * kWave), 16, 0, 0);
+  }
+}
+
+// (KV head, job) of job j < the block's total, jobs in (head, job) order.
+__device__ __forceinline__ int job_head(const int* lnj, int j, int& q) {
+  int h = 0;
+  while (h < 3 && j >= lnj[h]) {
+    j -= lnj[h];
+    ++h;
+  }
+  q = j;
+  return h;
+}
+
+// Pass A: the index log-sum-exp, block by block.  Work-group (block, sequence,
+// split); every wave takes jobs of 16 index columns on its own (no barriers
+// after the setup): job q of KV head h is rows q 16/nih .. of h's list, lane
+// column n = (row n / nih, index head h + Hkv (n % nih)).  S^T = iK iQ^T over
+// the block's 64 keys gives, per column, the max and the sum of 2^(s - max)
+// over the keys the row attends, stored per (list entry, index head).
+template <int G>
+__global__ void __launch_bounds__(256) kl_lse_kernel(KlArgs a) {
+  __shared__ u32x4 itile[kBlock * 8];
+  __shared__ int lbeg[4], llen[4], lnj[4];
+  const int c = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int n = lane % 16, g = lane / 16;
+  const int nih = a.nih, rpj = 16 / nih;
+  block_setup(a, b, c, rpj, lbeg, llen, lnj, itile);
+  wait_all_loads();
+  __syncthreads();
+  const int total = lnj[0] + lnj[1] + lnj[2] + lnj[3];
+  const int nsplit = key_splits(total);
+  if (split >= nsplit) return;
+  const int j0 = (int)((long long)split * total / nsplit);
+  const int j1 = (int)((long long)(split + 1) * total / nsplit);
+  const int rr = n / nih, m = n % nih;
+  for (int j = j0 + wave; j < j1; j += 4) {
+    int q;
+    const int h = job_head(lnj, j, q);
+    const int li = q * rpj + rr;  // the column's row: entry li of h's list
+    const bool ok = li < llen[h];
+    const int t = ok ? a.lists[lbeg[h] + li] : 0;
+    const int pos = a.q_start + t;
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        a.iq + (((long long)b * a.Sq + t) * kIdxHeads + h + a.Hkv * m) * kIdxDim);
+    bf16x8 iqf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 v = {0, 0, 0, 0};
+      if (ok) v = src[4 * ks + g];
+      iqf[ks] = as_bf16x8(v);
+    }
+    f32x4 si[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      si[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        si[mt] = mfma16(as_bf16x8(itile[islot(16 * mt + n, 4 * ks + g)]), iqf[ks], si[mt]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = c * kBlock + 16 * mt + 4 * g + r;
+        si[mt][r] = (ok && key <= pos) ? si[mt][r] * kLog2eB : -__builtin_huge_valf();
+      }
+    const float mx = wave_max_xor16_32(max16(si));
+    float l = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) l += si[mt][r] != -__builtin_huge_valf() ? exp2f(si[mt][r] - mx) : 0.f;
+    l = wave_sum_xor16_32(l);
+    if (ok && g == 0) a.part_ml[(long long)(lbeg[h] + li) * nih + m] = f32x2{mx, l};
+  }
+}
+
+// The index log-sum-exp of every (row, index head): its entries' block
+// partials combined in slot order.  One thread per (sequence, index head, row).
+__global__ void __launch_bounds__(256) kl_lse_merge_kernel(KlArgs a) {
+  const long long x = (long long)blockIdx.x * 256 + threadIdx.x;  // (b * 4 + i) * Sq + t
+  if (x >= (long long)a.B * kIdxHeads * a.Sq) return;
+  const int t = (int)(x % a.Sq);
+  const long long bi = x / a.Sq;
+  const int i = (int)(bi % kIdxHeads), b = (int)(bi / kIdxHeads);
+  const int h = i % a.Hkv, m = i / a.Hkv;
+  const int32_t* sp = a.slotpos + (((long long)b * a.Hkv + h) * a.Sq + t) * a.top_k;
+  float M = -__builtin_huge_valf(), L = 0.f;
+  for (int s = 0; s < a.top_k; ++s) {
+    const int e = sp[s];
+    if (e < 0) continue;
+    const f32x2 v = a.part_ml[(long long)e * a.nih + m];
+    if (!(v[1] > 0.f)) continue;
+    if (v[0] > M) {
+      L = L * exp2f(M - v[0]) + v[1];
+      M = v[0];
+    } else {
+      L += v[1] * exp2f(v[0] - M);
+    }
+  }
+  a.lse_idx[x] = L > 0.f ? M + __log2f(L) : -__builtin_huge_valf();
+}
+
+// Pass B.  Work-group (block, sequence, split), 4 waves; jobs are chunks of
+// R = 64/G rows of one KV head's list (64 main-branch columns).  Per chunk:
+//   S^T part: wave w takes main columns 16w .. 16w+15 (rows w 16/G + n/G,
+//     query head n % G) over the block's 64 keys: S^T = K Q^T with K in LDS
+//     (reloaded when the head changes) and Q straight into registers; P per
+//     head from the forward's log-sum-exp, averaged over the row's G-lane
+//     segment (DPP); lane e < nih of a segment is the index column (row,
+//     index head h + Hkv e): its scores S^T = iK iQ^T, Q = 2^(s - lse),
+//     C = Q - P, and over the block's keys the loss partial sum P (log P -
+//     log Q) and the diq partial sum C ik (one MFMA product over the index-key
+//     tile), stored per (list entry, index head).  P goes to an LDS table.
+//   key part: wave w takes keys 16w .. 16w+15 over the chunk's index columns
+//     (their queries staged in LDS by LDS-bound loads, the next chunk's while
+//     one is computed): the same scores with keys on N, C from the table, and
+//     dik^T += iq^T C^T.
+// Split s of a block with n splits takes jobs [s total / n, (s+1) total / n);
+// with one split it writes dik itself, with more each writes its partial and
+// kl_dik_merge_kernel adds them in split order (deterministic).
+template <int G>
+__global__ void __launch_bounds__(256) kl_key_kernel(KlArgs a) {
+  constexpr int R = 64 / G, RPG = 16 / G;
+  __shared__ u32x4 ktile[kBlock * 16];   // the block's K for the current KV head, swz_slot layout
+  __shared__ u32x4 itile[kBlock * 8];    // the block's index keys, islot layout
+  __shared__ u32x4 iqtile[2][32 * 8];    // a chunk's index-query columns, islot layout
+  __shared__ float ilse[2][32];
+  __shared__ int ipos[2][32];
+  __shared__ float ptab[16][kBlock + 1]; // P of the chunk's rows x the block's keys
+  __shared__ int lbeg[4], llen[4], lnch[4];
+  const int c = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int n = lane % 16, g = lane / 16;
+  const int nih = a.nih, NI = R * nih;
+  const int key0 = c * kBlock + 16 * wave;
+  const int nkeys = max(0, min(16, a.Skv - key0));
+  const int key = key0 + n;
+  block_setup(a, b, c, R, lbeg, llen, lnch, itile);
+  // index-key operand of the key part (N = the wave's keys), zero past the cache
   bf16x8 ikf[2];
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(a.ik + ((long long)b * a.Skv + min(key, a.Skv - 1)) * kIdxDim);
@@ -401,138 +318,162 @@ __global__ void __launch_bounds__(256) kl_key_kernel(KlArgs a) {
   f32x4 dka[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) dka[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  wait_all_loads();
   __syncthreads();
   const int total = lnch[0] + lnch[1] + lnch[2] + lnch[3];
-  // (KV head, chunk) of job j < total
-  auto head_of = [&](int j, int& chunk) {
-    int h = 0;
-    while (h < 3 && j >= lnch[h]) {
-      j -= lnch[h];
-      ++h;
-    }
-    chunk = j;
-    return h;
-  };
-  // this thread's four 16-byte slots of a main tile (column colt, stored
-  // chunk lane % 16 = dim chunk cht) and one slot of the index tile
-  int colt[4], cht[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    colt[t] = 4 * (4 * wave + t) + lane / 16;
-    cht[t] = (lane & 15) ^ (colt[t] & 15);
-  }
+  const int nsplit = key_splits(total);
+  if (split >= nsplit) return;  // uniform over the work-group
+  const int j0 = (int)((long long)split * total / nsplit);
+  const int j1 = (int)((long long)(split + 1) * total / nsplit);
+  // S^T part: this lane's main column (chunk row rw, query head hd); lanes
+  // hd < nih also carry index column (rw, index head slot hd)
+  const int rw = wave * RPG + n / G, hd = n % G;
+  const bool is_idx = hd < nih;
+  // key part staging: this thread's slot of the index-query tile (column
+  // icol, stored chunk tid % 8 = dim chunk ich) and, for tid < 32, the
+  // metadata of index column tid
   const int icol = tid / 8, ich = (tid & 7) ^ (icol & 7);
-  // the chunk row a metadata thread describes: main column tid, index column tid - 64
-  const int mrr = tid < 64 ? tid / G : min((tid - 64) / nih, R - 1);
+  const int mrow = min((tid & 31) / nih, R - 1);
   // list entry of chunk row rr (rows past the list repeat its first entry;
   // their columns are masked)
   auto row_at = [&](int h, int chunk, int rr) {
     const int e = chunk * R + rr;
     return a.lists[lbeg[h] + (e < llen[h] ? e : 0)];
   };
-  int rt[4], rti = 0, rm = 0;  // rows of the next job to stage
+  int rti = 0, rmi = 0, rsi = 0;  // rows of the next job to stage
   auto fetch_rows = [&](int j) {
     int chunk;
-    const int h = head_of(j, chunk);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) rt[t] = row_at(h, chunk, colt[t] / G);
+    const int h = job_head(lnch, j, chunk);
     rti = row_at(h, chunk, min(icol / nih, R - 1));
-    if (tid < 96) rm = row_at(h, chunk, mrr);
+    rmi = row_at(h, chunk, mrow);
+    rsi = row_at(h, chunk, rw);
   };
-  float ml = 0.f;
-  int mp = -1;
+  // the staged job's S^T-part registers
+  bf16x8 qn[4], iqn[2];
+  float lse2n = 0.f, ilse2n = 0.f, mln = 0.f;
+  int posn = -1, erown = 0, mpn = -1;
+  bool rokn = false;
   auto stage = [&](int j, int buf) {
     int chunk;
-    const int h = head_of(j, chunk);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const long long e = (((long long)b * a.Sq + rt[t]) * a.Hq + h * G + colt[t] % G) * kHeadDim + 8 * cht[t];
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.q + e),
-                                       (__attribute__((address_space(3))) void*)(&qtile[buf][64 * (4 * wave + t)]),
-                                       16, 0, 0);
-    }
+    const int h = job_head(lnch, j, chunk);
     {
-      const long long e = (((long long)b * a.Sq + rti) * kIdxHeads + h + a.Hkv * (icol % nih)) * kIdxDim + 8 * ich;
+      const long long e = (((long long)b * a.Sq + rti) * kIdxHeads + h + a.Hkv * (icol % nih)) *
+                          kIdxDim + 8 * ich;
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.iq + e),
                                        (__attribute__((address_space(3))) void*)(&iqtile[buf][64 * wave]),
                                        16, 0, 0);
     }
-    if (tid < 64) {  // main column tid
-      const bool ok = chunk * R + mrr < llen[h];
-      ml = ok ? a.lse[((long long)b * a.Hq + h * G + tid % G) * a.Sq + rm] * kLog2eB : 0.f;
-      mp = ok ? a.q_start + rm : -1;
-    } else if (tid < 96) {  // index column tid - 64
-      const int ic = tid - 64;
-      const bool ok = ic < NI && chunk * R + ic / nih < llen[h];
-      ml = ok ? a.lse_idx[((long long)b * kIdxHeads + h + a.Hkv * (ic % nih)) * a.Sq + rm] : 0.f;
-      mp = ok ? a.q_start + rm : -1;
+    if (tid < 32) {  // index column tid
+      const bool ok = tid < NI && chunk * R + tid / nih < llen[h];
+      mln = ok ? a.lse_idx[((long long)b * kIdxHeads + h + a.Hkv * (tid % nih)) * a.Sq + rmi] : 0.f;
+      mpn = ok ? a.q_start + rmi : -1;
     }
+    rokn = chunk * R + rw < llen[h];
+    const long long bt = (long long)b * a.Sq + rsi;
+    const u32x4* qs = reinterpret_cast<const u32x4*>(a.q + (bt * a.Hq + h * G + hd) * kHeadDim);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 v = {0, 0, 0, 0};
+      if (rokn) v = qs[4 * ks + g];
+      qn[ks] = as_bf16x8(v);
+    }
+    const u32x4* is = reinterpret_cast<const u32x4*>(
+        a.iq + (bt * kIdxHeads + h + a.Hkv * (is_idx ? hd : 0)) * kIdxDim);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 v = {0, 0, 0, 0};
+      if (rokn && is_idx) v = is[4 * ks + g];
+      iqn[ks] = as_bf16x8(v);
+    }
+    lse2n = rokn ? a.lse[((long long)b * a.Hq + h * G + hd) * a.Sq + rsi] * kLog2eB : 0.f;
+    ilse2n = (rokn && is_idx)
+                 ? a.lse_idx[((long long)b * kIdxHeads + h + a.Hkv * hd) * a.Sq + rsi] : 0.f;
+    posn = rokn ? a.q_start + rsi : -1;
+    erown = lbeg[h] + chunk * R + rw;
   };
-  bf16x8 kf[4];  // main-branch K operand of the wave's keys for the current head
-  int kf_head = -1;
-  const int nsplit = key_splits(total), split = blockIdx.z;
-  if (split >= nsplit) return;  // uniform over the work-group
-  const int j0 = (int)((long long)split * total / nsplit);
-  const int j1 = (int)((long long)(split + 1) * total / nsplit);
+  int k_head = -1;
   if (j0 < j1) {
     fetch_rows(j0);
     stage(j0, 0);
     if (j0 + 1 < j1) fetch_rows(j0 + 1);
   }
+  const float invG = 1.f / (float)G;
   for (int j = j0; j < j1; ++j) {
     const int buf = (j - j0) & 1;
     int chunk;
-    const int h = head_of(j, chunk);
-    if (h != kf_head) {  // uniform; loads complete at the wait below
-      const u32x4* ks = reinterpret_cast<const u32x4*>(
-          a.k + (((long long)b * a.Hkv + h) * a.Skv + min(key, a.Skv - 1)) * kHeadDim);
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        u32x4 v = {0, 0, 0, 0};
-        if (n < nkeys) v = ks[4 * s4 + g];
-        kf[s4] = as_bf16x8(v);
+    const int h = job_head(lnch, j, chunk);
+    if (h != k_head) {  // uniform: the block's K for this KV head (the last
+                        // iteration's barrier ended every read of the old one)
+      const long long koff = (((long long)b * a.Hkv + h) * a.Skv + (long long)c * kBlock) * kHeadDim;
+      for (int inst = wave; inst < 16; inst += 4) {
+        const int slot = inst * kWave + lane;
+        const int kk = slot >> 4, ch = (slot & 15) ^ (kk & 15);
+        const int krow = min(c * kBlock + kk, a.Skv - 1) - c * kBlock;
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(a.k + koff + (long long)krow * kHeadDim + 8 * ch),
+            (__attribute__((address_space(3))) void*)(ktile + inst * kWave), 16, 0, 0);
       }
-      kf_head = h;
+      k_head = h;
     }
-    wait_all_loads();  // job j's tiles and metadata values, job j + 1's rows
-    if (tid < 64) {
-      clse[buf][tid] = ml;
-      cpos[buf][tid] = mp;
-    } else if (tid < 96) {
-      ilse[buf][tid - 64] = ml;
-      ipos[buf][tid - 64] = mp;
+    wait_all_loads();  // job j's tile, registers and metadata; the K tile; job j + 1's rows
+    if (tid < 32) {
+      ilse[buf][tid] = mln;
+      ipos[buf][tid] = mpn;
     }
+    bf16x8 qf[4], iqf[2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = qn[ks];
+    iqf[0] = iqn[0];
+    iqf[1] = iqn[1];
+    const float lse2 = lse2n, ilse2 = ilse2n;
+    const int pos = posn, erow = erown;
+    const bool rok = rokn;
     __syncthreads();
     if (j + 1 < j1) {
       stage(j + 1, buf ^ 1);
       if (j + 2 < j1) fetch_rows(j + 2);
     }
-    // X = Q K^T: M = main columns (16mt + 4g + r), N = the wave's keys
-    f32x4 x[4];
+    // ---- S^T part
+    f32x4 sv[4], si[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      x[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sv[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      si[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        x[mt] = mfma16(as_bf16x8(qtile[buf][swz_slot(16 * mt + n, 4 * ks + g)]), kf[ks], x[mt]);
-    }
-    // P per row: the G columns of chunk row (16mt + 4g) / G are 16mt + 4g' + r
-    // over the G / 4 lanes g' that share it
+        sv[mt] = mfma16(as_bf16x8(ktile[swz_slot(16 * mt + n, 4 * ks + g)]), qf[ks], sv[mt]);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      float sum = 0.f;
+      for (int ks = 0; ks < 2; ++ks)
+        si[mt] = mfma16(as_bf16x8(itile[islot(16 * mt + n, 4 * ks + g)]), iqf[ks], si[mt]);
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int col = 16 * mt + 4 * g + r;
-        sum += (n < nkeys && key <= cpos[buf][col])
-                   ? exp2f(x[mt][r] * a.scale_log2 - clse[buf][col]) : 0.f;
+        const int kl = 16 * mt + 4 * g + r;
+        const bool att = rok && c * kBlock + kl <= pos;
+        const float p = att ? exp2f(sv[mt][r] * a.scale_log2 - lse2) : 0.f;
+        const float pr = segment_sum<G>(p) * invG;
+        if (hd == 0) ptab[rw][kl] = pr;
+        const float s2 = si[mt][r] * kLog2eB;
+        const bool ci = att && is_idx;
+        si[mt][r] = ci ? exp2f(s2 - ilse2) - pr : 0.f;  // C = Q - P
+        if (ci && pr > 0.f) lsum += pr * (__log2f(pr) - s2 + ilse2);
       }
+    lsum = wave_sum_xor16_32(lsum);
+    f32x4 aq[4];
 #pragma unroll
-      for (int o = 16; o < 4 * G; o <<= 1) sum += __shfl_xor(sum, o);
-      ptab[wave][(16 * mt + 4 * g) / G][n] = sum * (1.f / (float)G);
+    for (int i = 0; i < 4; ++i) aq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    pv_idx<2>(si, itile, aq);  // sum over the block's keys of C ik
+    if (is_idx && rok) {
+      float* dst = a.part_q + ((long long)erow * nih + hd) * kIdxDim;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * g) = aq[mt];
+      if (g == 0) a.part_l[(long long)erow * nih + hd] = kLn2 * lsum;
     }
-    __builtin_amdgcn_wave_barrier();
-    // index scores of the chunk's index columns: M = index columns, N = keys
+    __syncthreads();  // the P table is complete
+    // ---- key part: M = the chunk's index columns, N = the wave's keys
     f32x4 xi[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -543,18 +484,17 @@ __global__ void __launch_bounds__(256) kl_key_kernel(KlArgs a) {
           xi[mt] = mfma16(as_bf16x8(iqtile[buf][islot(16 * mt + n, 4 * ks + g)]), ikf[ks], xi[mt]);
       }
     }
-    // C = Q - P at the attended (column, key) pairs
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int ic = 16 * mt + 4 * g + r;
         const bool ok = n < nkeys && key <= ipos[buf][ic];
-        const float pv = ptab[wave][min(ic / nih, 15)][n];
+        const float pv = ptab[min(ic / nih, 15)][16 * wave + n];
         xi[mt][r] = ok ? exp2f(xi[mt][r] * kLog2eB - ilse[buf][ic]) - pv : 0.f;
       }
     pv_idx<1>(xi, iqtile[buf], dka);  // dik^T += iq^T C^T
-    __syncthreads();                  // buffers buf free for job j + 2
+    __syncthreads();                  // buffers buf and the P table free
   }
   if (n < nkeys) {
     float* dst = nsplit == 1
@@ -564,6 +504,29 @@ __global__ void __launch_bounds__(256) kl_key_kernel(KlArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * g) = dka[mt];
   }
+}
+
+// loss and diq of every (row, index head): its entries' block partials added
+// in slot order.  One wave per (sequence, row, index head), lane = dim.
+__global__ void __launch_bounds__(256) kl_merge_kernel(KlArgs a) {
+  const long long w = (long long)blockIdx.x * 4 + threadIdx.x / kWave;  // (b * Sq + t) * 4 + i
+  const int lane = threadIdx.x % kWave;
+  if (w >= (long long)a.B * a.Sq * kIdxHeads) return;
+  const int i = (int)(w % kIdxHeads);
+  const long long bt = w / kIdxHeads;
+  const int t = (int)(bt % a.Sq), b = (int)(bt / a.Sq);
+  const int h = i % a.Hkv, m = i / a.Hkv;
+  const int32_t* sp = a.slotpos + (((long long)b * a.Hkv + h) * a.Sq + t) * a.top_k;
+  float acc = 0.f, ls = 0.f;
+  for (int s = 0; s < a.top_k; ++s) {
+    const int e = sp[s];
+    if (e < 0) continue;
+    const long long pe = (long long)e * a.nih + m;
+    acc += a.part_q[pe * kIdxDim + lane];
+    ls += a.part_l[pe];
+  }
+  a.diq[w * kIdxDim + lane] = acc;
+  if (lane == 0) a.loss[w] = ls;
 }
 
 // dik of the blocks whose list was split: the splits' partials added in split
@@ -603,24 +566,27 @@ bool index_kl_supported(const Shape& s) {
   return (s.G == 4 || s.G == 8 || s.G == 16) && (16 / s.G) * nih <= 8 && s.bs == kBlock;
 }
 
+// Workspace: the index log-sum-exp, the dik split partials, the entries' list
+// positions, the per-entry partials (entries <= B Hkv Sq k, and Hkv nih = 4),
+// then the inverse lists.
 size_t index_kl_workspace_bytes(const Shape& s) {
-  return (size_t)s.B * kIdxHeads * s.Sq * 4 + 256 +                       // index log-sum-exp
-         (size_t)s.B * s.nblk * kKeySplits * kBlock * kIdxDim * 4 + 256 +  // dik split partials
-         inverse_lists_bytes(s);
+  const size_t ent = (size_t)s.B * kIdxHeads * s.Sq * s.top_k;  // (entry, index head) pairs
+  return (size_t)s.B * kIdxHeads * s.Sq * 4 + 256 +
+         (size_t)s.B * s.nblk * kKeySplits * kBlock * kIdxDim * 4 + 256 +
+         (size_t)s.B * s.Hkv * s.Sq * s.top_k * 4 + 256 +
+         ent * 8 + 256 + ent * kIdxDim * 4 + 256 + ent * 4 + 256 + inverse_lists_bytes(s);
 }
 
 namespace {
 template <int G>
 hipError_t launch_kl(const Shape& s, const KlArgs& a, hipStream_t st) {
-  const size_t lds = (size_t)3 * 1024 * 16 + (size_t)s.nblk * 4;
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kl_row_kernel<G>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  constexpr int waves = G / 2;  // G row groups, two per wave
-  kl_row_kernel<G><<<dim3(ceil_div(s.Sq, kKlTileRows), s.Hkv, s.B), waves * kWave, lds, st>>>(a);
-  kl_key_kernel<G><<<dim3(s.nblk, s.B, kKeySplits), 256, 0, st>>>(a);
+  const dim3 blocks(s.nblk, s.B, kKeySplits);
+  kl_lse_kernel<G><<<blocks, 256, 0, st>>>(a);
+  const long long rows = (long long)s.B * kIdxHeads * s.Sq;
+  kl_lse_merge_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, st>>>(a);
+  kl_key_kernel<G><<<blocks, 256, 0, st>>>(a);
   kl_dik_merge_kernel<<<dim3(s.nblk, s.B), 256, 0, st>>>(a);
+  kl_merge_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 }  // namespace
@@ -630,19 +596,29 @@ hipError_t launch_index_kl_backward(const Shape& s, const void* q, const void* k
                                     float* loss, float* diq, float* dik, void* ws,
                                     hipStream_t st) {
   if (!index_kl_supported(s)) return hipErrorInvalidValue;
+  const size_t ent = (size_t)s.B * kIdxHeads * s.Sq * s.top_k;
   char* p = align256(static_cast<char*>(ws));
   float* lse_idx = reinterpret_cast<float*>(p);
   p = align256(p + (size_t)s.B * kIdxHeads * s.Sq * 4);
   float* dikp = reinterpret_cast<float*>(p);
-  p += (size_t)s.B * s.nblk * kKeySplits * kBlock * kIdxDim * 4;
+  p = align256(p + (size_t)s.B * s.nblk * kKeySplits * kBlock * kIdxDim * 4);
+  int32_t* slotpos = reinterpret_cast<int32_t*>(p);
+  p = align256(p + (size_t)s.B * s.Hkv * s.Sq * s.top_k * 4);
+  f32x2* part_ml = reinterpret_cast<f32x2*>(p);
+  p = align256(p + ent * 8);
+  float* part_q = reinterpret_cast<float*>(p);
+  p = align256(p + ent * kIdxDim * 4);
+  float* part_l = reinterpret_cast<float*>(p);
+  p = align256(p + ent * 4);
   const int32_t* base = nullptr;
   const int32_t* lists = nullptr;
-  hipError_t e = launch_inverse_lists(s, sel, p, &base, &lists, st);
+  hipError_t e = launch_inverse_lists(s, sel, p, &base, &lists, st, slotpos);
   if (e != hipSuccess) return e;
   KlArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
            static_cast<const uint16_t*>(iq), static_cast<const uint16_t*>(ik), sel, lse, loss,
-           diq, dik, lse_idx, dikp, base, lists, s.B, s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.G,
-           s.top_k, s.nblk, kIdxHeads / s.Hkv, s.scale * kLog2eB};
+           diq, dik, lse_idx, dikp, slotpos, part_ml, part_q, part_l, base, lists, s.B, s.Sq,
+           s.Skv, s.q_start, s.Hq, s.Hkv, s.G, s.top_k, s.nblk, kIdxHeads / s.Hkv,
+           s.scale * kLog2eB};
   switch (s.G) {
     case 4: return launch_kl<4>(s, a, st);
     case 8: return launch_kl<8>(s, a, st);

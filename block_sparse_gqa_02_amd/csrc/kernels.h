@@ -66,10 +66,13 @@ hipError_t launch_sparse_attn_backward(const Shape& s, const void* q, const void
                                        hipStream_t st);
 // The rows that selected each (sequence, KV head, block), ascending, built
 // from sel [B][Hkv][Sq][top_k] in ws (inverse_lists_bytes(s) bytes): list
-// starts base[(b * Hkv + h) * nblk + c] (then the total) into lists.
+// starts base[(b * Hkv + h) * nblk + c] (then the total) into lists.  With
+// slotpos ([B][Hkv][Sq][top_k]), also the list position of every selection
+// entry (-1 where the entry attends nothing).
 size_t inverse_lists_bytes(const Shape& s);
 hipError_t launch_inverse_lists(const Shape& s, const int32_t* sel, void* ws,
-                                const int32_t** base, const int32_t** lists, hipStream_t st);
+                                const int32_t** base, const int32_t** lists, hipStream_t st,
+                                int32_t* slotpos = nullptr);
 
 // Index-branch KL gradient (prefill): loss [B][Sq][4], diq [B][Sq][4][64],
 // dik [B][Skv][64] in fp32 from q, k, iq, ik (bf16), the selection and the
