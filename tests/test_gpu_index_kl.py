@@ -14,9 +14,8 @@ blocks' row lists are split over several work-groups of the key pass.
 Tolerance, from the arithmetic: scores and softmax statistics are fp32 from
 exact bf16 products, so the loss carries only fp32 rounding (max abs error
 <= 1e-3 against losses of order 1).  The gradients' products round their
-weights to bf16 (P and the index softmax numerators in the row pass, Q - P in
-the key pass; unit roundoff 2^-9) and sum in fp32, as the main-branch
-gradient does: max |gpu - ref| <= 2e-2 max |ref| and mean |gpu - ref| <=
+weights C = Q - P to bf16 (unit roundoff 2^-9) and sum in fp32, as the
+main-branch gradient does: max |gpu - ref| <= 2e-2 max |ref| and mean |gpu - ref| <=
 4e-3 mean |ref| per tensor."""
 import numpy as np
 import pytest
