@@ -166,8 +166,8 @@ def test_index_kl_128k_sampled_rows_last_block_and_identities():
     sample against the oracle (compact per-row problems).  dik of every key of
     the last block, which exactly the last 64 rows attend (their own block),
     summed from the oracle over those rows and all KV heads.  And two
-    identities of the whole output, which tie the key pass to the row pass:
-    sum_j dik_j = 0 (each row's Q - P sums to zero) and
+    identities of the whole output, which tie the per-key sums (dik) to the
+    per-row merges (diq): sum_j dik_j = 0 (each row's Q - P sums to zero) and
     sum_j dik_j . ik_j = sum_(t,i) diq_(t,i) . iq_(t,i) (both are the sum of
     (Q_j - P_j) s_j over every attended triple).  Their residuals come from
     the bf16 rounding of the products' weights; a dropped or misplaced term
