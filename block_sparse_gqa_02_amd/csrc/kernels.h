@@ -126,9 +126,6 @@ hipError_t launch_attn_decode(const Shape& s, const void* q, const void* k, cons
                               const int32_t* seq_lens, const int32_t* sel, void* out, float* lse,
                               void* ws, size_t ws_bytes, hipStream_t st,
                               const Paging* pg = nullptr);
-// The library's own decode scratch on the current device (no allocation):
-// its address and size.  hipGetSymbolAddress runs once per device.
-hipError_t decode_scratch(void** ptr, size_t* bytes);
 
 // Token-level selection (block size 1, prefill positions): token scores
 // [B][Hkv][Sq][Skv] (entries j <= pos written), per-KV-head top-k over them,
