@@ -73,6 +73,7 @@ struct KlArgs {
   f32x2* part_ml;          // workspace [entries][nih]: block max and sum (log2 domain)
   float* part_q;           // workspace [entries][nih][64]: diq partials
   float* part_l;           // workspace [entries][nih]: loss partials
+  uint16_t* cbuf;          // workspace [entries][nih][64]: C = Q - P (bf16) per key of the block
   const int32_t* base;     // inverse lists: starts per (sequence, KV head, block), then the total
   const int32_t* lists;    // rows
   int B, Sq, Skv, q_start, Hq, Hkv, G, top_k, nblk, nih;
@@ -236,7 +237,8 @@ __global__ void __launch_bounds__(256) kl_lse_kernel(KlArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) l += si[mt][r] != -__builtin_huge_valf() ? exp2f(si[mt][r] - mx) : 0.f;
+      for (int r = 0; r < 4; ++r)
+        l += si[mt][r] != -__builtin_huge_valf() ? __builtin_amdgcn_exp2f(si[mt][r] - mx) : 0.f;
     l = wave_sum_xor16_32(l);
     if (ok && g == 0) a.part_ml[(long long)(lbeg[h] + li) * nih + m] = f32x2{mx, l};
   }
@@ -268,142 +270,45 @@ __global__ void __launch_bounds__(256) kl_lse_merge_kernel(KlArgs a) {
   a.lse_idx[x] = L > 0.f ? M + __log2f(L) : -__builtin_huge_valf();
 }
 
-// Pass B.  Work-group (block, sequence, split), 4 waves; jobs are chunks of
-// R = 64/G rows of one KV head's list (64 main-branch columns).  Per chunk:
-//   S^T part: wave w takes main columns 16w .. 16w+15 (rows w 16/G + n/G,
-//     query head n % G) over the block's 64 keys: S^T = K Q^T with K in LDS
-//     (reloaded when the head changes) and Q straight into registers; P per
-//     head from the forward's log-sum-exp, averaged over the row's G-lane
-//     segment (DPP); lane e < nih of a segment is the index column (row,
-//     index head h + Hkv e): its scores S^T = iK iQ^T, Q = 2^(s - lse),
-//     C = Q - P, and over the block's keys the loss partial sum P (log P -
-//     log Q) and the diq partial sum C ik (one MFMA product over the index-key
-//     tile), stored per (list entry, index head).  P goes to an LDS table.
-//   key part: wave w takes keys 16w .. 16w+15 over the chunk's index columns
-//     (their queries staged in LDS by LDS-bound loads, the next chunk's while
-//     one is computed): the same scores with keys on N, C from the table, and
-//     dik^T += iq^T C^T.
-// Split s of a block with n splits takes jobs [s total / n, (s+1) total / n);
-// with one split it writes dik itself, with more each writes its partial and
-// kl_dik_merge_kernel adds them in split order (deterministic).
+// Pass B1: everything a (list entry, index head) needs from one block.
+// Work-group (block, sequence, split); the block's K for one KV head at a time
+// and its index keys sit in LDS, and every wave takes jobs of 16 main-branch
+// columns on its own: job q of KV head h is rows q 16/G .. of h's list, lane
+// column n = (row n / G, query head n % G).  S^T = K Q^T over the block's 64
+// keys with Q straight into registers; P per head from the forward's
+// log-sum-exp, averaged over the row's G-lane segment (DPP); lane e < nih of
+// a segment is also the index column (row, index head h + Hkv e): its scores
+// S^T = iK iQ^T, Q = 2^(s - lse), C = Q - P (rounded to bf16), and over the
+// block's keys the loss partial sum P (log P - log Q) and the diq partial
+// sum C ik (one MFMA product over the index-key tile).  C itself is stored
+// for the dik pass.
 template <int G>
-__global__ void __launch_bounds__(256) kl_key_kernel(KlArgs a) {
-  constexpr int R = 64 / G, RPG = 16 / G;
-  __shared__ u32x4 ktile[kBlock * 16];   // the block's K for the current KV head, swz_slot layout
-  __shared__ u32x4 itile[kBlock * 8];    // the block's index keys, islot layout
-  __shared__ u32x4 iqtile[2][32 * 8];    // a chunk's index-query columns, islot layout
-  __shared__ float ilse[2][32];
-  __shared__ int ipos[2][32];
-  __shared__ float ptab[16][kBlock + 1]; // P of the chunk's rows x the block's keys
-  __shared__ int lbeg[4], llen[4], lnch[4];
+__global__ void __launch_bounds__(256) kl_entry_kernel(KlArgs a) {
+  constexpr int RPG = 16 / G;
+  __shared__ u32x4 ktile[kBlock * 16];  // the block's K for the current KV head, swz_slot layout
+  __shared__ u32x4 itile[kBlock * 8];   // the block's index keys, islot layout
+  __shared__ int lbeg[4], llen[4], lnj[4];
   const int c = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n = lane % 16, g = lane / 16;
-  const int nih = a.nih, NI = R * nih;
-  const int key0 = c * kBlock + 16 * wave;
-  const int nkeys = max(0, min(16, a.Skv - key0));
-  const int key = key0 + n;
-  block_setup(a, b, c, R, lbeg, llen, lnch, itile);
-  // index-key operand of the key part (N = the wave's keys), zero past the cache
-  bf16x8 ikf[2];
-  {
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.ik + ((long long)b * a.Skv + min(key, a.Skv - 1)) * kIdxDim);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 v = {0, 0, 0, 0};
-      if (n < nkeys) v = src[4 * ks + g];
-      ikf[ks] = as_bf16x8(v);
-    }
-  }
-  f32x4 dka[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dka[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nih = a.nih;
+  block_setup(a, b, c, RPG, lbeg, llen, lnj, itile);
   wait_all_loads();
   __syncthreads();
-  const int total = lnch[0] + lnch[1] + lnch[2] + lnch[3];
+  const int total = lnj[0] + lnj[1] + lnj[2] + lnj[3];
   const int nsplit = key_splits(total);
-  if (split >= nsplit) return;  // uniform over the work-group
+  if (split >= nsplit) return;
   const int j0 = (int)((long long)split * total / nsplit);
   const int j1 = (int)((long long)(split + 1) * total / nsplit);
-  // S^T part: this lane's main column (chunk row rw, query head hd); lanes
-  // hd < nih also carry index column (rw, index head slot hd)
-  const int rw = wave * RPG + n / G, hd = n % G;
+  const int rl = n / G, hd = n % G;
   const bool is_idx = hd < nih;
-  // key part staging: this thread's slot of the index-query tile (column
-  // icol, stored chunk tid % 8 = dim chunk ich) and, for tid < 32, the
-  // metadata of index column tid
-  const int icol = tid / 8, ich = (tid & 7) ^ (icol & 7);
-  const int mrow = min((tid & 31) / nih, R - 1);
-  // list entry of chunk row rr (rows past the list repeat its first entry;
-  // their columns are masked)
-  auto row_at = [&](int h, int chunk, int rr) {
-    const int e = chunk * R + rr;
-    return a.lists[lbeg[h] + (e < llen[h] ? e : 0)];
-  };
-  int rti = 0, rmi = 0, rsi = 0;  // rows of the next job to stage
-  auto fetch_rows = [&](int j) {
-    int chunk;
-    const int h = job_head(lnch, j, chunk);
-    rti = row_at(h, chunk, min(icol / nih, R - 1));
-    rmi = row_at(h, chunk, mrow);
-    rsi = row_at(h, chunk, rw);
-  };
-  // the staged job's S^T-part registers
-  bf16x8 qn[4], iqn[2];
-  float lse2n = 0.f, ilse2n = 0.f, mln = 0.f;
-  int posn = -1, erown = 0, mpn = -1;
-  bool rokn = false;
-  auto stage = [&](int j, int buf) {
-    int chunk;
-    const int h = job_head(lnch, j, chunk);
-    {
-      const long long e = (((long long)b * a.Sq + rti) * kIdxHeads + h + a.Hkv * (icol % nih)) *
-                          kIdxDim + 8 * ich;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.iq + e),
-                                       (__attribute__((address_space(3))) void*)(&iqtile[buf][64 * wave]),
-                                       16, 0, 0);
-    }
-    if (tid < 32) {  // index column tid
-      const bool ok = tid < NI && chunk * R + tid / nih < llen[h];
-      mln = ok ? a.lse_idx[((long long)b * kIdxHeads + h + a.Hkv * (tid % nih)) * a.Sq + rmi] : 0.f;
-      mpn = ok ? a.q_start + rmi : -1;
-    }
-    rokn = chunk * R + rw < llen[h];
-    const long long bt = (long long)b * a.Sq + rsi;
-    const u32x4* qs = reinterpret_cast<const u32x4*>(a.q + (bt * a.Hq + h * G + hd) * kHeadDim);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 v = {0, 0, 0, 0};
-      if (rokn) v = qs[4 * ks + g];
-      qn[ks] = as_bf16x8(v);
-    }
-    const u32x4* is = reinterpret_cast<const u32x4*>(
-        a.iq + (bt * kIdxHeads + h + a.Hkv * (is_idx ? hd : 0)) * kIdxDim);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 v = {0, 0, 0, 0};
-      if (rokn && is_idx) v = is[4 * ks + g];
-      iqn[ks] = as_bf16x8(v);
-    }
-    lse2n = rokn ? a.lse[((long long)b * a.Hq + h * G + hd) * a.Sq + rsi] * kLog2eB : 0.f;
-    ilse2n = (rokn && is_idx)
-                 ? a.lse_idx[((long long)b * kIdxHeads + h + a.Hkv * hd) * a.Sq + rsi] : 0.f;
-    posn = rokn ? a.q_start + rsi : -1;
-    erown = lbeg[h] + chunk * R + rw;
-  };
-  int k_head = -1;
-  if (j0 < j1) {
-    fetch_rows(j0);
-    stage(j0, 0);
-    if (j0 + 1 < j1) fetch_rows(j0 + 1);
-  }
   const float invG = 1.f / (float)G;
-  for (int j = j0; j < j1; ++j) {
-    const int buf = (j - j0) & 1;
-    int chunk;
-    const int h = job_head(lnch, j, chunk);
-    if (h != k_head) {  // uniform: the block's K for this KV head (the last
-                        // iteration's barrier ended every read of the old one)
+  int hstart = 0;  // first job of KV head h
+  for (int h = 0; h < a.Hkv; hstart += lnj[h], ++h) {
+    const int hj0 = max(j0, hstart), hj1 = min(j1, hstart + lnj[h]);
+    if (hj0 >= hj1) continue;  // uniform over the work-group
+    __syncthreads();           // every read of the previous head's K is done
+    {
       const long long koff = (((long long)b * a.Hkv + h) * a.Skv + (long long)c * kBlock) * kHeadDim;
       for (int inst = wave; inst < 16; inst += 4) {
         const int slot = inst * kWave + lane;
@@ -413,96 +318,236 @@ __global__ void __launch_bounds__(256) kl_key_kernel(KlArgs a) {
             reinterpret_cast<const void*>(a.k + koff + (long long)krow * kHeadDim + 8 * ch),
             (__attribute__((address_space(3))) void*)(ktile + inst * kWave), 16, 0, 0);
       }
-      k_head = h;
     }
-    wait_all_loads();  // job j's tile, registers and metadata; the K tile; job j + 1's rows
-    if (tid < 32) {
-      ilse[buf][tid] = mln;
-      ipos[buf][tid] = mpn;
-    }
-    bf16x8 qf[4], iqf[2];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = qn[ks];
-    iqf[0] = iqn[0];
-    iqf[1] = iqn[1];
-    const float lse2 = lse2n, ilse2 = ilse2n;
-    const int pos = posn, erow = erown;
-    const bool rok = rokn;
+    wait_all_loads();
     __syncthreads();
-    if (j + 1 < j1) {
-      stage(j + 1, buf ^ 1);
-      if (j + 2 < j1) fetch_rows(j + 2);
-    }
-    // ---- S^T part
-    f32x4 sv[4], si[4];
+    // Jobs hj0 + wave, + 4, ...: the next job's operands load while one is
+    // computed, and the list entry of the job after that one step earlier.
+    auto entry_of = [&](int j, int& li) {
+      li = (j - hstart) * RPG + rl;  // the column's row: entry li of h's list
+      return li < llen[h] ? a.lists[lbeg[h] + li] : -1;
+    };
+    bf16x8 qn[4], iqn[2];
+    float lse2n = 0.f, ilse2n = 0.f;
+    int tn = -1, lin = 0, tnn = -1, linn = 0;
+    auto load_job = [&](int t) {
+      const bool ok = t >= 0;
+      const long long bt = (long long)b * a.Sq + (ok ? t : 0);
+      const u32x4* qs = reinterpret_cast<const u32x4*>(a.q + (bt * a.Hq + h * G + hd) * kHeadDim);
+      const u32x4* is = reinterpret_cast<const u32x4*>(
+          a.iq + (bt * kIdxHeads + h + a.Hkv * (is_idx ? hd : 0)) * kIdxDim);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      sv[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      si[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        sv[mt] = mfma16(as_bf16x8(ktile[swz_slot(16 * mt + n, 4 * ks + g)]), qf[ks], sv[mt]);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        si[mt] = mfma16(as_bf16x8(itile[islot(16 * mt + n, 4 * ks + g)]), iqf[ks], si[mt]);
-    }
-    float lsum = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kl = 16 * mt + 4 * g + r;
-        const bool att = rok && c * kBlock + kl <= pos;
-        const float p = att ? exp2f(sv[mt][r] * a.scale_log2 - lse2) : 0.f;
-        const float pr = segment_sum<G>(p) * invG;
-        if (hd == 0) ptab[rw][kl] = pr;
-        const float s2 = si[mt][r] * kLog2eB;
-        const bool ci = att && is_idx;
-        si[mt][r] = ci ? exp2f(s2 - ilse2) - pr : 0.f;  // C = Q - P
-        if (ci && pr > 0.f) lsum += pr * (__log2f(pr) - s2 + ilse2);
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4 v = {0, 0, 0, 0};
+        if (ok) v = qs[4 * ks + g];
+        qn[ks] = as_bf16x8(v);
       }
-    lsum = wave_sum_xor16_32(lsum);
-    f32x4 aq[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) aq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    pv_idx<2>(si, itile, aq);  // sum over the block's keys of C ik
-    if (is_idx && rok) {
-      float* dst = a.part_q + ((long long)erow * nih + hd) * kIdxDim;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * g) = aq[mt];
-      if (g == 0) a.part_l[(long long)erow * nih + hd] = kLn2 * lsum;
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4 v = {0, 0, 0, 0};
+        if (ok && is_idx) v = is[4 * ks + g];
+        iqn[ks] = as_bf16x8(v);
+      }
+      lse2n = ok ? a.lse[((long long)b * a.Hq + h * G + hd) * a.Sq + t] * kLog2eB : 0.f;
+      ilse2n = (ok && is_idx) ? a.lse_idx[((long long)b * kIdxHeads + h + a.Hkv * hd) * a.Sq + t] : 0.f;
+    };
+    if (hj0 + wave < hj1) {
+      tn = entry_of(hj0 + wave, lin);
+      load_job(tn);
+      if (hj0 + wave + 4 < hj1) tnn = entry_of(hj0 + wave + 4, linn);
     }
-    __syncthreads();  // the P table is complete
-    // ---- key part: M = the chunk's index columns, N = the wave's keys
-    f32x4 xi[2];
+    for (int j = hj0 + wave; j < hj1; j += 4) {
+      const int t = tn, li = lin;
+      const bool ok = t >= 0;
+      const int erow = lbeg[h] + li;
+      const int pos = ok ? a.q_start + t : -1;
+      bf16x8 qf[4], iqf[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      xi[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (16 * mt < NI) {
+      for (int ks = 0; ks < 4; ++ks) qf[ks] = qn[ks];
+      iqf[0] = iqn[0];
+      iqf[1] = iqn[1];
+      const float lse2 = lse2n, ilse2 = ilse2n;
+      if (j + 4 < hj1) {
+        tn = tnn;
+        lin = linn;
+        load_job(tn);
+        if (j + 8 < hj1) tnn = entry_of(j + 8, linn);
+      }
+      f32x4 sv[4], si[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        sv[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        si[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          sv[mt] = mfma16(as_bf16x8(ktile[swz_slot(16 * mt + n, 4 * ks + g)]), qf[ks], sv[mt]);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          xi[mt] = mfma16(as_bf16x8(iqtile[buf][islot(16 * mt + n, 4 * ks + g)]), ikf[ks], xi[mt]);
+          si[mt] = mfma16(as_bf16x8(itile[islot(16 * mt + n, 4 * ks + g)]), iqf[ks], si[mt]);
+      }
+      float lsum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool att = c * kBlock + 16 * mt + 4 * g + r <= pos;
+          // v_exp_f32 / v_log_f32 directly: results below the normal range
+          // flush to zero, and the log term skips P < 1e-30 (each such term
+          // is below 1e-28)
+          const float p = att ? __builtin_amdgcn_exp2f(sv[mt][r] * a.scale_log2 - lse2) : 0.f;
+          const float pr = segment_sum<G>(p) * invG;
+          const float s2 = si[mt][r] * kLog2eB;
+          const bool ci = att && is_idx;
+          si[mt][r] = ci ? __builtin_amdgcn_exp2f(s2 - ilse2) - pr : 0.f;  // C = Q - P
+          if (ci && pr > 1e-30f) lsum += pr * (__builtin_amdgcn_logf(pr) - s2 + ilse2);
+        }
+      lsum = wave_sum_xor16_32(lsum);
+      f32x4 aq[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) aq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pv_idx<2>(si, itile, aq);  // sum over the block's keys of C ik
+      if (ok && is_idx) {
+        const long long pe = (long long)erow * nih + hd;
+        float* dst = a.part_q + pe * kIdxDim;
+        uint16_t* cd = a.cbuf + pe * kBlock;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * g) = aq[mt];
+          u32x2 w2;
+          w2[0] = pack_bf16x2(si[mt][0], si[mt][1]);
+          w2[1] = pack_bf16x2(si[mt][2], si[mt][3]);
+          *reinterpret_cast<u32x2*>(cd + 16 * mt + 4 * g) = w2;  // keys 16mt + 4g .. +3
+        }
+        if (g == 0) a.part_l[pe] = kLn2 * lsum;
       }
     }
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ic = 16 * mt + 4 * g + r;
-        const bool ok = n < nkeys && key <= ipos[buf][ic];
-        const float pv = ptab[min(ic / nih, 15)][16 * wave + n];
-        xi[mt][r] = ok ? exp2f(xi[mt][r] * kLog2eB - ilse[buf][ic]) - pv : 0.f;
-      }
-    pv_idx<1>(xi, iqtile[buf], dka);  // dik^T += iq^T C^T
-    __syncthreads();                  // buffers buf and the P table free
   }
-  if (n < nkeys) {
-    float* dst = nsplit == 1
-                     ? a.dik + ((long long)b * a.Skv + key) * kIdxDim
-                     : a.dikp + ((((long long)b * a.nblk + c) * kKeySplits + split) * kBlock +
-                                 16 * wave + n) * kIdxDim;
+}
+
+constexpr int kDikBatch = 32;  // (entry, index head) pairs per step of the dik pass
+
+// Pass B2: dik.  Work-group (block, sequence, split); every wave covers all
+// 64 keys of the block and runs on its own over batches of 32 (entry, index
+// head) pairs of the block (every KV head's list in order, index heads
+// innermost; batch j to wave j mod 4): the pairs' index queries and their C
+// rows are staged in wave-private LDS tiles by LDS-bound loads (the next
+// batch's while one is computed), and dik^T += iq^T C^T per 16-key tile.
+// The four waves' sums are then added in wave order.  Split s of a block with
+// n splits takes batches [s nb / n, (s+1) nb / n); with one split it writes
+// dik itself, with more each writes its partial and kl_dik_merge_kernel adds
+// them in split order (deterministic).
+__global__ void __launch_bounds__(256) kl_dik_kernel(KlArgs a) {
+  __shared__ u32x4 qt[4][2][kDikBatch * 8];  // per wave: index queries of a batch, islot layout
+  __shared__ u32x4 ct[4][2][kDikBatch * 8];  // per wave: C rows of a batch (32 x 64 bf16)
+  __shared__ int lbeg[4], lnp[4];
+  // the cross-wave sum, in the query tiles' memory once the batches are done
+  float(*red)[kIdxDim + 4] = reinterpret_cast<float(*)[kIdxDim + 4]>(&qt[0][0][0]);
+  static_assert(sizeof(float) * kBlock * (kIdxDim + 4) <= sizeof(u32x4) * 4 * 2 * kDikBatch * 8,
+                "the reduction fits in the query tiles");
+  const int c = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int n = lane % 16, g = lane / 16;
+  const int nih = a.nih;
+  if (tid < 4) {
+    const bool hv = tid < a.Hkv;
+    const long long e = ((long long)b * a.Hkv + (hv ? tid : 0)) * a.nblk + c;
+    const int bg = hv ? a.base[e] : 0;
+    lbeg[tid] = bg;
+    lnp[tid] = hv ? (a.base[e + 1] - bg) * nih : 0;
+  }
+  __syncthreads();
+  const int pairs = lnp[0] + lnp[1] + lnp[2] + lnp[3];
+  const int nb = (pairs + kDikBatch - 1) / kDikBatch;
+  const int nsplit = key_splits(nb);
+  if (split >= nsplit) return;  // uniform over the work-group
+  const int j0 = (int)((long long)split * nb / nsplit);
+  const int j1 = (int)((long long)(split + 1) * nb / nsplit);
+  // pair p of the block: its KV head and its row in cbuf (entry e nih + m)
+  auto pair_at = [&](int p, int& row, int& m) {
+    int h = 0;
+    while (h < 3 && p >= lnp[h]) {
+      p -= lnp[h];
+      ++h;
+    }
+    row = lbeg[h] * nih + p;
+    m = p % nih;
+    return h;
+  };
+  // four loads of 64 lanes per tile: slot = pair x 8 chunks (islot layout)
+  auto stage = [&](int jb, int buf) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * g) = dka[mt];
+    for (int inst = 0; inst < 4; ++inst) {
+      const int slot = inst * kWave + lane;
+      const int pr = slot >> 3, ch = (slot & 7) ^ (pr & 7);
+      const int p = min(jb * kDikBatch + pr, pairs - 1);
+      int row, m;
+      const int h = pair_at(p, row, m);
+      const int t = a.lists[row / nih];
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(a.iq + (((long long)b * a.Sq + t) * kIdxHeads + h + a.Hkv * m) *
+                                                   kIdxDim + 8 * ch),
+          (__attribute__((address_space(3))) void*)(&qt[wave][buf][inst * kWave]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(a.cbuf + (long long)row * kBlock + 8 * ch),
+          (__attribute__((address_space(3))) void*)(&ct[wave][buf][inst * kWave]), 16, 0, 0);
+    }
+  };
+  f32x4 dka[4][4];  // [key tile][dim M-tile]
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dka[kt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (j0 + wave < j1) stage(j0 + wave, 0);
+  int buf = 0;
+  for (int jb = j0 + wave; jb < j1; jb += 4, buf ^= 1) {
+    wait_all_loads();  // batch jb's tiles
+    __builtin_amdgcn_wave_barrier();
+    if (jb + 4 < j1) stage(jb + 4, buf ^ 1);
+    const int nvalid = pairs - jb * kDikBatch;  // pairs past this are padding
+    const uint16_t* cw16 = reinterpret_cast<const uint16_t*>(&ct[wave][buf][0]);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      // register r of cw[mt]: pair 16mt + 4g + r, key 16kt + n (islot chunk of the key)
+      f32x4 cw[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pr = 16 * mt + 4 * g + r, kk = 16 * kt + n;
+          const uint16_t v = cw16[islot(pr, kk >> 3) * 8 + (kk & 7)];
+          cw[mt][r] = pr < nvalid ? __uint_as_float((uint32_t)v << 16) : 0.f;
+        }
+      pv_idx<1>(cw, qt[wave][buf], dka[kt]);
+    }
+  }
+  // the waves' sums, added in wave order (the first barrier also ends every
+  // wave's reads of the tiles); thread = (key, 16-dim quarter)
+  for (int w = 0; w < 4; ++w) {
+    __syncthreads();
+    if (wave == w) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float& dst = red[16 * kt + n][16 * mt + 4 * g + r];
+            dst = (w == 0 ? 0.f : dst) + dka[kt][mt][r];
+          }
+    }
+  }
+  __syncthreads();
+  const int kl = tid / 4, d0 = 16 * (tid % 4);
+  const int key = c * kBlock + kl;
+  if (key < a.Skv) {
+    float* dst = nsplit == 1
+                     ? a.dik + ((long long)b * a.Skv + key) * kIdxDim + d0
+                     : a.dikp + ((((long long)b * a.nblk + c) * kKeySplits + split) * kBlock + kl) *
+                                    kIdxDim + d0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<f32x4*>(dst + 4 * i) =
+          f32x4{red[kl][d0 + 4 * i], red[kl][d0 + 4 * i + 1], red[kl][d0 + 4 * i + 2], red[kl][d0 + 4 * i + 3]};
   }
 }
 
@@ -533,12 +578,12 @@ __global__ void __launch_bounds__(256) kl_merge_kernel(KlArgs a) {
 // order.  Work-group (block, sequence); thread = (key, 16-dim quarter).
 __global__ void __launch_bounds__(256) kl_dik_merge_kernel(KlArgs a) {
   const int c = blockIdx.x, b = blockIdx.y;
-  int total = 0;
+  int pairs = 0;
   for (int h = 0; h < a.Hkv; ++h) {
     const long long e = ((long long)b * a.Hkv + h) * a.nblk + c;
-    total += (a.base[e + 1] - a.base[e] + 64 / a.G - 1) / (64 / a.G);
+    pairs += (a.base[e + 1] - a.base[e]) * a.nih;
   }
-  const int nsplit = key_splits(total);
+  const int nsplit = key_splits((pairs + kDikBatch - 1) / kDikBatch);
   if (nsplit == 1) return;
   const int kl = threadIdx.x / 4, d0 = 16 * (threadIdx.x % 4);
   const int key = c * kBlock + kl;
@@ -574,7 +619,8 @@ size_t index_kl_workspace_bytes(const Shape& s) {
   return (size_t)s.B * kIdxHeads * s.Sq * 4 + 256 +
          (size_t)s.B * s.nblk * kKeySplits * kBlock * kIdxDim * 4 + 256 +
          (size_t)s.B * s.Hkv * s.Sq * s.top_k * 4 + 256 +
-         ent * 8 + 256 + ent * kIdxDim * 4 + 256 + ent * 4 + 256 + inverse_lists_bytes(s);
+         ent * 8 + 256 + ent * kIdxDim * 4 + 256 + ent * 4 + 256 + ent * kBlock * 2 + 256 +
+         inverse_lists_bytes(s);
 }
 
 namespace {
@@ -584,7 +630,8 @@ hipError_t launch_kl(const Shape& s, const KlArgs& a, hipStream_t st) {
   kl_lse_kernel<G><<<blocks, 256, 0, st>>>(a);
   const long long rows = (long long)s.B * kIdxHeads * s.Sq;
   kl_lse_merge_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, st>>>(a);
-  kl_key_kernel<G><<<blocks, 256, 0, st>>>(a);
+  kl_entry_kernel<G><<<blocks, 256, 0, st>>>(a);
+  kl_dik_kernel<<<blocks, 256, 0, st>>>(a);
   kl_dik_merge_kernel<<<dim3(s.nblk, s.B), 256, 0, st>>>(a);
   kl_merge_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(a);
   return hipGetLastError();
@@ -610,13 +657,15 @@ hipError_t launch_index_kl_backward(const Shape& s, const void* q, const void* k
   p = align256(p + ent * kIdxDim * 4);
   float* part_l = reinterpret_cast<float*>(p);
   p = align256(p + ent * 4);
+  uint16_t* cbuf = reinterpret_cast<uint16_t*>(p);
+  p = align256(p + ent * kBlock * 2);
   const int32_t* base = nullptr;
   const int32_t* lists = nullptr;
   hipError_t e = launch_inverse_lists(s, sel, p, &base, &lists, st, slotpos);
   if (e != hipSuccess) return e;
   KlArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
            static_cast<const uint16_t*>(iq), static_cast<const uint16_t*>(ik), sel, lse, loss,
-           diq, dik, lse_idx, dikp, slotpos, part_ml, part_q, part_l, base, lists, s.B, s.Sq,
+           diq, dik, lse_idx, dikp, slotpos, part_ml, part_q, part_l, cbuf, base, lists, s.B, s.Sq,
            s.Skv, s.q_start, s.Hq, s.Hkv, s.G, s.top_k, s.nblk, kIdxHeads / s.Hkv,
            s.scale * kLog2eB};
   switch (s.G) {
