@@ -127,8 +127,7 @@ msa_status check_index_kl(const msa::Shape& s) {
   if (st != MSA_OK) return st;
   if (!msa::index_kl_supported(s))
     return fail(MSA_ERR_UNSUPPORTED,
-                "index KL gradient needs n_q_heads / n_kv_heads in {4, 8, 16} and at most 8 "
-                "(row, index head) pairs per 16 query columns: (16 / G) * (4 / n_kv_heads) <= 8");
+                "index KL gradient needs n_q_heads / n_kv_heads in {4, 8, 16}");
   if ((size_t)3 * 1024 * 16 + (size_t)s.nblk * 4 > 160 * 1024)
     return fail(MSA_ERR_UNSUPPORTED, "index KL gradient needs seq_kv <= 1310720");
   return MSA_OK;

@@ -68,6 +68,7 @@ struct KlArgs {
   float* diq;              // [B][Sq][4][64]
   float* dik;              // [B][Skv][64]
   float* lse_idx;          // workspace [B][4][Sq]: index log-sum-exp, log2 domain
+  float* lse_t;            // workspace [B][Sq][Hq]: the forward's log-sum-exp, log2 domain
   float* dikp;             // workspace [B][nblk][kKeySplits][64][64]: split partials of dik
   const int32_t* slotpos;  // workspace [B][Hkv][Sq][top_k]: list position of an entry, or -1
   f32x2* part_ml;          // workspace [entries][nih]: block max and sum (log2 domain)
@@ -117,19 +118,6 @@ __device__ __forceinline__ void pv_idx(const f32x4 (&w)[2 * KV], const u32x4* ti
       acc[mt] = mfma16(tf, pb, acc[mt]);
     }
   }
-}
-
-// Sum over the G-lane segment of each 16-lane row (G = 4, 8, 16), in every
-// lane of the segment: DPP swaps of neighbours and of pairs (quads), then
-// the half-row mirror (the other quad of 8 lanes) and the row mirror (the
-// other 8 of 16).
-template <int G>
-__device__ __forceinline__ float segment_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-  if (G >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
-  if (G >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
-  return v;
 }
 
 __device__ __forceinline__ float max16(const f32x4 (&v)[4]) {
@@ -270,29 +258,46 @@ __global__ void __launch_bounds__(256) kl_lse_merge_kernel(KlArgs a) {
   a.lse_idx[x] = L > 0.f ? M + __log2f(L) : -__builtin_huge_valf();
 }
 
+// The forward's log-sum-exp in (row, query head) order and the log2 domain,
+// so that a row's heads are one contiguous read.  One thread per element.
+__global__ void __launch_bounds__(256) kl_lse_t_kernel(KlArgs a) {
+  const long long x = (long long)blockIdx.x * 256 + threadIdx.x;  // (b * Sq + t) * Hq + hq
+  if (x >= (long long)a.B * a.Sq * a.Hq) return;
+  const int hq = (int)(x % a.Hq);
+  const long long bt = x / a.Hq;
+  const int t = (int)(bt % a.Sq), b = (int)(bt / a.Sq);
+  a.lse_t[x] = a.lse[((long long)b * a.Hq + hq) * a.Sq + t] * kLog2eB;
+}
+
 // Pass B1: everything a (list entry, index head) needs from one block.
 // Work-group (block, sequence, split); the block's K for one KV head at a time
-// and its index keys sit in LDS, and every wave takes jobs of 16 main-branch
-// columns on its own: job q of KV head h is rows q 16/G .. of h's list, lane
-// column n = (row n / G, query head n % G).  S^T = K Q^T over the block's 64
-// keys with Q straight into registers; P per head from the forward's
-// log-sum-exp, averaged over the row's G-lane segment (DPP); lane e < nih of
-// a segment is also the index column (row, index head h + Hkv e): its scores
-// S^T = iK iQ^T, Q = 2^(s - lse), C = Q - P (rounded to bf16), and over the
-// block's keys the loss partial sum P (log P - log Q) and the diq partial
-// sum C ik (one MFMA product over the index-key tile).  C itself is stored
-// for the dik pass.
+// and its index keys sit in LDS, and every wave takes jobs of 16 rows of a KV
+// head's list on its own, in two phases.
+//  1. The rows' main-branch weights, G column groups of 16/G rows x G query
+//     heads: S = Q K^T with the query heads on the M side, so a lane holds
+//     four heads of one row for one key; P, the mean over the G heads of
+//     2^(s scale - lse), is a sum over the lane's registers plus, for G > 4,
+//     over the lanes of the other 16-lane rows holding the same row.  P of
+//     the 16 rows goes to a wave-private LDS tile.
+//  2. Per index head of the KV head, the 16 rows' index scores S^T = iK iQ^T
+//     (a row per column): Q = 2^(s - lse), C = Q - P (rounded to bf16), over
+//     the block's keys the loss partial sum P (log P - log Q) and the diq
+//     partial sum C ik (one MFMA product over the index-key tile).  C itself
+//     is stored for the dik pass.
 template <int G>
 __global__ void __launch_bounds__(256) kl_entry_kernel(KlArgs a) {
-  constexpr int RPG = 16 / G;
+  constexpr int RPG = 16 / G;  // rows per main-branch column group
+  constexpr int HQ4 = G / 4;   // 16-lane rows that hold the same query row in phase 1
+  constexpr int kJob = 16;     // rows per job
   __shared__ u32x4 ktile[kBlock * 16];  // the block's K for the current KV head, swz_slot layout
   __shared__ u32x4 itile[kBlock * 8];   // the block's index keys, islot layout
+  __shared__ f32x4 ptile[4][kJob][kBlock / 4 + 1];  // per wave: P of the job's rows, (row, key)
   __shared__ int lbeg[4], llen[4], lnj[4];
   const int c = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n = lane % 16, g = lane / 16;
   const int nih = a.nih;
-  block_setup(a, b, c, RPG, lbeg, llen, lnj, itile);
+  block_setup(a, b, c, kJob, lbeg, llen, lnj, itile);
   wait_all_loads();
   __syncthreads();
   const int total = lnj[0] + lnj[1] + lnj[2] + lnj[3];
@@ -300,20 +305,20 @@ __global__ void __launch_bounds__(256) kl_entry_kernel(KlArgs a) {
   if (split >= nsplit) return;
   const int j0 = (int)((long long)split * total / nsplit);
   const int j1 = (int)((long long)(split + 1) * total / nsplit);
-  const int rl = n / G, hd = n % G;
-  const bool is_idx = hd < nih;
   const float invG = 1.f / (float)G;
+  const int key0 = c * kBlock;
+  f32x4* pw = &ptile[wave][0][0];
   int hstart = 0;  // first job of KV head h
   for (int h = 0; h < a.Hkv; hstart += lnj[h], ++h) {
     const int hj0 = max(j0, hstart), hj1 = min(j1, hstart + lnj[h]);
     if (hj0 >= hj1) continue;  // uniform over the work-group
     __syncthreads();           // every read of the previous head's K is done
     {
-      const long long koff = (((long long)b * a.Hkv + h) * a.Skv + (long long)c * kBlock) * kHeadDim;
+      const long long koff = (((long long)b * a.Hkv + h) * a.Skv + (long long)key0) * kHeadDim;
       for (int inst = wave; inst < 16; inst += 4) {
         const int slot = inst * kWave + lane;
         const int kk = slot >> 4, ch = (slot & 15) ^ (kk & 15);
-        const int krow = min(c * kBlock + kk, a.Skv - 1) - c * kBlock;
+        const int krow = min(key0 + kk, a.Skv - 1) - key0;
         __builtin_amdgcn_global_load_lds(
             reinterpret_cast<const void*>(a.k + koff + (long long)krow * kHeadDim + 8 * ch),
             (__attribute__((address_space(3))) void*)(ktile + inst * kWave), 16, 0, 0);
@@ -321,105 +326,149 @@ __global__ void __launch_bounds__(256) kl_entry_kernel(KlArgs a) {
     }
     wait_all_loads();
     __syncthreads();
-    // Jobs hj0 + wave, + 4, ...: the next job's operands load while one is
-    // computed, and the list entry of the job after that one step earlier.
-    auto entry_of = [&](int j, int& li) {
-      li = (j - hstart) * RPG + rl;  // the column's row: entry li of h's list
-      return li < llen[h] ? a.lists[lbeg[h] + li] : -1;
+    const float* lse_h = a.lse_t + h * G + 4 * (g % HQ4);  // + (b Sq + t) Hq: heads of lane's M rows
+    // rows of job j: entries (j - hstart) 16 .. +15 of h's list; lane n < 16
+    // holds the row of entry n (-1 past the list)
+    auto job_rows = [&](int j) {
+      const int li = (j - hstart) * kJob + n;
+      return (lane < 16 && li < llen[h]) ? a.lists[lbeg[h] + li] : -1;
     };
-    bf16x8 qn[4], iqn[2];
-    float lse2n = 0.f, ilse2n = 0.f;
-    int tn = -1, lin = 0, tnn = -1, linn = 0;
-    auto load_job = [&](int t) {
-      const bool ok = t >= 0;
-      const long long bt = (long long)b * a.Sq + (ok ? t : 0);
-      const u32x4* qs = reinterpret_cast<const u32x4*>(a.q + (bt * a.Hq + h * G + hd) * kHeadDim);
-      const u32x4* is = reinterpret_cast<const u32x4*>(
-          a.iq + (bt * kIdxHeads + h + a.Hkv * (is_idx ? hd : 0)) * kIdxDim);
+    // phase-1 operands of column group u: Q of row u RPG + n / G, head n % G
+    // (A operand), and the log2-domain LSE of the lane's four output heads
+    bf16x8 qn[4];
+    f32x4 lsen;
+    auto load_group = [&](int tl, int u) {
+      const int ta = __shfl(tl, u * RPG + n / G);
+      const int to = __shfl(tl, u * RPG + (4 * g) / G);
+      const long long ba = (long long)b * a.Sq + (ta >= 0 ? ta : 0);
+      const u32x4* qs = reinterpret_cast<const u32x4*>(a.q + (ba * a.Hq + h * G + n % G) * kHeadDim);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         u32x4 v = {0, 0, 0, 0};
-        if (ok) v = qs[4 * ks + g];
+        if (ta >= 0) v = qs[4 * ks + g];
         qn[ks] = as_bf16x8(v);
       }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u32x4 v = {0, 0, 0, 0};
-        if (ok && is_idx) v = is[4 * ks + g];
-        iqn[ks] = as_bf16x8(v);
-      }
-      lse2n = ok ? a.lse[((long long)b * a.Hq + h * G + hd) * a.Sq + t] * kLog2eB : 0.f;
-      ilse2n = (ok && is_idx) ? a.lse_idx[((long long)b * kIdxHeads + h + a.Hkv * hd) * a.Sq + t] : 0.f;
+      lsen = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (to >= 0) lsen = *reinterpret_cast<const f32x4*>(lse_h + ((long long)b * a.Sq + to) * a.Hq);
     };
-    if (hj0 + wave < hj1) {
-      tn = entry_of(hj0 + wave, lin);
-      load_job(tn);
-      if (hj0 + wave + 4 < hj1) tnn = entry_of(hj0 + wave + 4, linn);
-    }
+    int tl = hj0 + wave < hj1 ? job_rows(hj0 + wave) : -1;
+    if (hj0 + wave < hj1) load_group(tl, 0);
     for (int j = hj0 + wave; j < hj1; j += 4) {
-      const int t = tn, li = lin;
-      const bool ok = t >= 0;
-      const int erow = lbeg[h] + li;
-      const int pos = ok ? a.q_start + t : -1;
-      bf16x8 qf[4], iqf[2];
+      const int tnext = j + 4 < hj1 ? job_rows(j + 4) : -1;
+      // ---- phase 1: P of the job's 16 rows into the wave's LDS tile
+      for (int u = 0; u < G; ++u) {
+        bf16x8 qf[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qf[ks] = qn[ks];
-      iqf[0] = iqn[0];
-      iqf[1] = iqn[1];
-      const float lse2 = lse2n, ilse2 = ilse2n;
-      if (j + 4 < hj1) {
-        tn = tnn;
-        lin = linn;
-        load_job(tn);
-        if (j + 8 < hj1) tnn = entry_of(j + 8, linn);
-      }
-      f32x4 sv[4], si[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        sv[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        si[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          sv[mt] = mfma16(as_bf16x8(ktile[swz_slot(16 * mt + n, 4 * ks + g)]), qf[ks], sv[mt]);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          si[mt] = mfma16(as_bf16x8(itile[islot(16 * mt + n, 4 * ks + g)]), iqf[ks], si[mt]);
-      }
-      float lsum = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool att = c * kBlock + 16 * mt + 4 * g + r <= pos;
-          // v_exp_f32 / v_log_f32 directly: results below the normal range
-          // flush to zero, and the log term skips P < 1e-30 (each such term
-          // is below 1e-28)
-          const float p = att ? __builtin_amdgcn_exp2f(sv[mt][r] * a.scale_log2 - lse2) : 0.f;
-          const float pr = segment_sum<G>(p) * invG;
-          const float s2 = si[mt][r] * kLog2eB;
-          const bool ci = att && is_idx;
-          si[mt][r] = ci ? __builtin_amdgcn_exp2f(s2 - ilse2) - pr : 0.f;  // C = Q - P
-          if (ci && pr > 1e-30f) lsum += pr * (__builtin_amdgcn_logf(pr) - s2 + ilse2);
-        }
-      lsum = wave_sum_xor16_32(lsum);
-      f32x4 aq[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) aq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      pv_idx<2>(si, itile, aq);  // sum over the block's keys of C ik
-      if (ok && is_idx) {
-        const long long pe = (long long)erow * nih + hd;
-        float* dst = a.part_q + pe * kIdxDim;
-        uint16_t* cd = a.cbuf + pe * kBlock;
+        for (int ks = 0; ks < 4; ++ks) qf[ks] = qn[ks];
+        const f32x4 lse2 = lsen;
+        const int to = __shfl(tl, u * RPG + (4 * g) / G);
+        if (u + 1 < G) load_group(tl, u + 1);
+        f32x4 sv[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * g) = aq[mt];
-          u32x2 w2;
-          w2[0] = pack_bf16x2(si[mt][0], si[mt][1]);
-          w2[1] = pack_bf16x2(si[mt][2], si[mt][3]);
-          *reinterpret_cast<u32x2*>(cd + 16 * mt + 4 * g) = w2;  // keys 16mt + 4g .. +3
+          sv[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            sv[mt] = mfma16(qf[ks], as_bf16x8(ktile[swz_slot(16 * mt + n, 4 * ks + g)]), sv[mt]);
         }
-        if (g == 0) a.part_l[pe] = kLn2 * lsum;
+        // lane (n, g): register r of sv[mt] is head 4 (g % HQ4) + r of row
+        // u RPG + 4g / G for key 16mt + n
+        const int lim = to >= 0 ? a.q_start + to - key0 : -1;  // last attended key of the block
+        float ps[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          float s = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s += __builtin_amdgcn_exp2f(sv[mt][r] * a.scale_log2 - lse2[r]);
+          ps[mt] = s;
+        }
+        if constexpr (HQ4 >= 2) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(ps[mt]), __float_as_uint(ps[mt]), false, false);
+            ps[mt] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+          }
+        }
+        if constexpr (HQ4 >= 4) {
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps[mt]), __float_as_uint(ps[mt]), false, false);
+            ps[mt] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+          }
+        }
+        // the HQ4 lanes of a (row, key) hold the same P: lane g writes the
+        // key tiles mt with mt % HQ4 == g % HQ4
+        float* prow = reinterpret_cast<float*>(pw + (u * RPG + (4 * g) / G) * (kBlock / 4 + 1));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          if (mt % HQ4 == g % HQ4) prow[16 * mt + n] = 16 * mt + n <= lim ? ps[mt] * invG : 0.f;
       }
+      __builtin_amdgcn_wave_barrier();
+      // ---- phase 2: per index head, the rows' index scores, C, loss and diq
+      const int tn = __shfl(tl, n);  // row of column n
+      const int limn = tn >= 0 ? a.q_start + tn - key0 : -1;
+      const long long ebase = (long long)lbeg[h] + (long long)(j - hstart) * kJob + n;  // list entry of column n
+      f32x4 pr[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) pr[mt] = pw[n * (kBlock / 4 + 1) + 4 * mt + g];
+      for (int m = 0; m < nih; ++m) {
+        const int i = h + a.Hkv * m;
+        const long long bt = (long long)b * a.Sq + (tn >= 0 ? tn : 0);
+        const u32x4* is = reinterpret_cast<const u32x4*>(a.iq + (bt * kIdxHeads + i) * kIdxDim);
+        bf16x8 iqf[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          u32x4 v = {0, 0, 0, 0};
+          if (tn >= 0) v = is[4 * ks + g];
+          iqf[ks] = as_bf16x8(v);
+        }
+        const float ilse2 = tn >= 0 ? a.lse_idx[((long long)b * kIdxHeads + i) * a.Sq + tn] : 0.f;
+        if (m + 1 == nih && j + 4 < hj1) load_group(tnext, 0);  // next job's first group
+        f32x4 si[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          si[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            si[mt] = mfma16(as_bf16x8(itile[islot(16 * mt + n, 4 * ks + g)]), iqf[ks], si[mt]);
+        }
+        // lane (n, g): register r of si[mt] is key 16mt + 4g + r of row n
+        float lsum = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool att = 16 * mt + 4 * g + r <= limn;
+            const float p = pr[mt][r];  // 0 where not attended
+            const float s2 = si[mt][r] * kLog2eB;
+            // v_exp_f32 / v_log_f32 directly: results below the normal
+            // range flush to zero, and the log term skips P < 1e-30 (each
+            // such term is below 1e-28)
+            si[mt][r] = att ? __builtin_amdgcn_exp2f(s2 - ilse2) - p : 0.f;  // C = Q - P
+            if (p > 1e-30f) lsum += p * (__builtin_amdgcn_logf(p) - s2 + ilse2);
+          }
+        lsum = wave_sum_xor16_32(lsum);
+        f32x4 aq[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) aq[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        pv_idx<2>(si, itile, aq);  // sum over the block's keys of C ik
+        if (tn >= 0) {
+          const long long pe = ebase * nih + m;
+          float* dst = a.part_q + pe * kIdxDim;
+          uint16_t* cd = a.cbuf + pe * kBlock;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            *reinterpret_cast<f32x4*>(dst + 16 * mt + 4 * g) = aq[mt];
+            u32x2 w2;
+            w2[0] = pack_bf16x2(si[mt][0], si[mt][1]);
+            w2[1] = pack_bf16x2(si[mt][2], si[mt][3]);
+            *reinterpret_cast<u32x2*>(cd + 16 * mt + 4 * g) = w2;  // keys 16mt + 4g .. +3
+          }
+          if (g == 0) a.part_l[pe] = kLn2 * lsum;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();  // the tile's reads before the next job's writes
+      tl = tnext;
     }
   }
 }
@@ -607,16 +656,15 @@ char* align256(char* p) { return reinterpret_cast<char*>(((uintptr_t)p + 255) & 
 }  // namespace
 
 bool index_kl_supported(const Shape& s) {
-  const int nih = kIdxHeads / s.Hkv;
-  return (s.G == 4 || s.G == 8 || s.G == 16) && (16 / s.G) * nih <= 8 && s.bs == kBlock;
+  return (s.G == 4 || s.G == 8 || s.G == 16) && s.bs == kBlock;
 }
 
-// Workspace: the index log-sum-exp, the dik split partials, the entries' list
-// positions, the per-entry partials (entries <= B Hkv Sq k, and Hkv nih = 4),
-// then the inverse lists.
+// Workspace: the index log-sum-exp, the forward's log-sum-exp by row, the dik
+// split partials, the entries' list positions, the per-entry partials
+// (entries <= B Hkv Sq k, and Hkv nih = 4), then the inverse lists.
 size_t index_kl_workspace_bytes(const Shape& s) {
   const size_t ent = (size_t)s.B * kIdxHeads * s.Sq * s.top_k;  // (entry, index head) pairs
-  return (size_t)s.B * kIdxHeads * s.Sq * 4 + 256 +
+  return (size_t)s.B * kIdxHeads * s.Sq * 4 + 256 + (size_t)s.B * s.Sq * s.Hq * 4 + 256 +
          (size_t)s.B * s.nblk * kKeySplits * kBlock * kIdxDim * 4 + 256 +
          (size_t)s.B * s.Hkv * s.Sq * s.top_k * 4 + 256 +
          ent * 8 + 256 + ent * kIdxDim * 4 + 256 + ent * 4 + 256 + ent * kBlock * 2 + 256 +
@@ -628,6 +676,8 @@ template <int G>
 hipError_t launch_kl(const Shape& s, const KlArgs& a, hipStream_t st) {
   const dim3 blocks(s.nblk, s.B, kKeySplits);
   kl_lse_kernel<G><<<blocks, 256, 0, st>>>(a);
+  const long long nlse = (long long)s.B * s.Sq * s.Hq;
+  kl_lse_t_kernel<<<(unsigned)((nlse + 255) / 256), 256, 0, st>>>(a);
   const long long rows = (long long)s.B * kIdxHeads * s.Sq;
   kl_lse_merge_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, st>>>(a);
   kl_entry_kernel<G><<<blocks, 256, 0, st>>>(a);
@@ -647,6 +697,8 @@ hipError_t launch_index_kl_backward(const Shape& s, const void* q, const void* k
   char* p = align256(static_cast<char*>(ws));
   float* lse_idx = reinterpret_cast<float*>(p);
   p = align256(p + (size_t)s.B * kIdxHeads * s.Sq * 4);
+  float* lse_t = reinterpret_cast<float*>(p);
+  p = align256(p + (size_t)s.B * s.Sq * s.Hq * 4);
   float* dikp = reinterpret_cast<float*>(p);
   p = align256(p + (size_t)s.B * s.nblk * kKeySplits * kBlock * kIdxDim * 4);
   int32_t* slotpos = reinterpret_cast<int32_t*>(p);
@@ -665,7 +717,7 @@ hipError_t launch_index_kl_backward(const Shape& s, const void* q, const void* k
   if (e != hipSuccess) return e;
   KlArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
            static_cast<const uint16_t*>(iq), static_cast<const uint16_t*>(ik), sel, lse, loss,
-           diq, dik, lse_idx, dikp, slotpos, part_ml, part_q, part_l, cbuf, base, lists, s.B, s.Sq,
+           diq, dik, lse_idx, lse_t, dikp, slotpos, part_ml, part_q, part_l, cbuf, base, lists, s.B, s.Sq,
            s.Skv, s.q_start, s.Hq, s.Hkv, s.G, s.top_k, s.nblk, kIdxHeads / s.Hkv,
            s.scale * kLog2eB};
   switch (s.G) {

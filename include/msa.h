@@ -331,8 +331,7 @@ msa_status msa_sparse_attn_prefill_backward(const msa_problem* p, const void* q,
  * each block at most once per list; lse (fp32, [B][Hq][Sq], natural log) as
  * msa_sparse_attn_prefill returned it for this selection.  Outputs (device,
  * fp32, fully overwritten): loss [B][Sq][4], diq [B][Sq][4][64], dik
- * [B][Skv][64].  Hq / Hkv must be 4, 8 or 16 with (16 / G) (4 / Hkv) <= 8;
- * seq_kv at most 1310720.  workspace: msa_workspace_bytes(p,
+ * [B][Skv][64].  Hq / Hkv must be 4, 8 or 16; seq_kv at most 1310720.  workspace: msa_workspace_bytes(p,
  * MSA_OP_INDEX_KL_BACKWARD) bytes, any contents.  bf16 products (P, the index
  * softmax numerators and Q - P rounded to bf16), fp32 accumulation and
  * softmax statistics; deterministic (no floating-point atomics). */

@@ -44,6 +44,10 @@ CASES = {
     # G = 8 over one KV head: all four index heads drive it
     "g8_hkv1": TINY_PREFILL_2K.shrink(name="kl_hkv1", seq_q=600, seq_kv=700, q_start=100,
                                       n_q_heads=8, n_kv_heads=1, top_k=5),
+    # G = 4 over one KV head: four index heads per KV head, four rows per
+    # main-branch column group
+    "g4_hkv1": TINY_PREFILL_2K.shrink(name="kl_g4_hkv1", seq_q=450, seq_kv=600, q_start=150,
+                                      n_q_heads=4, n_kv_heads=1, top_k=7),
     # G = 16: one row per 16 query columns
     "g16_hkv2": TINY_PREFILL_2K.shrink(name="kl_g16", seq_q=400, seq_kv=900, q_start=500,
                                        n_q_heads=32, n_kv_heads=2, top_k=6),
