@@ -285,7 +285,7 @@ __global__ void __launch_bounds__(256) kl_lse_t_kernel(KlArgs a) {
 //     partial sum C ik (one MFMA product over the index-key tile).  C itself
 //     is stored for the dik pass.
 template <int G>
-__global__ void __launch_bounds__(256) kl_entry_kernel(KlArgs a) {
+__global__ void __launch_bounds__(256, 2) kl_entry_kernel(KlArgs a) {
   constexpr int RPG = 16 / G;  // rows per main-branch column group
   constexpr int HQ4 = G / 4;   // 16-lane rows that hold the same query row in phase 1
   constexpr int kJob = 16;     // rows per job
@@ -334,10 +334,12 @@ __global__ void __launch_bounds__(256) kl_entry_kernel(KlArgs a) {
       return (lane < 16 && li < llen[h]) ? a.lists[lbeg[h] + li] : -1;
     };
     // phase-1 operands of column group u: Q of row u RPG + n / G, head n % G
-    // (A operand), and the log2-domain LSE of the lane's four output heads
-    bf16x8 qn[4];
-    f32x4 lsen;
-    auto load_group = [&](int tl, int u) {
+    // (A operand), and the log2-domain LSE of the lane's four output heads.
+    // Two register sets: groups u and u + 1 are in flight while u - 1 is
+    // computed.
+    bf16x8 qa[4], qb[4];
+    f32x4 lsea, lseb;
+    auto load_group = [&](int tl, int u, bf16x8 (&qn)[4], f32x4& lsen) {
       const int ta = __shfl(tl, u * RPG + n / G);
       const int to = __shfl(tl, u * RPG + (4 * g) / G);
       const long long ba = (long long)b * a.Sq + (ta >= 0 ? ta : 0);
@@ -352,17 +354,24 @@ __global__ void __launch_bounds__(256) kl_entry_kernel(KlArgs a) {
       if (to >= 0) lsen = *reinterpret_cast<const f32x4*>(lse_h + ((long long)b * a.Sq + to) * a.Hq);
     };
     int tl = hj0 + wave < hj1 ? job_rows(hj0 + wave) : -1;
-    if (hj0 + wave < hj1) load_group(tl, 0);
+    if (hj0 + wave < hj1) {
+      load_group(tl, 0, qa, lsea);
+      load_group(tl, 1, qb, lseb);
+    }
     for (int j = hj0 + wave; j < hj1; j += 4) {
       const int tnext = j + 4 < hj1 ? job_rows(j + 4) : -1;
+      const bool more = j + 4 < hj1;
       // ---- phase 1: P of the job's 16 rows into the wave's LDS tile
-      for (int u = 0; u < G; ++u) {
+      // group u from set a (u even) or b (u odd); the set is then refilled
+      // with group u + 2, of this job or the next
+      auto group = [&](int u, bf16x8 (&qn)[4], f32x4& lsen) {
         bf16x8 qf[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qf[ks] = qn[ks];
         const f32x4 lse2 = lsen;
         const int to = __shfl(tl, u * RPG + (4 * g) / G);
-        if (u + 1 < G) load_group(tl, u + 1);
+        if (u + 2 < G) load_group(tl, u + 2, qn, lsen);
+        else if (more) load_group(tnext, u + 2 - G, qn, lsen);
         f32x4 sv[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -402,6 +411,10 @@ __global__ void __launch_bounds__(256) kl_entry_kernel(KlArgs a) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
           if (mt % HQ4 == g % HQ4) prow[16 * mt + n] = 16 * mt + n <= lim ? ps[mt] * invG : 0.f;
+      };
+      for (int u = 0; u < G; u += 2) {
+        group(u, qa, lsea);
+        group(u + 1, qb, lseb);
       }
       __builtin_amdgcn_wave_barrier();
       // ---- phase 2: per index head, the rows' index scores, C, loss and diq
@@ -423,7 +436,6 @@ __global__ void __launch_bounds__(256) kl_entry_kernel(KlArgs a) {
           iqf[ks] = as_bf16x8(v);
         }
         const float ilse2 = tn >= 0 ? a.lse_idx[((long long)b * kIdxHeads + i) * a.Sq + tn] : 0.f;
-        if (m + 1 == nih && j + 4 < hj1) load_group(tnext, 0);  // next job's first group
         f32x4 si[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
