@@ -24,13 +24,16 @@
 //   kl_lse_kernel        per (list entry, index head), over the block's keys
 //                        the row attends: the max of the index scores and the
 //                        sum of 2^(s - max).
+//   kl_lse_t_kernel      the forward's log-sum-exp in (row, query head) order.
 //   kl_lse_merge_kernel  the index log-sum-exp per (row, index head), its
 //                        entries combined in slot order.
-//   kl_key_kernel        per chunk of a block's rows: P from the forward's
+//   kl_entry_kernel      per 16 rows of a block's list: P from the forward's
 //                        log-sum-exp, Q from the index log-sum-exp, C = Q - P;
-//                        per (list entry, index head) the loss partial and the
-//                        diq partial (sums over the block's keys), and per key
-//                        dik (a sum over the block's rows).  Long lists are
+//                        per (list entry, index head) the loss partial, the
+//                        diq partial (sums over the block's keys) and C itself
+//                        per key.  Long lists are split over work-groups.
+//   kl_dik_kernel        per key of the block, dik = the sum of C iq over the
+//                        block's (list entry, index head) pairs, long lists
 //                        split over work-groups.
 //   kl_dik_merge_kernel  dik of split blocks, partials added in split order.
 //   kl_merge_kernel      loss and diq per (row, index head), partials added in
@@ -243,16 +246,23 @@ __global__ void __launch_bounds__(256) kl_lse_merge_kernel(KlArgs a) {
   const int h = i % a.Hkv, m = i / a.Hkv;
   const int32_t* sp = a.slotpos + (((long long)b * a.Hkv + h) * a.Sq + t) * a.top_k;
   float M = -__builtin_huge_valf(), L = 0.f;
-  for (int s = 0; s < a.top_k; ++s) {
-    const int e = sp[s];
-    if (e < 0) continue;
-    const f32x2 v = a.part_ml[(long long)e * a.nih + m];
-    if (!(v[1] > 0.f)) continue;
-    if (v[0] > M) {
-      L = L * exp2f(M - v[0]) + v[1];
-      M = v[0];
-    } else {
-      L += v[1] * exp2f(v[0] - M);
+  // eight slots' partials loaded together, then combined in slot order
+  for (int s0 = 0; s0 < a.top_k; s0 += 8) {
+    f32x2 v[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int e = s0 + x < a.top_k ? sp[s0 + x] : -1;
+      v[x] = e >= 0 ? a.part_ml[(long long)e * a.nih + m] : f32x2{0.f, 0.f};
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      if (!(v[x][1] > 0.f)) continue;
+      if (v[x][0] > M) {
+        L = L * exp2f(M - v[x][0]) + v[x][1];
+        M = v[x][0];
+      } else {
+        L += v[x][1] * exp2f(v[x][0] - M);
+      }
     }
   }
   a.lse_idx[x] = L > 0.f ? M + __log2f(L) : -__builtin_huge_valf();
@@ -624,12 +634,21 @@ __global__ void __launch_bounds__(256) kl_merge_kernel(KlArgs a) {
   const int h = i % a.Hkv, m = i / a.Hkv;
   const int32_t* sp = a.slotpos + (((long long)b * a.Hkv + h) * a.Sq + t) * a.top_k;
   float acc = 0.f, ls = 0.f;
-  for (int s = 0; s < a.top_k; ++s) {
-    const int e = sp[s];
-    if (e < 0) continue;
-    const long long pe = (long long)e * a.nih + m;
-    acc += a.part_q[pe * kIdxDim + lane];
-    ls += a.part_l[pe];
+  // eight slots' partials loaded together, then added in slot order
+  for (int s0 = 0; s0 < a.top_k; s0 += 8) {
+    float vq[8], vl[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int e = s0 + x < a.top_k ? sp[s0 + x] : -1;
+      const long long pe = (long long)(e >= 0 ? e : 0) * a.nih + m;
+      vq[x] = e >= 0 ? a.part_q[pe * kIdxDim + lane] : 0.f;
+      vl[x] = e >= 0 ? a.part_l[pe] : 0.f;
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      acc += vq[x];
+      ls += vl[x];
+    }
   }
   a.diq[w * kIdxDim + lane] = acc;
   if (lane == 0) a.loss[w] = ls;
