@@ -179,23 +179,42 @@ __global__ void __launch_bounds__(256) inverse_kernel(BwdArgs a) {
 }
 
 // Pass 2a: per (sequence, KV head, block), the exclusive scan of the batch
-// counts (in place) and the list length.  One thread per block index.
+// counts (in place) and the list length.  A work-group takes 16 blocks and
+// cuts the batches into 16 segments, a thread per (segment, block): segment
+// sums, then each thread rewrites its segment from the sum of the segments
+// before it.  A batch whose last row's block is below c holds no count for c
+// (pass 1 never wrote it, pass 3 never reads it).
+constexpr int kScanBlocks = 16, kScanSegs = 16;
 __global__ void __launch_bounds__(256) batch_scan_kernel(BwdArgs a) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  __shared__ int32_t part[kScanSegs][kScanBlocks];
+  const int cl = threadIdx.x % kScanBlocks, seg = threadIdx.x / kScanBlocks;
+  const int c = blockIdx.x * kScanBlocks + cl;
   const long long hb = blockIdx.y;  // b * Hkv + h
-  if (c >= a.nblk) return;
-  int32_t* cnt = a.bcnt + hb * a.nbatch * a.nblk + c;
-  // a batch whose last row's block is below c holds no count for c (pass 1
-  // never wrote it, pass 3 never reads it)
-  int run = 0;
-  for (int j = 0; j < a.nbatch; ++j) {
+  const bool okc = c < a.nblk;
+  int32_t* cnt = a.bcnt + hb * a.nbatch * a.nblk + (okc ? c : 0);
+  const int j0 = (int)((long long)seg * a.nbatch / kScanSegs);
+  const int j1 = (int)((long long)(seg + 1) * a.nbatch / kScanSegs);
+  auto holds = [&](int j) {
     const int rows = min(kBatchRows, a.Sq - j * kBatchRows);
-    if ((a.q_start + j * kBatchRows + rows - 1) / kBlock < c) continue;
-    const int x = cnt[(long long)j * a.nblk];
-    cnt[(long long)j * a.nblk] = run;
-    run += x;
+    return (a.q_start + j * kBatchRows + rows - 1) / kBlock >= c;
+  };
+  int sum = 0;
+  if (okc)
+    for (int j = j0; j < j1; ++j)
+      if (holds(j)) sum += cnt[(long long)j * a.nblk];
+  part[seg][cl] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int x = 0; x < seg; ++x) run += part[x][cl];
+  if (okc) {
+    for (int j = j0; j < j1; ++j) {
+      if (!holds(j)) continue;
+      const int x = cnt[(long long)j * a.nblk];
+      cnt[(long long)j * a.nblk] = run;
+      run += x;
+    }
+    if (seg == kScanSegs - 1) a.base[hb * a.nblk + c] = run;  // length; a start after pass 2b
   }
-  a.base[hb * a.nblk + c] = run;  // length; turned into the start by pass 2b
 }
 
 // Pass 2b: exclusive scan of the list lengths over all (sequence, KV head,
@@ -618,7 +637,7 @@ hipError_t launch_inverse_lists(const Shape& s, const int32_t* sel, void* ws,
     if (e != hipSuccess) return e;
   }
   inverse_kernel<false><<<dim3(nbatch, s.Hkv, s.B), 256, bm_bytes, st>>>(a);
-  batch_scan_kernel<<<dim3(ceil_div(s.nblk, 256), s.B * s.Hkv), 256, 0, st>>>(a);
+  batch_scan_kernel<<<dim3(ceil_div(s.nblk, kScanBlocks), s.B * s.Hkv), 256, 0, st>>>(a);
   base_scan_kernel<<<1, 256, 0, st>>>(a);
   inverse_kernel<true><<<dim3(nbatch, s.Hkv, s.B), 256, bm_bytes, st>>>(a);
   *base_out = base;
