@@ -51,6 +51,12 @@ CASES = {
     # G = 16: one row per 16 query columns
     "g16_hkv2": TINY_PREFILL_2K.shrink(name="kl_g16", seq_q=400, seq_kv=900, q_start=500,
                                        n_q_heads=32, n_kv_heads=2, top_k=6),
+    # G = 16 over one KV head: both lane swaps of the head sum, four index heads
+    "g16_hkv1": TINY_PREFILL_2K.shrink(name="kl_g16_hkv1", seq_q=300, seq_kv=420, q_start=120,
+                                       n_q_heads=16, n_kv_heads=1, top_k=5),
+    # G = 4 over four KV heads: the head sum inside a lane, one index head each
+    "g4_hkv4": TINY_PREFILL_2K.shrink(name="kl_g4_hkv4", seq_q=333, seq_kv=333, n_q_heads=16,
+                                      n_kv_heads=4, top_k=4),
     # the 2K workload: early blocks' row lists are long enough that the key
     # pass splits them over several work-groups and merges the dik partials
     "tiny_2k": TINY_PREFILL_2K,
