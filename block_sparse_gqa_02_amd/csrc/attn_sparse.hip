@@ -193,8 +193,13 @@ __global__ void __launch_bounds__(256) decode_partial_kernel(DecodeArgs a) {
   }
 }
 
-// One wave per (sequence, query head): log-sum-exp merge of the splits.
+// One wave per (sequence, query head): log-sum-exp merge of the splits.  The
+// splits are read eight at a time, every load of a batch issued before any is
+// used; a batch raises the reference max once and rescales the sums so far
+// (with eight or fewer splits the one batch's max is the global one, and the
+// sums are those of a two-pass merge).
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
+  constexpr int kBatch = 8;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int hq = blockIdx.x * kAttnWaves + wave;
@@ -202,19 +207,35 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   if (hq >= a.Hq) return;
   const int h = hq / a.G, n = hq % a.G;
   const size_t col0 = ((size_t)b * a.Hkv + h) * a.nsplit * a.G + n;
-  float M = -__builtin_huge_valf();
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[2 * (col0 + (size_t)s * a.G)]);
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-  if (M > -__builtin_huge_valf()) {
-    for (int s = 0; s < a.nsplit; ++s) {
-      const size_t col = col0 + (size_t)s * a.G;
-      const float ms = a.part_ml[2 * col];
-      if (ms == -__builtin_huge_valf()) continue;
-      const float w = exp2f(ms - M);
-      L += w * a.part_ml[2 * col + 1];
-      const f32x2 ov = reinterpret_cast<const f32x2*>(a.part_o + col * kHeadDim)[lane];
-      o0 += w * ov[0];
-      o1 += w * ov[1];
+  const float ninf = -__builtin_huge_valf();
+  float M = ninf, L = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s0 = 0; s0 < a.nsplit; s0 += kBatch) {
+    f32x2 ml[kBatch], ov[kBatch];
+#pragma unroll
+    for (int x = 0; x < kBatch; ++x) {
+      const bool ok = s0 + x < a.nsplit;
+      const size_t col = col0 + (size_t)(ok ? s0 + x : 0) * a.G;
+      ml[x] = ok ? reinterpret_cast<const f32x2*>(a.part_ml)[col] : f32x2{ninf, 0.f};
+      ov[x] = ok ? reinterpret_cast<const f32x2*>(a.part_o + col * kHeadDim)[lane] : f32x2{0.f, 0.f};
+    }
+    float bm = M;
+#pragma unroll
+    for (int x = 0; x < kBatch; ++x) bm = fmaxf(bm, ml[x][0]);  // -inf: the split attended nothing
+    if (bm == ninf) continue;
+    if (bm > M) {
+      const float sc = M == ninf ? 0.f : exp2f(M - bm);
+      L *= sc;
+      o0 *= sc;
+      o1 *= sc;
+      M = bm;
+    }
+#pragma unroll
+    for (int x = 0; x < kBatch; ++x) {
+      if (ml[x][0] == ninf) continue;
+      const float w = exp2f(ml[x][0] - M);
+      L += w * ml[x][1];
+      o0 += w * ov[x][0];
+      o1 += w * ov[x][1];
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
