@@ -81,7 +81,6 @@ __device__ __forceinline__ void pv_tr(const f32x4 (&pt)[4], const u32x4* tile, f
   // byte (32kv + 16hf) * 256 + (vlane ^ 32mt) of the tile
   const int r15 = 4 * g + n / 4;
   const int vlane = r15 * 256 + 16 * (((n >> 1) & 1) ^ r15) + 8 * (n & 1);
-  const uint32_t tb = lds_byte_addr(tile);
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
     u32x4 pw;
@@ -92,10 +91,9 @@ __device__ __forceinline__ void pv_tr(const f32x4 (&pt)[4], const u32x4* tile, f
     const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-      const uint32_t va = tb + (uint32_t)(32 * kv * 256) + (uint32_t)(vlane ^ (32 * mt));
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)va);
-      const s16x4 hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)(va + 16 * 256));
+      const uint32_t va = (uint32_t)(32 * kv * 256) + (uint32_t)(vlane ^ (32 * mt));
+      const s16x4 lo = lds_read_tr_at(tile, va);
+      const s16x4 hi = lds_read_tr_at(tile, va + 16 * 256);
       const bf16x8 tf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       acc[mt] = mfma16(tf, pb, acc[mt]);
     }
@@ -454,10 +452,13 @@ constexpr int kDqTileRows = 16;  // 4 waves at G = 8: two work-groups share a CU
 
 
 __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
-  extern __shared__ u32x4 dqlds[];
-  u32x4* ktiles = dqlds;                      // [2][1024]: K of the current / next block
-  u32x4* vtiles = dqlds + 2 * kBlock * 16;    // [2][1024]: V
-  uint32_t* rmask = reinterpret_cast<uint32_t*>(dqlds + 4 * kBlock * 16);  // [cmax + 1]
+  // K and V of the current and the next block, each tile its own LDS object,
+  // and the block loop unrolled by two so that every access names its tile:
+  // the compiler then tells the LDS-bound loads into one pair from the reads
+  // of the other (and of the row masks) and makes neither wait for them.
+  __shared__ u32x4 ktile0[kBlock * 16], ktile1[kBlock * 16];
+  __shared__ u32x4 vtile0[kBlock * 16], vtile1[kBlock * 16];
+  extern __shared__ uint32_t rmask[];  // [cmax + 1]
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int nwaves = blockDim.x / kWave;
   const int n = lane % 16, g = lane / 16;
@@ -520,7 +521,7 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
   };
   // LDS-bound loads of block c's K and V into tiles bf: load inst writes key
   // rows 4 inst .. 4 inst + 3, lane -> row 4 inst + lane/16, stored chunk lane%16
-  auto fetch = [&](int c, int bf) {
+  auto fetch = [&](int c, u32x4* kdst, u32x4* vdst) {
     const long long off0 = (hb * a.Skv + (long long)c * kBlock) * kHeadDim;
     for (int inst = wave; inst < 16; inst += nwaves) {
       const int slot = inst * kWave + lane;
@@ -529,23 +530,16 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
       const int krow = min(c * kBlock + key, a.Skv - 1) - c * kBlock;  // rows past the cache: masked
       const long long e = off0 + (long long)krow * kHeadDim + 8 * ch;
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.k + e),
-                                       (__attribute__((address_space(3))) void*)(ktiles + bf * 1024 + inst * kWave),
+                                       (__attribute__((address_space(3))) void*)(kdst + inst * kWave),
                                        16, 0, 0);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.v + e),
-                                       (__attribute__((address_space(3))) void*)(vtiles + bf * 1024 + inst * kWave),
+                                       (__attribute__((address_space(3))) void*)(vdst + inst * kWave),
                                        16, 0, 0);
     }
   };
-  int c = next_block(0), bf = 0;
-  if (c <= cmax) fetch(c, 0);
-  while (c <= cmax) {
-    const int cn = next_block(c + 1);
-    wait_all_loads();
-    __syncthreads();  // block c's tiles complete in every wave
-    if (cn <= cmax) fetch(cn, bf ^ 1);
+  // block c from tiles (kt, vt)
+  auto compute = [&](int c, const u32x4* kt, const u32x4* vt) {
     const uint32_t m = rmask[c];
-    const u32x4* kt = ktiles + bf * 1024;
-    const u32x4* vt = vtiles + bf * 1024;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int grp = 2 * wave + j;
@@ -575,9 +569,27 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
         }
       pv_tr(sv, kt, acc[j]);  // dQ^T += K^T dS^T
     }
-    __syncthreads();  // tiles bf free for the block after cn
+  };
+  int c = next_block(0);
+  if (c <= cmax) fetch(c, ktile0, vtile0);
+  while (c <= cmax) {
+    // tiles 0 hold block c; block cn goes to tiles 1
+    int cn = next_block(c + 1);
+    wait_all_loads();
+    __syncthreads();  // block c's tiles complete in every wave
+    if (cn <= cmax) fetch(cn, ktile1, vtile1);
+    compute(c, ktile0, vtile0);
+    __syncthreads();  // tiles 0 free for the block after cn
     c = cn;
-    bf ^= 1;
+    if (c > cmax) break;
+    // tiles 1 hold block c; block cn goes to tiles 0
+    cn = next_block(c + 1);
+    wait_all_loads();
+    __syncthreads();
+    if (cn <= cmax) fetch(cn, ktile0, vtile0);
+    compute(c, ktile1, vtile1);
+    __syncthreads();  // tiles 1 free for the block after cn
+    c = cn;
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -671,7 +683,7 @@ hipError_t launch_sparse_attn_backward(const Shape& s, const void* q, const void
   a.base = const_cast<int32_t*>(base);
   a.lists = const_cast<int32_t*>(lists);
   if (s.G == 4 || s.G == 8) {
-    const size_t dq_lds = (size_t)4 * kBlock * 16 * 16 + (size_t)s.nblk * 4;
+    const size_t dq_lds = (size_t)s.nblk * 4;  // the row masks (the tiles are static)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dq_tile_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)dq_lds);
     if (e != hipSuccess) return e;

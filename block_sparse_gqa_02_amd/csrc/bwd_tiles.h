@@ -26,6 +26,14 @@ __device__ __forceinline__ s16x4 lds_read_tr(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(uintptr_t)addr);
 }
 
+// ds_read_b64_tr_b16 at byte `off` of the LDS tile `tile`.  Unlike an address
+// rebuilt from an integer, the pointer keeps the tile's LDS object in view of
+// the compiler, so the read waits only for LDS-bound loads into that object.
+__device__ __forceinline__ s16x4 lds_read_tr_at(const void* tile, uint32_t off) {
+  typedef __attribute__((address_space(3))) const char* lds_cchar_ptr;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)((lds_cchar_ptr)tile + off));
+}
+
 // s_waitcnt vmcnt(0) with a compiler fence: the LDS-bound loads of the
 // staged columns are complete (for this wave) before anything below.
 __device__ __forceinline__ void wait_all_loads() {
