@@ -80,7 +80,10 @@ __device__ __forceinline__ void pv_tr(const f32x4 (&pt)[4], const u32x4* tile, f
   const int lane = lane_id(), n = lane % 16, g = lane / 16;
   // byte (32kv + 16hf) * 256 + (vlane ^ 32mt) of the tile
   const int r15 = 4 * g + n / 4;
-  const int vlane = r15 * 256 + 16 * (((n >> 1) & 1) ^ r15) + 8 * (n & 1);
+  int vlane = r15 * 256 + 16 * (((n >> 1) & 1) ^ r15) + 8 * (n & 1);
+  // opaque here, so that a caller's loop does not keep every tile's read
+  // addresses live as loop invariants (registers)
+  asm volatile("" : "+v"(vlane));
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
     u32x4 pw;
@@ -316,8 +319,12 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdArgs a) {
 // travel by LDS-bound loads into the second pair of tiles while chunk j is
 // computed; the row indices that address them are loaded a chunk earlier.
 __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
-  __shared__ u32x4 qtile[2][kBlock * 16];  // 64 columns x 128 dims, swz_slot layout
-  __shared__ u32x4 gtile[2][kBlock * 16];  // the same columns of dO
+  // Two tile pairs (64 columns x 128 dims of Q and of dO, swz_slot layout),
+  // each tile its own LDS object and the chunk loop unrolled by two, so that
+  // every access names its tile and the compiler does not make the reads of
+  // one pair wait for the LDS-bound loads into the other.
+  __shared__ u32x4 qtile0[kBlock * 16], qtile1[kBlock * 16];
+  __shared__ u32x4 gtile0[kBlock * 16], gtile1[kBlock * 16];
   __shared__ float clse[2][64], cds[2][64];
   __shared__ int cpos[2][64];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -353,52 +360,59 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
   // their columns are masked through cpos = -1)
   auto row_of = [&](int j, int col) { return rows[min(j * R + col / a.G, len - 1)]; };
   int rt[4];          // rows of this thread's slots, next chunk to stage
-  int rmeta = 0;      // row of column tid (tid < 64), next chunk to stage
-  float ml = 0.f, md = 0.f;  // its staged metadata, written at the next iteration
-  int mp = -1;
-  auto stage = [&](int j, int bf) {  // issue chunk j's loads (rows already in rt / rmeta)
+  int rmeta = 0;      // row of column lane, next chunk to stage
+  // Column lane's metadata, loaded raw with its chunk's tiles and turned into
+  // LDS values at the next iteration (wave 0's are the ones kept): a value
+  // used right after its load would make the wait for it, which the in-order
+  // load counter extends to the tile loads issued before it, land inside the
+  // iteration that is meant to overlap them.
+  float ml = 0.f, md = 0.f;
+  int mrow = 0;
+  bool mok = false;
+  auto stage = [&](int j, u32x4* qdst, u32x4* gdst) {  // chunk j's loads (rows in rt / rmeta)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const long long e = (((long long)b * a.Sq + rt[t]) * a.Hq + h * a.G + colt[t] % a.G) *
                           kHeadDim + 8 * cht[t];
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.q + e),
-                                       (__attribute__((address_space(3))) void*)(&qtile[bf][64 * (4 * wave + t)]),
+                                       (__attribute__((address_space(3))) void*)(qdst + 64 * (4 * wave + t)),
                                        16, 0, 0);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.dout + e),
-                                       (__attribute__((address_space(3))) void*)(&gtile[bf][64 * (4 * wave + t)]),
+                                       (__attribute__((address_space(3))) void*)(gdst + 64 * (4 * wave + t)),
                                        16, 0, 0);
     }
-    if (tid < 64) {
-      const bool ok = j * R + tid / a.G < len;
-      const long long li = ((long long)b * a.Hq + h * a.G + tid % a.G) * a.Sq + rmeta;
-      ml = ok ? a.lse[li] * kLog2eB : 0.f;
-      md = ok ? a.dsum[li] : 0.f;
-      mp = ok ? a.q_start + rmeta : -1;
-    }
+    mok = j * R + lane / a.G < len;
+    mrow = rmeta;
+    const long long li = ((long long)b * a.Hq + h * a.G + lane % a.G) * a.Sq + rmeta;
+    ml = a.lse[li];
+    md = a.dsum[li];
   };
   auto fetch_rows = [&](int j) {  // row indices of chunk j into rt / rmeta
 #pragma unroll
     for (int t = 0; t < 4; ++t) rt[t] = row_of(j, colt[t]);
-    if (tid < 64) rmeta = row_of(j, tid);
+    rmeta = row_of(j, lane);
   };
   if (nchunk > 0) {
     fetch_rows(0);
-    stage(0, 0);
+    stage(0, qtile0, gtile0);
     if (nchunk > 1) fetch_rows(1);
   }
-  for (int j = 0; j < nchunk; ++j) {
-    const int bf = j & 1;
+  // chunk j from tiles (qcur, gcur); chunk j + 1 staged into (qnext, gnext)
+  auto step = [&](int j, int bf, const u32x4* qcur, const u32x4* gcur, u32x4* qnext,
+                  u32x4* gnext) {
     wait_all_loads();  // chunk j's tiles (issued last iteration) and its metadata values
     if (tid < 64) {
-      clse[bf][tid] = ml;
-      cds[bf][tid] = md;
-      cpos[bf][tid] = mp;
+      clse[bf][tid] = mok ? ml * kLog2eB : 0.f;
+      cds[bf][tid] = mok ? md : 0.f;
+      cpos[bf][tid] = mok ? a.q_start + mrow : -1;
     }
     __syncthreads();
     if (j + 1 < nchunk) {
-      stage(j + 1, bf ^ 1);
+      stage(j + 1, qnext, gnext);
       if (j + 2 < nchunk) fetch_rows(j + 2);
     }
+    int nl = n, gl = g;  // opaque lane coordinates: the tile read addresses stay per step
+    asm volatile("" : "+v"(nl), "+v"(gl));
     // X = Q K^T and Y = dO V^T: M = columns (M-tile mt: columns 16mt + 4g + r
     // in the result), N = this wave's keys
     f32x4 x[4], y[4];
@@ -408,8 +422,8 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
       y[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 qa = as_bf16x8(qtile[bf][swz_slot(16 * mt + n, 4 * ks + g)]);
-        const bf16x8 ga = as_bf16x8(gtile[bf][swz_slot(16 * mt + n, 4 * ks + g)]);
+        const bf16x8 qa = as_bf16x8(qcur[swz_slot(16 * mt + nl, 4 * ks + gl)]);
+        const bf16x8 ga = as_bf16x8(gcur[swz_slot(16 * mt + nl, 4 * ks + gl)]);
         x[mt] = mfma16(qa, ks_.qf[ks], x[mt]);
         y[mt] = mfma16(ga, vs_.qf[ks], y[mt]);
       }
@@ -425,9 +439,15 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
         x[mt][rr] = p;                              // P (columns x keys)
         y[mt][rr] = p * (y[mt][rr] - cds[bf][col]);  // dS
       }
-    pv_tr(x, gtile[bf], dva);  // dV^T += dO^T P
-    pv_tr(y, qtile[bf], dka);  // dK^T += Q^T dS
-    __syncthreads();                       // buffers bf free for chunk j + 2
+    pv_tr(x, gcur, dva);  // dV^T += dO^T P
+    pv_tr(y, qcur, dka);  // dK^T += Q^T dS
+    __syncthreads();      // tiles (qcur, gcur) free for chunk j + 2
+  };
+  for (int j = 0; j < nchunk; j += 2) {
+    step(j, 0, qtile0, gtile0, qtile1, gtile1);
+    __builtin_amdgcn_sched_barrier(0);  // the two steps are not interleaved (registers)
+    if (j + 1 < nchunk) step(j + 1, 1, qtile1, gtile1, qtile0, gtile0);
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (n < nkeys) {
     store_tr_f32(dva, a.dv + (hb * a.Skv + key0 + n) * kHeadDim, 1.f);
