@@ -102,7 +102,8 @@ __device__ __forceinline__ void pv_idx(const f32x4 (&w)[2 * KV], const u32x4* ti
                                        f32x4 (&acc)[4]) {
   const int lane = lane_id(), n = lane % 16, g = lane / 16;
   const int r15 = 4 * g + n / 4;
-  const uint32_t tb = lds_byte_addr(tile) + (uint32_t)(r15 * 128 + 8 * (n & 1));
+  int tb = r15 * 128 + 8 * (n & 1);  // byte offset in the tile
+  asm volatile("" : "+v"(tb));  // opaque: a caller's loop keeps no per-tile address registers
 #pragma unroll
   for (int kv = 0; kv < KV; ++kv) {
     u32x4 pw;
@@ -114,9 +115,9 @@ __device__ __forceinline__ void pv_idx(const f32x4 (&w)[2 * KV], const u32x4* ti
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const uint32_t ch = (uint32_t)((2 * mt + ((n >> 1) & 1)) ^ (r15 & 7));
-      const uint32_t va = tb + (uint32_t)(32 * kv * 128) + 16 * ch;
-      const s16x4 lo = lds_read_tr(va);
-      const s16x4 hi = lds_read_tr(va + 16 * 128);
+      const uint32_t va = (uint32_t)tb + (uint32_t)(32 * kv * 128) + 16 * ch;
+      const s16x4 lo = lds_read_tr_at(tile, va);
+      const s16x4 hi = lds_read_tr_at(tile, va + 16 * 128);
       const bf16x8 tf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       acc[mt] = mfma16(tf, pb, acc[mt]);
     }
@@ -508,13 +509,18 @@ constexpr int kDikBatch = 32;  // (entry, index head) pairs per step of the dik 
 // dik itself, with more each writes its partial and kl_dik_merge_kernel adds
 // them in split order (deterministic).
 __global__ void __launch_bounds__(256) kl_dik_kernel(KlArgs a) {
-  __shared__ u32x4 qt[4][2][kDikBatch * 8];  // per wave: index queries of a batch, islot layout
-  __shared__ u32x4 ct[4][2][kDikBatch * 8];  // per wave: C rows of a batch (32 x 64 bf16)
+  // Per wave, two tile pairs (a batch's index queries and its C rows, islot
+  // layout), each tile its own LDS object and the batch loop unrolled by two,
+  // so that every access names its tile and the reads of one pair do not wait
+  // for the LDS-bound loads into the other.
+  __shared__ u32x4 qt0[4 * kDikBatch * 8], qt1[4 * kDikBatch * 8];
+  __shared__ u32x4 ct0[4 * kDikBatch * 8], ct1[4 * kDikBatch * 8];
   __shared__ int lbeg[4], lnp[4];
-  // the cross-wave sum, in the query tiles' memory once the batches are done
-  float(*red)[kIdxDim + 4] = reinterpret_cast<float(*)[kIdxDim + 4]>(&qt[0][0][0]);
-  static_assert(sizeof(float) * kBlock * (kIdxDim + 4) <= sizeof(u32x4) * 4 * 2 * kDikBatch * 8,
-                "the reduction fits in the query tiles");
+  // the cross-wave sum, 32 keys at a time, in the first query tiles' memory
+  // once the batches are done
+  float(*red)[kIdxDim + 4] = reinterpret_cast<float(*)[kIdxDim + 4]>(&qt0[0]);
+  static_assert(sizeof(float) * (kBlock / 2) * (kIdxDim + 4) <= sizeof(qt0),
+                "half the reduction fits in the query tiles");
   const int c = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n = lane % 16, g = lane / 16;
@@ -544,8 +550,20 @@ __global__ void __launch_bounds__(256) kl_dik_kernel(KlArgs a) {
     m = p % nih;
     return h;
   };
-  // four loads of 64 lanes per tile: slot = pair x 8 chunks (islot layout)
-  auto stage = [&](int jb, int buf) {
+  // four loads of 64 lanes per tile: slot = pair x 8 chunks (islot layout).
+  // The query rows of a batch's pairs are read from the lists a batch ahead,
+  // so that no load address waits for a load.
+  int trow[4];
+  auto rows_of = [&](int jb) {
+#pragma unroll
+    for (int inst = 0; inst < 4; ++inst) {
+      const int pr = (inst * kWave + lane) >> 3;
+      int row, m;
+      pair_at(min(jb * kDikBatch + pr, pairs - 1), row, m);
+      trow[inst] = a.lists[row / nih];
+    }
+  };
+  auto stage = [&](int jb, u32x4* qdst, u32x4* cdst) {
 #pragma unroll
     for (int inst = 0; inst < 4; ++inst) {
       const int slot = inst * kWave + lane;
@@ -553,14 +571,14 @@ __global__ void __launch_bounds__(256) kl_dik_kernel(KlArgs a) {
       const int p = min(jb * kDikBatch + pr, pairs - 1);
       int row, m;
       const int h = pair_at(p, row, m);
-      const int t = a.lists[row / nih];
+      const int t = trow[inst];
       __builtin_amdgcn_global_load_lds(
           reinterpret_cast<const void*>(a.iq + (((long long)b * a.Sq + t) * kIdxHeads + h + a.Hkv * m) *
                                                    kIdxDim + 8 * ch),
-          (__attribute__((address_space(3))) void*)(&qt[wave][buf][inst * kWave]), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(qdst + inst * kWave), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(
           reinterpret_cast<const void*>(a.cbuf + (long long)row * kBlock + 8 * ch),
-          (__attribute__((address_space(3))) void*)(&ct[wave][buf][inst * kWave]), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(cdst + inst * kWave), 16, 0, 0);
     }
   };
   f32x4 dka[4][4];  // [key tile][dim M-tile]
@@ -568,57 +586,89 @@ __global__ void __launch_bounds__(256) kl_dik_kernel(KlArgs a) {
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) dka[kt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (j0 + wave < j1) stage(j0 + wave, 0);
-  int buf = 0;
-  for (int jb = j0 + wave; jb < j1; jb += 4, buf ^= 1) {
-    wait_all_loads();  // batch jb's tiles
+  const int wo = wave * kDikBatch * 8;
+  if (j0 + wave < j1) {
+    rows_of(j0 + wave);
+    stage(j0 + wave, qt0 + wo, ct0 + wo);
+    rows_of(min(j0 + wave + 4, j1 - 1));
+  }
+  // Byte offset in a C tile of (pair 16 mt + 4 g + r, key 16 kt + n): the
+  // islot address 128 pr + 16 ((kk >> 3) ^ (pr & 7)) + 2 (kk & 7) splits into
+  // disjoint bit fields, (A ^ 16 (2 kt ^ r)) + 128 r + 2048 mt with A the
+  // lane's part; the eight A ^ 16 c are kept, so every read is one step from
+  // the tile pointer plus an immediate.
+  uint32_t cbase[8];
+  {
+    const uint32_t A = 512u * g + 16u * ((n >> 3) | 4u * (g & 1)) + 2u * (n & 7);
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      cbase[cc] = A ^ (16u * cc);
+      asm volatile("" : "+v"(cbase[cc]));
+    }
+  }
+  // Batch jb from tiles (qcur, ccur); batch jb + 4 staged into (qnext, cnext).
+  // The staging is unconditional (the split's last batch once more when jb + 4
+  // is past it, never read): with no branch around the LDS-bound loads the
+  // compiler keeps the reads of one tile pair from waiting for the other's.
+  auto step = [&](int jb, const u32x4* qcur, const u32x4* ccur, u32x4* qnext, u32x4* cnext) {
+    wait_all_loads();  // batch jb's tiles and batch jb + 4's query rows
     __builtin_amdgcn_wave_barrier();
-    if (jb + 4 < j1) stage(jb + 4, buf ^ 1);
+    stage(min(jb + 4, j1 - 1), qnext, cnext);
+    rows_of(min(jb + 8, j1 - 1));
     const int nvalid = pairs - jb * kDikBatch;  // pairs past this are padding
-    const uint16_t* cw16 = reinterpret_cast<const uint16_t*>(&ct[wave][buf][0]);
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      // register r of cw[mt]: pair 16mt + 4g + r, key 16kt + n (islot chunk of the key)
+      // register r of cw[mt]: pair 16mt + 4g + r, key 16kt + n; padding pairs
+      // masked to +0 (a mask, not a branch around the read)
       f32x4 cw[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int pr = 16 * mt + 4 * g + r, kk = 16 * kt + n;
-          const uint16_t v = cw16[islot(pr, kk >> 3) * 8 + (kk & 7)];
-          cw[mt][r] = pr < nvalid ? __uint_as_float((uint32_t)v << 16) : 0.f;
+          const uint32_t keep = 16 * mt + 4 * g + r < nvalid ? 0xffffu : 0u;
+          const uint32_t v = lds_u16_at(ccur, cbase[(2 * kt) ^ r] + 128 * r + 2048 * mt);
+          cw[mt][r] = __uint_as_float((v & keep) << 16);
         }
-      pv_idx<1>(cw, qt[wave][buf], dka[kt]);
+      pv_idx<1>(cw, qcur, dka[kt]);
     }
+  };
+  for (int jb = j0 + wave; jb < j1; jb += 8) {
+    step(jb, qt0 + wo, ct0 + wo, qt1 + wo, ct1 + wo);
+    if (jb + 4 < j1) step(jb + 4, qt1 + wo, ct1 + wo, qt0 + wo, ct0 + wo);
   }
-  // the waves' sums, added in wave order (the first barrier also ends every
-  // wave's reads of the tiles); thread = (key, 16-dim quarter)
-  for (int w = 0; w < 4; ++w) {
+  wait_all_loads();  // the batch staged past the end has landed
+  // the waves' sums, added in wave order, keys 32 hh .. 32 hh + 31 at a time
+  // (the first barrier also ends every wave's reads of the tiles); writer
+  // thread = (key, 16-dim quarter) of the half, the first 128 threads
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    for (int w = 0; w < 4; ++w) {
+      __syncthreads();
+      if (wave == w) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float& dst = red[16 * kh + n][16 * mt + 4 * g + r];
+              dst = (w == 0 ? 0.f : dst) + dka[2 * hh + kh][mt][r];
+            }
+      }
+    }
     __syncthreads();
-    if (wave == w) {
+    const int kl = tid / 4, d0 = 16 * (tid % 4);
+    const int key = c * kBlock + 32 * hh + kl;
+    if (tid < 128 && key < a.Skv) {
+      float* dst = nsplit == 1
+                       ? a.dik + ((long long)b * a.Skv + key) * kIdxDim + d0
+                       : a.dikp + ((((long long)b * a.nblk + c) * kKeySplits + split) * kBlock +
+                                   32 * hh + kl) * kIdxDim + d0;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float& dst = red[16 * kt + n][16 * mt + 4 * g + r];
-            dst = (w == 0 ? 0.f : dst) + dka[kt][mt][r];
-          }
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<f32x4*>(dst + 4 * i) = f32x4{red[kl][d0 + 4 * i], red[kl][d0 + 4 * i + 1],
+                                                       red[kl][d0 + 4 * i + 2], red[kl][d0 + 4 * i + 3]};
     }
-  }
-  __syncthreads();
-  const int kl = tid / 4, d0 = 16 * (tid % 4);
-  const int key = c * kBlock + kl;
-  if (key < a.Skv) {
-    float* dst = nsplit == 1
-                     ? a.dik + ((long long)b * a.Skv + key) * kIdxDim + d0
-                     : a.dikp + ((((long long)b * a.nblk + c) * kKeySplits + split) * kBlock + kl) *
-                                    kIdxDim + d0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<f32x4*>(dst + 4 * i) =
-          f32x4{red[kl][d0 + 4 * i], red[kl][d0 + 4 * i + 1], red[kl][d0 + 4 * i + 2], red[kl][d0 + 4 * i + 3]};
   }
 }
 
