@@ -18,9 +18,11 @@
 //                    blocks in LDS (bit i = row i of the batch), counted, scanned
 //                    over batches and over blocks, then filled in row order.
 //                    Deterministic: no atomics outside LDS bit sets.
-//   dq_tile_kernel   (groups of 4 or 8 heads) a work-group per 16-row tile
-//                    walks the union of the tile's selected blocks, each
-//                    block's K and V fetched once into LDS; per block and
+//   dq_union_kernel  (groups of 4 or 8 heads) a work-group per 32-row tile
+//                    (64 at G = 4) walks the union of the tile's selected
+//                    blocks through a ring of LDS slots, each block's K and V
+//                    fetched once, the forward's tile-union protocol (only the
+//                    waves that want a block wait for it); per block and
 //                    wanting row group S^T = K Q^T, dP^T = V dO^T, dS from the
 //                    saved log-sum-exp, dQ^T += K^T dS^T (the forward's PV step
 //                    with K in the V-tile role).
@@ -36,6 +38,7 @@
 #include "bwd_tiles.h"
 #include "common.h"
 #include "kernels.h"
+#include "lds_ring.h"
 
 namespace msa {
 namespace {
@@ -60,6 +63,7 @@ struct BwdArgs {
   int32_t* slotpos;      // optional [B][Hkv][Sq][top_k]: list position of each entry, or -1
   int B, Sq, Skv, q_start, Hq, Hkv, G, top_k, nblk, nbatch;
   float scale, scale_log2;
+  int spin_limit;        // ring tag polls before a wave gives up (dq_union_kernel)
 };
 
 __device__ __forceinline__ float wave_sum64(float v) {
@@ -455,58 +459,76 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
   }
 }
 
-// dQ, tile-union schedule (groups of 4 or 8 query heads): a work-group owns
-// 16 consecutive rows of one (sequence, KV head), split into row groups of
-// 16 / G rows x G heads (the 16 MFMA columns), two groups per wave.  A 32-bit
-// mask per block (LDS) records which of the tile's rows selected it; the
-// work-group walks the blocks with a nonzero mask in ascending order, fetching
-// each one's K and V once into double-buffered LDS tiles by LDS-bound loads
-// (the next block's while the current one is computed).  A group computes a
-// block only if one of its rows selected it, and a column whose row did not
-// gets P = 0.  Per block: S^T = K Q^T and dP^T = V dO^T from the tiles, dS,
-// and dQ^T += K^T dS^T.
-//
-// The K and V tiles use the swz_slot layout; dQ^T += K^T dS^T is pv_tr with
-// the K tile.
-constexpr int kDqTileRows = 16;  // 4 waves at G = 8: two work-groups share a CU
+// dQ, ring schedule (groups of 4 or 8 query heads).  A work-group of eight
+// waves owns TR = 32 (G = 8) or 64 (G = 4) consecutive rows of one (sequence,
+// KV head): 16 row groups of 16/G rows x G heads (the 16 MFMA columns), wave w
+// owning groups w and w + 8 with their Q, dO and dQ accumulators in
+// registers.  Per window of kDqWin blocks the work-group builds the row and
+// row-group bitmasks of every block from the rows' selections and walks the
+// union in ascending order; each block's K and V (32 KiB) are fetched once
+// into a ring of kDqRing LDS slots by LDS-bound buffer loads.  The ring runs
+// the forward's tile-union protocol: only the waves owning a group that wants
+// a block wait for its slot's tag, compute and count themselves done; the
+// last of them refills the slot with the entry kDqRing ahead, and an LDS-bound
+// load of the entry number after the data publishes the tag.  Per block and
+// wanting group: S^T = K Q^T, dP^T = V dO^T, P from the saved log-sum-exp
+// (0 for a column whose row did not pick the block and for keys after the
+// row), dS = P (dP - Dsum), dQ^T += K^T dS^T (pv_tr on the K slot).  A group
+// takes its blocks in ascending order, as a row's own list does.  Every tag
+// wait is bounded (the library's wait limit): a work-group that gives up
+// stores NaN for its rows' dq.
+constexpr int kDqWaves = 8;
+constexpr int kDqRing = 4;
+constexpr int kDqWin = 512;  // blocks per union window
+static_assert(kDqWin <= kRingEntries, "ring tags cover a window");
 
+template <int G>
+__global__ void __launch_bounds__(kDqWaves * kWave, 1) dq_union_kernel(BwdArgs a) {
+  constexpr int RPG = 16 / G;           // rows per group
+  constexpr int kNG = 2 * kDqWaves;     // row groups per tile
+  constexpr int TR = kNG * RPG;         // rows per tile
+  constexpr int NWR = (TR + 31) / 32;   // row-mask words per block
+  constexpr int kBlockBytes = kBlock * kHeadDim * 2;
+  __shared__ u32x4 ktile[kDqRing][kBlock * 16];
+  __shared__ u32x4 vtile[kDqRing][kBlock * 16];
+  __shared__ uint32_t rmask[kDqWin][NWR];  // per block: tile rows that picked it
+  __shared__ uint32_t gmask[kDqWin];       // per block: row groups that picked it
+  __shared__ int32_t ulist[kDqWin];        // union entries: block | (waves wanting it) << 24
+  __shared__ int32_t wcount[kDqWaves];
+  __shared__ int32_t ready[kDqRing];       // union entry held by each slot
+  __shared__ int32_t done[kDqRing];        // waves finished with the slot's entry
+  __shared__ int32_t failed;
 
-__global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
-  // K and V of the current and the next block, each tile its own LDS object,
-  // and the block loop unrolled by two so that every access names its tile:
-  // the compiler then tells the LDS-bound loads into one pair from the reads
-  // of the other (and of the row masks) and makes neither wait for them.
-  __shared__ u32x4 ktile0[kBlock * 16], ktile1[kBlock * 16];
-  __shared__ u32x4 vtile0[kBlock * 16], vtile1[kBlock * 16];
-  extern __shared__ uint32_t rmask[];  // [cmax + 1]
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int nwaves = blockDim.x / kWave;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // scalar (LDS destinations in M0)
   const int n = lane % 16, g = lane / 16;
+  const int tile = (int)gridDim.x - 1 - (int)blockIdx.x;  // late (long) tiles first
   const int h = blockIdx.y, b = blockIdx.z;
-  const int RPG = 16 / a.G;  // rows per group
-  const int t0 = blockIdx.x * kDqTileRows;
-  const int rows = min(kDqTileRows, a.Sq - t0);
-  const int cmax = (a.q_start + t0 + rows - 1) / kBlock;
+  const int t0 = tile * TR;
+  const int rows = min(TR, a.Sq - t0);
+  const int pos0 = a.q_start + t0;
+  const int pos_last = pos0 + rows - 1;
+  const int cur_last = pos_last / kBlock;
   const long long hb = (long long)b * a.Hkv + h;
-  for (int c = tid; c <= cmax; c += blockDim.x) rmask[c] = 0u;
-  __syncthreads();
-  const int32_t* srow = a.sel + (hb * a.Sq + t0) * a.top_k;
-  for (int idx = tid; idx < rows * a.top_k; idx += blockDim.x) {
-    const int i = idx / a.top_k;
-    const int c = srow[idx];
-    if (c >= 0 && c <= (a.q_start + t0 + i) / kBlock) atomicOr(&rmask[c], 1u << i);
-  }
-  __syncthreads();
-  // this lane's column in each of the wave's two groups
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.k + hb * a.Skv * kHeadDim), (short)0, a.Skv * kHeadDim * 2, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.v + hb * a.Skv * kHeadDim), (short)0, a.Skv * kHeadDim * 2, kRsrcFlags);
+  const __amdgpu_buffer_rsrc_t rtag = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)&kEntryIds, (short)0, (int)sizeof(kEntryIds), kRsrcFlags);
+  const int32_t* selh = a.sel + (hb * a.Sq + t0) * a.top_k;
+  const int rr = n / G, hh = n % G;  // this lane's column: row in group, head
+
+  // owned groups gi = wave + 8j: this lane's column in each
   bf16x8 qf[2][4], gf[2][4];
   float lse2[2], dsv[2];
-  int pos[2], rloc[2];
+  int pos[2];
   long long colbase[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    rloc[j] = (2 * wave + j) * RPG + n / a.G;
-    const bool ok = rloc[j] < rows;
-    const int t = t0 + (ok ? rloc[j] : 0), hq = h * a.G + n % a.G;
+    const int row = (wave + kDqWaves * j) * RPG + rr;
+    const bool ok = row < rows;
+    const int t = t0 + (ok ? row : 0), hq = h * G + hh;
     colbase[j] = ((long long)b * a.Sq + t) * a.Hq + hq;
     const u32x4* qs = reinterpret_cast<const u32x4*>(a.q + colbase[j] * kHeadDim);
     const u32x4* gs = reinterpret_cast<const u32x4*>(a.dout + colbase[j] * kHeadDim);
@@ -530,41 +552,58 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // first block >= from with a nonzero mask (cmax + 1 if none); same in every wave
-  auto next_block = [&](int from) {
-    for (int base = from; base <= cmax; base += kWave) {
-      const int c = base + lane;
-      const uint64_t bal = ballot(c <= cmax && rmask[c] != 0u);
-      if (bal != 0ull) return base + (int)__builtin_ctzll(bal);
-    }
-    return cmax + 1;
+  if (tid == 0) failed = 0;
+
+  // Slot fill: instruction j of a block's K (or V) covers key rows 4j..4j+3,
+  // lane -> row 4j + lane/16, LDS chunk lane%16, which holds the row's chunk
+  // (lane%16) ^ (row & 15) (the swz_slot layout; the lane's offset depends on
+  // j mod 4 only).  The diagonal block re-reads its last used row in place of
+  // later ones (masked keys, kept finite).
+  auto koff = [&](int jm) {
+    return (lane / 16) * 256 + 16 * ((lane % 16) ^ kswz(4 * jm + lane / 16));
   };
-  // LDS-bound loads of block c's K and V into tiles bf: load inst writes key
-  // rows 4 inst .. 4 inst + 3, lane -> row 4 inst + lane/16, stored chunk lane%16
-  auto fetch = [&](int c, u32x4* kdst, u32x4* vdst) {
-    const long long off0 = (hb * a.Skv + (long long)c * kBlock) * kHeadDim;
-    for (int inst = wave; inst < 16; inst += nwaves) {
-      const int slot = inst * kWave + lane;
-      const int key = slot >> 4;
-      const int ch = (slot & 15) ^ (key & 15);
-      const int krow = min(c * kBlock + key, a.Skv - 1) - c * kBlock;  // rows past the cache: masked
-      const long long e = off0 + (long long)krow * kHeadDim + 8 * ch;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.k + e),
-                                       (__attribute__((address_space(3))) void*)(kdst + inst * kWave),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.v + e),
-                                       (__attribute__((address_space(3))) void*)(vdst + inst * kWave),
-                                       16, 0, 0);
+  auto fetch_rows = [&](int c, int sl, int j0, int j1) {
+    const int sb = c * kBlockBytes;
+    const int last = min(pos_last - c * kBlock, kBlock - 1);
+    for (int j = j0; j < j1; ++j) {
+      const int row = 4 * j + lane / 16, srow = min(row, last);
+      const int off = srow * 256 + 16 * ((lane % 16) ^ kswz(row));
+      load_lds16(rk, &ktile[sl][j * kWave], off, sb);
+      load_lds16(rv, &vtile[sl][j * kWave], off, sb);
     }
   };
-  // block c from tiles (kt, vt)
-  auto compute = [&](int c, const u32x4* kt, const u32x4* vt) {
-    const uint32_t m = rmask[c];
+  auto fetch_full = [&](int c, int sl) {
+    const int sb = c * kBlockBytes;
+    if (c * kBlock + kBlock - 1 <= pos_last) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int off = koff(j & 3);
+        load_lds16(rk, &ktile[sl][j * kWave], off, sb + j * 1024);
+        load_lds16(rv, &vtile[sl][j * kWave], off, sb + j * 1024);
+      }
+    } else {
+      fetch_rows(c, sl, 0, 16);
+    }
+  };
+
+  // block c from slot sl for the wave's groups that want it
+  auto compute = [&](int sl, int c, uint32_t gm, const uint32_t* rm) {
+    const u32x4* kt = &ktile[sl][0];
+    const u32x4* vt = &vtile[sl][0];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int grp = 2 * wave + j;
-      if (((m >> (grp * RPG)) & ((1u << RPG) - 1u)) == 0u) continue;  // wave-uniform
-      const bool wants = (m >> rloc[j]) & 1u;
+      const int gi = wave + kDqWaves * j;
+      if (!((gm >> gi) & 1u)) continue;  // wave-uniform
+      const int row = gi * RPG + rr;
+      const bool wants = (rm[row / 32] >> (row % 32)) & 1u;
+      // the lane's operand bytes in a slot: row 16 mt + n, chunk 4 ks + g at
+      // swz_slot, i.e. 4096 mt + kb[ks]
+      uint32_t kb[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        kb[ks] = 256u * n + 16u * ((4 * ks + g) ^ n);
+        asm volatile("" : "+v"(kb[ks]));
+      }
       f32x4 sv[4], dp[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -572,8 +611,8 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
         dp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 kf = as_bf16x8(kt[swz_slot(16 * mt + n, 4 * ks + g)]);
-          const bf16x8 vf = as_bf16x8(vt[swz_slot(16 * mt + n, 4 * ks + g)]);
+          const bf16x8 kf = as_bf16x8(lds_u32x4_at(kt, kb[ks] + 4096 * mt));
+          const bf16x8 vf = as_bf16x8(lds_u32x4_at(vt, kb[ks] + 4096 * mt));
           sv[mt] = mfma16(kf, qf[j][ks], sv[mt]);
           dp[mt] = mfma16(vf, gf[j][ks], dp[mt]);
         }
@@ -581,39 +620,129 @@ __global__ void __launch_bounds__(512) dq_tile_kernel(BwdArgs a) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int key = c * kBlock + 16 * mt + 4 * g + rr;
-          const float p = (wants && key <= pos[j])
-                              ? exp2f(sv[mt][rr] * a.scale_log2 - lse2[j]) : 0.f;
-          sv[mt][rr] = p * (dp[mt][rr] - dsv[j]);
+        for (int r = 0; r < 4; ++r) {
+          const int key = c * kBlock + 16 * mt + 4 * g + r;
+          const float p = (wants && key <= pos[j]) ? exp2f(sv[mt][r] * a.scale_log2 - lse2[j]) : 0.f;
+          sv[mt][r] = p * (dp[mt][r] - dsv[j]);
         }
       pv_tr(sv, kt, acc[j]);  // dQ^T += K^T dS^T
     }
   };
-  int c = next_block(0);
-  if (c <= cmax) fetch(c, ktile0, vtile0);
-  while (c <= cmax) {
-    // tiles 0 hold block c; block cn goes to tiles 1
-    int cn = next_block(c + 1);
-    wait_all_loads();
-    __syncthreads();  // block c's tiles complete in every wave
-    if (cn <= cmax) fetch(cn, ktile1, vtile1);
-    compute(c, ktile0, vtile0);
-    __syncthreads();  // tiles 0 free for the block after cn
-    c = cn;
-    if (c > cmax) break;
-    // tiles 1 hold block c; block cn goes to tiles 0
-    cn = next_block(c + 1);
-    wait_all_loads();
+
+  bool ok_run = true;
+  for (int wb = 0; wb <= cur_last && ok_run; wb += kDqWin) {
+    const int we = min(wb + kDqWin, cur_last + 1);
+    // 1. row and group bitmasks of the window's blocks
+    for (int x = tid; x < kDqWin * NWR; x += kDqWaves * kWave) (&rmask[0][0])[x] = 0u;
+    for (int x = tid; x < kDqWin; x += kDqWaves * kWave) gmask[x] = 0u;
+    if (tid < kDqRing) {
+      ready[tid] = -1;
+      done[tid] = 0;
+    }
     __syncthreads();
-    if (cn <= cmax) fetch(cn, ktile0, vtile0);
-    compute(c, ktile1, vtile1);
-    __syncthreads();  // tiles 1 free for the block after cn
-    c = cn;
+    {
+      constexpr int parts = kDqWaves * kWave / TR;
+      const int row = tid % TR, part = tid / TR;
+      if (row < rows) {
+        const int cur = (pos0 + row) / kBlock;
+        const int32_t* lst = selh + (size_t)row * a.top_k;
+        for (int x = part; x < a.top_k; x += parts) {
+          const int c = lst[x];
+          if (c >= wb && c < we && c <= cur) {
+            atomicOr(&rmask[c - wb][row / 32], 1u << (row % 32));
+            atomicOr(&gmask[c - wb], 1u << (row / RPG));
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // 2. union list of the window, ascending, with the waves that want each entry
+    int nu = 0;
+    for (int j = 0; j < kDqWin; j += kDqWaves * kWave) {
+      const int pidx = j + tid;
+      const uint32_t gmv = pidx < we - wb ? gmask[pidx] : 0u;
+      const bool nz = gmv != 0u;
+      const uint64_t bal = ballot(nz);
+      if (lane == 0) wcount[wave] = __popcll(bal);
+      __syncthreads();
+      int before = nu;
+      for (int w = 0; w < wave; ++w) before += wcount[w];
+      if (nz) {
+        const uint32_t wbits = (gmv | (gmv >> kDqWaves)) & 0xffu;
+        ulist[before + prefix_count(bal)] = (wb + pidx) | (int)(wbits << 24);
+      }
+#pragma unroll
+      for (int w = 0; w < kDqWaves; ++w) nu += wcount[w];
+      __syncthreads();
+    }
+    // 3. first kDqRing entries: every wave moves 2 of the 16 instructions of each
+    for (int s = 0; s < kDqRing && s < nu; ++s)
+      fetch_rows(ulist[s] & 0xffffff, s, 2 * wave, 2 * wave + 2);
+    wait_vm(0);
+    __syncthreads();
+    if (tid < kDqRing && tid < nu) ready[tid] = tid;
+    __syncthreads();
+    // 4. decoupled sweep over the entries this wave wants
+    for (int u0 = 0; u0 < nu && ok_run; u0 += kWave) {
+      const int ue = u0 + lane < nu ? ulist[u0 + lane] : 0;
+      uint64_t mine = ballot(u0 + lane < nu && ((ue >> (24 + wave)) & 1));
+      while (mine != 0ull) {
+        const int bit = __builtin_ctzll(mine);
+        mine &= mine - 1;
+        const int u = u0 + bit;
+        const int e = __builtin_amdgcn_readlane(ue, bit);
+        const int c = e & 0xffffff;
+        const int need = __builtin_popcount((uint32_t)e >> 24);
+        const int sl = u % kDqRing;
+        // a wave's LDS operations complete in order, so once the tag reads u
+        // the slot's data reads below see the block
+        if (lds_load_tag(&ready[sl]) != u) {
+          int spins = 0;
+          while (lds_load_tag(&ready[sl]) != u) {
+            if (++spins > a.spin_limit) {
+              ok_run = false;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+          }
+          if (!ok_run) {
+            if (lane == 0) failed = 1;
+            break;
+          }
+        }
+        // the wave holding a slot issues ahead of its SIMD's other wave until
+        // its refill (if it is the last wanting wave) has gone out
+        cbarrier();
+        __builtin_amdgcn_s_setprio(2);
+        compute(sl, c, gmask[c - wb], rmask[c - wb]);
+        cbarrier();
+        int prev = 0;
+        if (lane == 0) prev = lds_fetch_add_tag(&done[sl], 1);
+        prev = __builtin_amdgcn_readfirstlane(prev);
+        if (prev == need - 1) {
+          // the count is reset before the loads are issued; the tag that lets
+          // the next entry's waves in is written after the block's data
+          if (lane == 0) lds_store_tag(&done[sl], 0);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          if (u + kDqRing < nu) {
+            fetch_full(ulist[u + kDqRing] & 0xffffff, sl);
+            if (lane == 0)
+              __builtin_amdgcn_raw_ptr_buffer_load_lds(rtag, (lds_ptr)&ready[sl], 4, 0,
+                                                       (u + kDqRing) * 4, 0, 0);
+          }
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
+    wait_vm(0);
+    __syncthreads();
+    if (failed) ok_run = false;
   }
+  // a failed sweep (bounded wait exceeded) stores NaN so the caller sees it
+  const float mul = ok_run ? a.scale : __builtin_nanf("");
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    if (rloc[j] < rows) store_tr_f32(acc[j], a.dq + colbase[j] * kHeadDim, a.scale);
+    if ((wave + kDqWaves * j) * RPG + rr < rows) store_tr_f32(acc[j], a.dq + colbase[j] * kHeadDim, mul);
 }
 
 }  // namespace
@@ -703,12 +832,13 @@ hipError_t launch_sparse_attn_backward(const Shape& s, const void* q, const void
   a.base = const_cast<int32_t*>(base);
   a.lists = const_cast<int32_t*>(lists);
   if (s.G == 4 || s.G == 8) {
-    const size_t dq_lds = (size_t)s.nblk * 4;  // the row masks (the tiles are static)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dq_tile_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dq_lds);
-    if (e != hipSuccess) return e;
-    const int waves = (kDqTileRows / (16 / s.G)) / 2;  // two row groups per wave
-    dq_tile_kernel<<<dim3(ceil_div(s.Sq, kDqTileRows), s.Hkv, s.B), waves * kWave, dq_lds, st>>>(a);
+    // the buffer descriptors address one head's K or V with 32-bit byte offsets
+    if ((long long)s.Skv * kHeadDim * 2 > 0x7fffffffLL) return hipErrorInvalidValue;
+    a.spin_limit = union_spin_limit();
+    const int TR = 2 * kDqWaves * (16 / s.G);
+    const dim3 grid(ceil_div(s.Sq, TR), s.Hkv, s.B);
+    if (s.G == 8) dq_union_kernel<8><<<grid, kDqWaves * kWave, 0, st>>>(a);
+    else dq_union_kernel<4><<<grid, kDqWaves * kWave, 0, st>>>(a);
   } else {
     const long long nw = (long long)s.B * s.Hkv * s.Sq;
     dq_kernel<<<(unsigned)((nw + 3) / 4), 256, 0, st>>>(a);

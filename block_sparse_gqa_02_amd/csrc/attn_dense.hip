@@ -30,10 +30,6 @@ constexpr int kRing = 4;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
-
 struct DenseArgs {
   const uint16_t* q;
   const uint16_t* k;

@@ -62,7 +62,6 @@ constexpr int kRing = 4;           // K/V slots in the LDS ring
 constexpr int kDefaultSpinLimit = 1 << 22;  // tag polls before a wave gives up
 constexpr int kStatusBytes = 256;           // failure word at the end of the workspace
 constexpr int kBlockBytes = kBlock * kHeadDim * 2;  // one K or V block
-constexpr int kRsrcFlags = 0x00020000;              // raw buffer descriptor word 3
 
 struct UnionArgs {
   const uint16_t* q;    // [B][Sq][Hq][128]
@@ -124,53 +123,7 @@ __global__ void __launch_bounds__(256) vt_kernel(VtArgs a) {
   }
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
-}
-
-// Ring-tag accesses as plain LDS instructions.  The compiler would otherwise
-// put a wait for every outstanding LDS-bound buffer load in front of them; the
-// kernel orders them against those loads with its own vmcnt waits.
-__device__ __forceinline__ int lds_load_tag(const int32_t* p) {
-  int v;
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
-  return v;
-}
-__device__ __forceinline__ void lds_store_tag(int32_t* p, int v) {
-  asm volatile("ds_write_b32 %0, %1" :: "v"(lds_addr(p)), "v"(v) : "memory");
-}
-__device__ __forceinline__ int lds_fetch_add_tag(int32_t* p, int v) {
-  int old;
-  asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
-               : "=v"(old) : "v"(lds_addr(p)), "v"(v) : "memory");
-  return old;
-}
-
-// s_waitcnt vmcnt(n) for n in {0, 32}, expcnt and lgkmcnt unconstrained
-// (vmcnt bits 3:0 and 15:14).
-__device__ __forceinline__ void wait_vm(int n) {
-  cbarrier();
-  if (n == 0) __builtin_amdgcn_s_waitcnt(0xf70);
-  else __builtin_amdgcn_s_waitcnt(0xf70 | (2 << 14));  // vmcnt = 32
-  cbarrier();
-}
-
-// One 16-byte LDS-bound buffer load per lane: LDS bytes dst + 16 * lane
-// receive bytes voff + soff of the descriptor's range (reads past the range
-// return zero).
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, const void* dst, int voff,
-                                           int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)dst, 16, voff, soff, 0, 0);
-}
-
-// Entry numbers 0..kWin-1, the source of the ring tags written by LDS-bound loads.
-struct EntryIds {
-  int32_t v[kWin];
-  constexpr EntryIds() : v() {
-    for (int i = 0; i < kWin; ++i) v[i] = i;
-  }
-};
-__device__ const EntryIds kEntryIds{};
+static_assert(kWin <= kRingEntries, "ring tags cover a window");
 
 template <int G>
 __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionArgs a) {
@@ -531,6 +484,8 @@ size_t union_prefill_status_offset(const Shape& s) { return vt_bytes(s); }
 static std::atomic<int> g_spin_limit{kDefaultSpinLimit};
 
 void set_union_spin_limit(int spins) { g_spin_limit.store(spins > 0 ? spins : kDefaultSpinLimit); }
+
+int union_spin_limit() { return g_spin_limit.load(); }
 
 hipError_t launch_vt_tiles(const Shape& s, const void* v, void* ws, hipStream_t st) {
   const int nblk_ctx = context_blocks(s);

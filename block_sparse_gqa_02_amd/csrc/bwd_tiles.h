@@ -34,6 +34,14 @@ __device__ __forceinline__ s16x4 lds_read_tr_at(const void* tile, uint32_t off) 
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)((lds_cchar_ptr)tile + off));
 }
 
+// The 16 bytes at byte `off` of the LDS tile `tile` (one step from the tile
+// pointer, like lds_read_tr_at).
+__device__ __forceinline__ u32x4 lds_u32x4_at(const void* tile, uint32_t off) {
+  typedef __attribute__((address_space(3))) const char* lds_cchar_ptr;
+  typedef __attribute__((address_space(3))) const u32x4* lds_u32x4_ptr;
+  return *(lds_u32x4_ptr)((lds_cchar_ptr)tile + off);
+}
+
 // The 16-bit word at byte `off` of the LDS tile `tile`, addressed like
 // lds_read_tr_at (one step from the tile pointer).
 __device__ __forceinline__ uint32_t lds_u16_at(const void* tile, uint32_t off) {

@@ -99,8 +99,10 @@ bool union_prefill_supported(const Shape& s);
 size_t union_prefill_workspace_bytes(const Shape& s);
 // Byte offset of the int32 failure word in the tile-union workspace.
 size_t union_prefill_status_offset(const Shape& s);
-// Polls of a ring tag before a wave gives up (<= 0 restores the default).
+// Polls of a ring tag before a wave gives up (<= 0 restores the default); the
+// bound of every ring kernel (tile-union prefill and its dQ).
 void set_union_spin_limit(int spins);
+int union_spin_limit();
 hipError_t launch_union_prefill(const Shape& s, const void* q, const void* k, const void* v,
                                 const int32_t* sel, void* out, float* lse, void* ws,
                                 hipStream_t st);

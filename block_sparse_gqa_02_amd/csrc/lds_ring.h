@@ -18,6 +18,61 @@ __device__ __forceinline__ int vswz(int row) { return (row & 7) << 1; }
 // Compiler-only memory barrier (no instruction).
 __device__ __forceinline__ void cbarrier() { asm volatile("" ::: "memory"); }
 
+// LDS byte address of a pointer into a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// Ring-tag accesses as plain LDS instructions.  The compiler would otherwise
+// put a wait for every outstanding LDS-bound buffer load in front of them; the
+// ring kernels order them against those loads with their own vmcnt waits.
+__device__ __forceinline__ int lds_load_tag(const int32_t* p) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(p)) : "memory");
+  return v;
+}
+__device__ __forceinline__ void lds_store_tag(int32_t* p, int v) {
+  asm volatile("ds_write_b32 %0, %1" :: "v"(lds_addr(p)), "v"(v) : "memory");
+}
+__device__ __forceinline__ int lds_fetch_add_tag(int32_t* p, int v) {
+  int old;
+  asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+               : "=v"(old) : "v"(lds_addr(p)), "v"(v) : "memory");
+  return old;
+}
+
+// s_waitcnt vmcnt(n) for n in {0, 32}, expcnt and lgkmcnt unconstrained
+// (vmcnt bits 3:0 and 15:14).
+__device__ __forceinline__ void wait_vm(int n) {
+  cbarrier();
+  if (n == 0) __builtin_amdgcn_s_waitcnt(0xf70);
+  else __builtin_amdgcn_s_waitcnt(0xf70 | (2 << 14));  // vmcnt = 32
+  cbarrier();
+}
+
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer descriptor word 3
+
+// One 16-byte LDS-bound buffer load per lane: LDS bytes dst + 16 * lane
+// receive bytes voff + soff of the descriptor's range (reads past the range
+// return zero).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, const void* dst, int voff,
+                                           int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)dst, 16, voff, soff, 0, 0);
+}
+
+// Entry numbers 0..kRingEntries-1, the source of the ring tags written by
+// LDS-bound loads (a union window holds at most this many entries).
+constexpr int kRingEntries = 512;
+struct RingEntryIds {
+  int32_t v[kRingEntries];
+  constexpr RingEntryIds() : v() {
+    for (int i = 0; i < kRingEntries; ++i) v[i] = i;
+  }
+};
+namespace {
+__device__ const RingEntryIds kEntryIds{};
+}  // namespace
+
 // s_barrier without the memory fences of __syncthreads: the kernels order
 // their global->LDS loads with explicit vmcnt waits instead.
 __device__ __forceinline__ void raw_barrier() {

@@ -305,7 +305,11 @@ msa_status msa_sparse_attn_decode_paged(const msa_problem* p, const void* q,
  * block bitmap lives in LDS).  workspace: msa_workspace_bytes(p,
  * MSA_OP_SPARSE_ATTN_PREFILL_BACKWARD) bytes, any contents.  bf16 products
  * (P and dS rounded to bf16, as P is in the forward), fp32 accumulation;
- * deterministic (no floating-point atomics). */
+ * deterministic (no floating-point atomics).  For group sizes 4 and 8 the dq
+ * pass shares blocks between rows through an LDS ring with bounded waits (as
+ * msa_sparse_attn_prefill does): should a wait give up (in practice only
+ * under msa_set_wait_limit), the rows of the affected tiles get NaN dq and
+ * the call still returns MSA_OK. */
 msa_status msa_sparse_attn_prefill_backward(const msa_problem* p, const void* q, const void* k,
                                             const void* v, const int32_t* sel, const void* out,
                                             const float* lse, const void* dout, float* dq,
@@ -347,9 +351,9 @@ msa_status msa_index_kl_backward(const msa_problem* p, const void* q, const void
 msa_status msa_sparse_attn_prefill_status_offset(const msa_problem* p, size_t* offset);
 
 /* Testing only: the number of polls of a ring tag after which a wave of the
- * sparse prefill gives up (process-wide; <= 0 restores the default, 2^22).
- * A tiny bound forces the failure path above with every kernel still
- * exiting normally. */
+ * sparse prefill (and of its gradient's dq pass) gives up (process-wide; <= 0
+ * restores the default, 2^22).  A tiny bound forces the failure paths above
+ * with every kernel still exiting normally. */
 void msa_set_wait_limit(int32_t polls);
 
 /* Workspace bytes an operation needs for problem p (0 if none).  Host only. */

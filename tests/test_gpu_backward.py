@@ -4,7 +4,7 @@ same bf16 inputs, every element compared.  Sizes span several 64-row batches
 and 64-key blocks with ragged tails, rows that precede k blocks (short, padded
 lists), a chunk whose rows start past 0 with a cache longer than the rows
 (blocks no row reads: their dk, dv must be exactly zero), query groups of
-2, 4, 8 and 16 heads (4 and 8 take the tile-union dq kernel, the others the
+2, 4, 8 and 16 heads (4 and 8 take the ring dq kernel, the others the
 per-row one), and row lists of hundreds of 64-column chunks.
 
 Tolerance, per tensor, from the arithmetic: the kernels round P and dS to
@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import block_sparse_gqa_02_amd as msa
-from block_sparse_gqa_02_amd.configs import TINY_PREFILL_2K
+from block_sparse_gqa_02_amd.configs import PREFILL_32K, TINY_PREFILL_2K
 from block_sparse_gqa_02_amd.inputs import cotangent, generate
 import oracle.oracle as O
 
@@ -98,6 +98,39 @@ def test_backward_matches_oracle(case):
         print(f"  {name}: max {mx:.2e} mean {mn:.2e} (of the reference's max / mean magnitude)",
               flush=True)
         assert mx <= MAX_REL and mn <= MEAN_REL, (name, mx, mn)
+
+
+def test_backward_bounded_wait_failure_gives_nan():
+    """The tile-union dq pass waits on its ring's tags with the library's
+    bound.  Forced down to one poll from the host, waves give up early: every
+    kernel still exits normally and rows of the affected tiles get NaN dq, while
+    dk and dv (a pass with no waits) are unchanged.  With the default bound
+    restored the call equals one made before the knob was touched."""
+    need_gpu()
+    w = PREFILL_32K.shrink(seq_q=4096, seq_kv=4096)
+    inp = generate(w, "cuda")
+    p = msa.Problem.from_workload(w)
+    sel = msa.msa_topk_blocks(p, msa.msa_index_block_scores(p, inp.iq, inp.ik))
+    lse = torch.empty((w.batch, w.n_q_heads, w.seq_q), dtype=torch.float32, device="cuda")
+    out = msa.msa_sparse_attn_prefill(p, inp.q, inp.k, inp.v, sel, lse=lse)
+    dout = cotangent(out, w.seed + 7)
+    ref = msa.msa_sparse_attn_prefill_backward(p, inp.q, inp.k, inp.v, sel, out, lse, dout)
+    torch.cuda.synchronize()
+    assert all(bool(torch.isfinite(t).all()) for t in ref)
+    try:
+        msa.msa_set_wait_limit(1)
+        bad = msa.msa_sparse_attn_prefill_backward(p, inp.q, inp.k, inp.v, sel, out, lse, dout)
+        torch.cuda.synchronize()
+        nan_rows = int(torch.isnan(bad[0]).any(dim=3).any(dim=2).sum().item())  # [B][Sq]
+        print(f"forced give-up: rows with NaN dq {nan_rows} of {w.seq_q}", flush=True)
+        assert nan_rows > 0
+        assert torch.equal(bad[1], ref[1]) and torch.equal(bad[2], ref[2])
+    finally:
+        msa.msa_set_wait_limit(0)
+    again = msa.msa_sparse_attn_prefill_backward(p, inp.q, inp.k, inp.v, sel, out, lse, dout)
+    torch.cuda.synchronize()
+    for a, b in zip(again, ref):
+        assert torch.equal(a, b)
 
 
 def _row_oracle_dq(w, inp, sel, dout, t):
