@@ -196,3 +196,42 @@ def test_backward_128k_sampled_rows_and_sum_rules():
     mx, mn = rel_errors(gq, ref)
     print(f"  dq on {len(rows)} rows: max {mx:.2e} mean {mn:.2e}", flush=True)
     assert mx <= MAX_REL and mn <= MEAN_REL, (mx, mn)
+
+
+def test_backward_g4_rows_past_one_union_window():
+    """Groups of 4 (64-row tiles in the ring dq kernel) over rows whose causal
+    range spans two 512-block union windows: 1500 rows at q_start 38000 of a
+    40000-token cache, k = 24.  dk and dv through the sum rules, dq of a row
+    sample on both sides of the window boundary against the oracle (compact
+    per-row problems)."""
+    need_gpu()
+    import parity as PAR
+    w = TINY_PREFILL_2K.shrink(name="bwd_g4_roll", seq_q=1500, seq_kv=40000, q_start=38000,
+                               n_q_heads=16, n_kv_heads=4, top_k=24)
+    print(f"[backward] {w.name}: Sq={w.seq_q} Skv={w.seq_kv} q_start={w.q_start} G={w.group}",
+          flush=True)
+    inp = generate(w, "cuda")
+    p = msa.Problem.from_workload(w)
+    sel = msa.msa_topk_blocks(p, msa.msa_index_block_scores(p, inp.iq, inp.ik))
+    assert int(sel.max()) >= 512 and int(sel[sel >= 0].min()) < 512  # both windows are read
+    lse = torch.empty((w.batch, w.n_q_heads, w.seq_q), dtype=torch.float32, device="cuda")
+    out = msa.msa_sparse_attn_prefill(p, inp.q, inp.k, inp.v, sel, lse=lse)
+    dout = cotangent(out, w.seed + 7)
+    dq, dk, dv = msa.msa_sparse_attn_prefill_backward(p, inp.q, inp.k, inp.v, sel, out, lse, dout)
+    torch.cuda.synchronize()
+    G = w.group
+    sk = dk.double().sum(dim=2)
+    ak = dk.double().abs().sum(dim=2)
+    want = dout.double().reshape(w.batch, w.seq_q, w.n_kv_heads, G, w.head_dim).sum(dim=(1, 3))
+    sv = dv.double().sum(dim=2)
+    av = dv.double().abs().sum(dim=2)
+    rk = float((sk.abs() / ak).max())
+    rv = float(((sv - want).abs() / av).max())
+    print(f"  sum rules: {rk:.2e} {rv:.2e}", flush=True)
+    assert rk <= 5e-4 and rv <= 5e-4, (rk, rv)
+    rows = PAR.sample_rows(w.seq_q, w.q_start, w.block_size, seed=11, n_uniform=96, n_log=8)
+    gq = f64(dq[0, torch.as_tensor(rows, device="cuda")])
+    ref = np.stack([_row_oracle_dq(w, inp, sel, dout, int(t)) for t in rows])
+    mx, mn = rel_errors(gq, ref)
+    print(f"  dq on {len(rows)} rows: max {mx:.2e} mean {mn:.2e}", flush=True)
+    assert mx <= MAX_REL and mn <= MEAN_REL, (mx, mn)
