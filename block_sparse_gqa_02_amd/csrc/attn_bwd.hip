@@ -66,12 +66,6 @@ struct BwdArgs {
   int spin_limit;        // ring tag polls before a wave gives up (dq_union_kernel)
 };
 
-__device__ __forceinline__ float wave_sum64(float v) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
 // acc += T^T P^T over one tile T (swz_slot layout; its 64 rows are the
 // contraction index) with P^T in S^T register layout: pt[mt] register r is
 // tile row 16mt + 4g + r, column n; rounded to bf16 here.  The T^T operand is
@@ -114,19 +108,35 @@ __device__ __forceinline__ void store_tr_f32(const f32x4 (&acc)[8], float* col_b
   for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(col_base + 16 * mt + 4 * g) = acc[mt] * mul;
 }
 
-// Dsum[b][hq][t] = sum_d dout * out; one wave per (b, t, hq), lanes over dim pairs.
+// Dsum[b][hq][t] = sum_d dout * out per column (b, t, hq): 16 lanes per
+// column, 16 bytes (8 dims) each, summed over the 16 lanes; a thread takes
+// kDsumCols columns 16 apart, every load issued before any is used.
+constexpr int kDsumCols = 4;
 __global__ void __launch_bounds__(256) dsum_kernel(BwdArgs a) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const long long w = (long long)blockIdx.x * 4 + wave;  // (b * Sq + t) * Hq + hq
-  if (w >= (long long)a.B * a.Sq * a.Hq) return;
-  const uint32_t o2 = reinterpret_cast<const uint32_t*>(a.out + w * kHeadDim)[lane];
-  const uint32_t g2 = reinterpret_cast<const uint32_t*>(a.dout + w * kHeadDim)[lane];
-  const float s = wave_sum64(bf16_lo(o2) * bf16_lo(g2) + bf16_hi(o2) * bf16_hi(g2));
-  if (lane == 0) {
-    const int hq = (int)(w % a.Hq);
-    const long long bt = w / a.Hq;
-    const int t = (int)(bt % a.Sq), b = (int)(bt / a.Sq);
-    a.dsum[((long long)b * a.Hq + hq) * a.Sq + t] = s;
+  const long long ncol = (long long)a.B * a.Sq * a.Hq;
+  const int sub = threadIdx.x & 15;  // this lane's 8 dims: 8 sub .. 8 sub + 7
+  const long long col0 = (long long)blockIdx.x * (16 * kDsumCols) + (threadIdx.x >> 4);
+  u32x4 ov[kDsumCols], gv[kDsumCols];
+#pragma unroll
+  for (int i = 0; i < kDsumCols; ++i) {
+    const long long col = min(col0 + 16 * i, ncol - 1);
+    ov[i] = reinterpret_cast<const u32x4*>(a.out + col * kHeadDim)[sub];
+    gv[i] = reinterpret_cast<const u32x4*>(a.dout + col * kHeadDim)[sub];
+  }
+#pragma unroll
+  for (int i = 0; i < kDsumCols; ++i) {
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s += bf16_lo(ov[i][k]) * bf16_lo(gv[i][k]) + bf16_hi(ov[i][k]) * bf16_hi(gv[i][k]);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);  // within the column's 16 lanes
+    const long long col = col0 + 16 * i;
+    if (sub == 0 && col < ncol) {
+      const int hq = (int)(col % a.Hq);
+      const long long bt = col / a.Hq;
+      const int t = (int)(bt % a.Sq), b = (int)(bt / a.Sq);
+      a.dsum[((long long)b * a.Hq + hq) * a.Sq + t] = s;
+    }
   }
 }
 
@@ -826,7 +836,7 @@ hipError_t launch_sparse_attn_backward(const Shape& s, const void* q, const void
             nullptr, s.B, s.Sq, s.Skv, s.q_start, s.Hq, s.Hkv, s.G, s.top_k, s.nblk,
             ceil_div(s.Sq, kBatchRows), s.scale, s.scale * kLog2eB};
   const long long nrows = (long long)s.B * s.Sq * s.Hq;
-  dsum_kernel<<<(unsigned)((nrows + 3) / 4), 256, 0, st>>>(a);
+  dsum_kernel<<<(unsigned)((nrows + 16 * kDsumCols - 1) / (16 * kDsumCols)), 256, 0, st>>>(a);
   hipError_t e = launch_inverse_lists(s, sel, p, &base, &lists, st);
   if (e != hipSuccess) return e;
   a.base = const_cast<int32_t*>(base);
