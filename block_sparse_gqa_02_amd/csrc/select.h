@@ -119,6 +119,26 @@ __device__ __forceinline__ uint32_t wave_mth_key2(uint32_t a, uint32_t b, int m)
   return V;
 }
 
+// A lower bound on the m-th largest of the 128 keys held in (a, b) over the
+// wave (zeros pad), or 0 when fewer than m of them are nonzero: the bisection
+// of wave_mth_key2 stopped at bit 16, so the bound has its low 16 bits clear
+// and at least m keys reach it.  Half the steps of the exact form; as a
+// filter threshold it admits only the keys sharing the m-th largest's top 16
+// bits (sign, exponent, 7 mantissa bits) in addition.  Wave-uniform.
+__device__ __forceinline__ uint32_t wave_mth_key2_lb(uint32_t a, uint32_t b, int m) {
+  const uint32_t mx = wave_reduce_uniform<true>(max(a, b));
+  const uint32_t mn = wave_reduce_uniform<false>(min(a, b));
+  if (mx == mn) return m <= 2 * kWave && mx != 0 ? mx : 0u;
+  const int top = 31 - __builtin_clz(mx ^ mn);
+  const uint32_t low = (top == 31) ? 0xffffffffu : ((2u << top) - 1u);
+  uint32_t V = mx & ~low;  // every key is >= V
+  for (int bit = top; bit >= 16; --bit) {
+    const uint32_t T = V | (1u << bit);
+    if (__popcll(ballot(a >= T)) + __popcll(ballot(b >= T)) >= m) V = T;
+  }
+  return __popcll(ballot(a >= V)) + __popcll(ballot(b >= V)) >= m ? V : 0u;
+}
+
 // Compacts entries [0, n) of (keys, idxs) (any address space, ascending idx
 // order, n > m >= 1, n <= 64 * MAXE) in place to the m entries with the
 // largest (key, -idx), preserving order; returns the m-th largest key.
@@ -225,7 +245,7 @@ __device__ __forceinline__ void stream_candidates(const float* src, int c_beg, i
         k2 = max(k2, min(k1, kk[i]));
         k1 = max(k1, kk[i]);
       }
-      const uint32_t T = wave_mth_key2(k1, k2, m);
+      const uint32_t T = wave_mth_key2_lb(k1, k2, m);
       if (T > thr) thr = T - 1u;
     }
 #pragma unroll
