@@ -686,24 +686,41 @@ __global__ void __launch_bounds__(256) kl_merge_kernel(KlArgs a) {
   const int t = (int)(bt % a.Sq), b = (int)(bt / a.Sq);
   const int h = i % a.Hkv, m = i / a.Hkv;
   const int32_t* sp = a.slotpos + (((long long)b * a.Hkv + h) * a.Sq + t) * a.top_k;
-  float acc = 0.f, ls = 0.f;
-  // eight slots' partials loaded together, then added in slot order
-  for (int s0 = 0; s0 < a.top_k; s0 += 8) {
-    float vq[8], vl[8];
+  // lane (q, c4): slots q, q + 4, q + 8, ... (16 lanes per slot), dims 4 c4 .. 4 c4 + 3
+  const int q = lane >> 4, c4 = lane & 15;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float ls = 0.f;
+  // eight slots per lane quarter per batch (32 slots), every load issued
+  // before any is used; a quarter adds its slots in ascending order, and the
+  // quarters are combined in a fixed order below (deterministic)
+  for (int s0 = 0; s0 < a.top_k; s0 += 32) {
+    int ev[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) ev[x] = sp[min(s0 + 4 * x + q, a.top_k - 1)];
+    f32x4 vq[8];
+    float vl[8];
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      const int e = s0 + x < a.top_k ? sp[s0 + x] : -1;
-      const long long pe = (long long)(e >= 0 ? e : 0) * a.nih + m;
-      vq[x] = e >= 0 ? a.part_q[pe * kIdxDim + lane] : 0.f;
-      vl[x] = e >= 0 ? a.part_l[pe] : 0.f;
+      const long long pe = (long long)max(ev[x], 0) * a.nih + m;
+      vq[x] = *reinterpret_cast<const f32x4*>(a.part_q + pe * kIdxDim + 4 * c4);
+      vl[x] = a.part_l[pe];
     }
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      acc += vq[x];
-      ls += vl[x];
+      const bool ok = s0 + 4 * x + q < a.top_k && ev[x] >= 0;
+      acc += ok ? vq[x] : f32x4{0.f, 0.f, 0.f, 0.f};
+      ls += ok ? vl[x] : 0.f;
     }
   }
-  a.diq[w * kIdxDim + lane] = acc;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    acc[k] += __shfl_xor(acc[k], 16);
+    acc[k] += __shfl_xor(acc[k], 32);
+  }
+  ls += __shfl_xor(ls, 16);
+  ls += __shfl_xor(ls, 32);
+  // every quarter now holds the total: lane (q, c4) stores dim 4 c4 + q
+  a.diq[w * kIdxDim + 4 * c4 + q] = acc[q];
   if (lane == 0) a.loss[w] = ls;
 }
 
