@@ -238,35 +238,52 @@ __global__ void __launch_bounds__(256) kl_lse_kernel(KlArgs a) {
 
 // The index log-sum-exp of every (row, index head): its entries' block
 // partials combined in slot order.  One thread per (sequence, index head, row).
+// (max, sum) pairs of the log2-domain softmax: B merged into A.
+__device__ __forceinline__ void merge_ml(float& M, float& L, float M2, float L2) {
+  if (!(L2 > 0.f)) return;
+  if (!(L > 0.f)) {
+    M = M2;
+    L = L2;
+  } else if (M2 > M) {
+    L = L * exp2f(M - M2) + L2;
+    M = M2;
+  } else {
+    L += L2 * exp2f(M2 - M);
+  }
+}
+
 __global__ void __launch_bounds__(256) kl_lse_merge_kernel(KlArgs a) {
-  const long long x = (long long)blockIdx.x * 256 + threadIdx.x;  // (b * 4 + i) * Sq + t
-  if (x >= (long long)a.B * kIdxHeads * a.Sq) return;
-  const int t = (int)(x % a.Sq);
-  const long long bi = x / a.Sq;
+  // 16 lanes per (row, index head): lane l merges slots l, l + 16, l + 32, ...
+  // in that order (the slot positions read 16 at a time, every load of a
+  // batch issued first), then the 16 lanes' pairs are merged by xor steps 1,
+  // 2, 4, 8 (both lanes of a step form the same sum: deterministic)
+  const long long x = ((long long)blockIdx.x * 256 + threadIdx.x) >> 4;  // (b * 4 + i) * Sq + t
+  const int l = threadIdx.x & 15;
+  const long long nx = (long long)a.B * kIdxHeads * a.Sq;
+  const long long xc = x < nx ? x : nx - 1;
+  const int t = (int)(xc % a.Sq);
+  const long long bi = xc / a.Sq;
   const int i = (int)(bi % kIdxHeads), b = (int)(bi / kIdxHeads);
   const int h = i % a.Hkv, m = i / a.Hkv;
   const int32_t* sp = a.slotpos + (((long long)b * a.Hkv + h) * a.Sq + t) * a.top_k;
   float M = -__builtin_huge_valf(), L = 0.f;
-  // eight slots' partials loaded together, then combined in slot order
-  for (int s0 = 0; s0 < a.top_k; s0 += 8) {
-    f32x2 v[8];
+  for (int s0 = 0; s0 < a.top_k; s0 += 64) {
+    int ev[4];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const int e = s0 + x < a.top_k ? sp[s0 + x] : -1;
-      v[x] = e >= 0 ? a.part_ml[(long long)e * a.nih + m] : f32x2{0.f, 0.f};
-    }
+    for (int r = 0; r < 4; ++r) ev[r] = sp[min(s0 + l + 16 * r, a.top_k - 1)];
+    f32x2 v[4];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      if (!(v[x][1] > 0.f)) continue;
-      if (v[x][0] > M) {
-        L = L * exp2f(M - v[x][0]) + v[x][1];
-        M = v[x][0];
-      } else {
-        L += v[x][1] * exp2f(v[x][0] - M);
-      }
-    }
+    for (int r = 0; r < 4; ++r) v[r] = a.part_ml[(long long)max(ev[r], 0) * a.nih + m];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (s0 + l + 16 * r < a.top_k && ev[r] >= 0) merge_ml(M, L, v[r][0], v[r][1]);
   }
-  a.lse_idx[x] = L > 0.f ? M + __log2f(L) : -__builtin_huge_valf();
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    const float M2 = __shfl_xor(M, o), L2 = __shfl_xor(L, o);
+    merge_ml(M, L, M2, L2);
+  }
+  if (x < nx && l == 0) a.lse_idx[x] = L > 0.f ? M + __log2f(L) : -__builtin_huge_valf();
 }
 
 // The forward's log-sum-exp in (row, query head) order and the log2 domain,
@@ -780,7 +797,7 @@ hipError_t launch_kl(const Shape& s, const KlArgs& a, hipStream_t st) {
   const long long nlse = (long long)s.B * s.Sq * s.Hq;
   kl_lse_t_kernel<<<(unsigned)((nlse + 255) / 256), 256, 0, st>>>(a);
   const long long rows = (long long)s.B * kIdxHeads * s.Sq;
-  kl_lse_merge_kernel<<<(unsigned)((rows + 255) / 256), 256, 0, st>>>(a);
+  kl_lse_merge_kernel<<<(unsigned)((rows * 16 + 255) / 256), 256, 0, st>>>(a);
   kl_entry_kernel<G><<<blocks, 256, 0, st>>>(a);
   kl_dik_kernel<<<blocks, 256, 0, st>>>(a);
   kl_dik_merge_kernel<<<dim3(s.nblk, s.B), 256, 0, st>>>(a);
