@@ -26,7 +26,7 @@
 //                        sum of 2^(s - max).
 //   kl_lse_t_kernel      the forward's log-sum-exp in (row, query head) order.
 //   kl_lse_merge_kernel  the index log-sum-exp per (row, index head), its
-//                        entries combined in slot order.
+//                        entries combined in a fixed order.
 //   kl_entry_kernel      per 16 rows of a block's list: P from the forward's
 //                        log-sum-exp, Q from the index log-sum-exp, C = Q - P;
 //                        per (list entry, index head) the loss partial, the
@@ -193,22 +193,43 @@ __global__ void __launch_bounds__(256) kl_lse_kernel(KlArgs a) {
   const int j0 = (int)((long long)split * total / nsplit);
   const int j1 = (int)((long long)(split + 1) * total / nsplit);
   const int rr = n / nih, m = n % nih;
+  if (j0 + wave >= j1) return;  // wave-uniform, and no barrier follows
+  // Jobs run as a pipeline: the list entry two jobs ahead and the index query
+  // row of the next job are loaded before the current job's products.  Loads
+  // of jobs past the split, or of rows past a list's end, read a clamped
+  // address; such columns are masked when the scores are formed.
+  auto entry = [&](int j) {
+    int q;
+    const int h = job_head(lnj, min(j, j1 - 1), q);
+    return lbeg[h] + min(q * rpj + rr, llen[h] - 1);
+  };
+  auto query = [&](int t, int h, bf16x8 (&f)[2]) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        a.iq + (((long long)b * a.Sq + t) * kIdxHeads + h + a.Hkv * m) * kIdxDim);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) f[ks] = as_bf16x8(src[4 * ks + g]);
+  };
+  int t_cur = a.lists[entry(j0 + wave)];
+  int t_nxt = a.lists[entry(j0 + wave + 4)];
+  bf16x8 iqf[2];
+  {
+    int q;
+    query(t_cur, job_head(lnj, j0 + wave, q), iqf);
+  }
   for (int j = j0 + wave; j < j1; j += 4) {
     int q;
     const int h = job_head(lnj, j, q);
     const int li = q * rpj + rr;  // the column's row: entry li of h's list
     const bool ok = li < llen[h];
-    const int t = ok ? a.lists[lbeg[h] + li] : 0;
-    const int pos = a.q_start + t;
-    const u32x4* src = reinterpret_cast<const u32x4*>(
-        a.iq + (((long long)b * a.Sq + t) * kIdxHeads + h + a.Hkv * m) * kIdxDim);
-    bf16x8 iqf[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 v = {0, 0, 0, 0};
-      if (ok) v = src[4 * ks + g];
-      iqf[ks] = as_bf16x8(v);
+    const int t = t_cur;
+    const int t_far = a.lists[entry(j + 8)];
+    bf16x8 iqn[2];
+    {
+      int qn;
+      query(t_nxt, job_head(lnj, min(j + 4, j1 - 1), qn), iqn);
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the next job's loads ahead of this job's products
+    const int pos = a.q_start + t;
     f32x4 si[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -217,27 +238,45 @@ __global__ void __launch_bounds__(256) kl_lse_kernel(KlArgs a) {
       for (int ks = 0; ks < 2; ++ks)
         si[mt] = mfma16(as_bf16x8(itile[islot(16 * mt + n, 4 * ks + g)]), iqf[ks], si[mt]);
     }
+    // max and sum over the keys each column attends: the max is taken on
+    // the raw scores and then scaled (the scale is positive and rounding is
+    // monotone, so this is the max of the scaled scores), each term
+    // 2^(s scale - max) with one fused multiply-add.  Jobs whose columns are
+    // all real rows attending the whole block skip the masks.
+    const bool full = ballot(ok && c * kBlock + kBlock - 1 <= pos) == ~0ull;
+    if (!full) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = c * kBlock + 16 * mt + 4 * g + r;
-        si[mt][r] = (ok && key <= pos) ? si[mt][r] * kLog2eB : -__builtin_huge_valf();
-      }
-    const float mx = wave_max_xor16_32(max16(si));
+        for (int r = 0; r < 4; ++r) {
+          const int key = c * kBlock + 16 * mt + 4 * g + r;
+          if (!(ok && key <= pos)) si[mt][r] = -__builtin_huge_valf();
+        }
+    }
+    const float mx = wave_max_xor16_32(max16(si)) * kLog2eB;
     float l = 0.f;
+    if (full) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        l += si[mt][r] != -__builtin_huge_valf() ? __builtin_amdgcn_exp2f(si[mt][r] - mx) : 0.f;
+        for (int r = 0; r < 4; ++r) l += __builtin_amdgcn_exp2f(__builtin_fmaf(si[mt][r], kLog2eB, -mx));
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          l += si[mt][r] != -__builtin_huge_valf()
+                   ? __builtin_amdgcn_exp2f(__builtin_fmaf(si[mt][r], kLog2eB, -mx)) : 0.f;
+    }
     l = wave_sum_xor16_32(l);
     if (ok && g == 0) a.part_ml[(long long)(lbeg[h] + li) * nih + m] = f32x2{mx, l};
+    t_cur = t_nxt;
+    t_nxt = t_far;
+    iqf[0] = iqn[0];
+    iqf[1] = iqn[1];
   }
 }
 
-// The index log-sum-exp of every (row, index head): its entries' block
-// partials combined in slot order.  One thread per (sequence, index head, row).
 // (max, sum) pairs of the log2-domain softmax: B merged into A.
 __device__ __forceinline__ void merge_ml(float& M, float& L, float M2, float L2) {
   if (!(L2 > 0.f)) return;
@@ -252,6 +291,8 @@ __device__ __forceinline__ void merge_ml(float& M, float& L, float M2, float L2)
   }
 }
 
+// The index log-sum-exp of every (row, index head): its entries' block
+// partials combined in a fixed order.
 __global__ void __launch_bounds__(256) kl_lse_merge_kernel(KlArgs a) {
   // 16 lanes per (row, index head): lane l merges slots l, l + 16, l + 32, ...
   // in that order (the slot positions read 16 at a time, every load of a
