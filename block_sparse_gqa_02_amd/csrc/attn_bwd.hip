@@ -329,7 +329,9 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdArgs a) {
 
 // dK and dV of one block: work-group per (block, KV head, sequence), wave w
 // owns keys 16w..16w+15.  Query columns (row slot i / G, head i % G) are taken
-// 64 at a time ("chunks") from the block's row list.  Chunk j+1's Q and dO rows
+// 64 at a time ("chunks") from the block's row list, from its end backwards:
+// the work-groups resident together then start on the same late rows, whose
+// Q and dO some of them find in cache.  Chunk j+1's Q and dO rows
 // travel by LDS-bound loads into the second pair of tiles while chunk j is
 // computed; the row indices that address them are loaded a chunk earlier.
 __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
@@ -370,9 +372,10 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
     colt[t] = 4 * (4 * wave + t) + lane / 16;
     cht[t] = (lane & 15) ^ (colt[t] & 15);
   }
-  // row of column col in chunk j (entries past the list repeat its first row;
-  // their columns are masked through cpos = -1)
-  auto row_of = [&](int j, int col) { return rows[min(j * R + col / a.G, len - 1)]; };
+  // row of column col in chunk j, which holds list entries (nchunk - 1 - j) R
+  // .. + R - 1 (entries past the list repeat its last row; their columns are
+  // masked through cpos = -1)
+  auto row_of = [&](int j, int col) { return rows[min((nchunk - 1 - j) * R + col / a.G, len - 1)]; };
   int rt[4];          // rows of this thread's slots, next chunk to stage
   int rmeta = 0;      // row of column lane, next chunk to stage
   // Column lane's metadata, loaded raw with its chunk's tiles and turned into
@@ -395,7 +398,7 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
                                        (__attribute__((address_space(3))) void*)(gdst + 64 * (4 * wave + t)),
                                        16, 0, 0);
     }
-    mok = j * R + lane / a.G < len;
+    mok = (nchunk - 1 - j) * R + lane / a.G < len;
     mrow = rmeta;
     const long long li = ((long long)b * a.Hq + h * a.G + lane % a.G) * a.Sq + rmeta;
     ml = a.lse[li];
