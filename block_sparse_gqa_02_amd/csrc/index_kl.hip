@@ -406,13 +406,12 @@ __global__ void __launch_bounds__(256, 2) kl_entry_kernel(KlArgs a) {
     // (A operand), and the log2-domain LSE of the lane's four output heads.
     // Two register sets: groups u and u + 1 are in flight while u - 1 is
     // computed.  The loads are unconditional (row 0 stands in for a missing
-    // row) and the zero for a missing row is applied when the group is used:
-    // a load under a branch, or a value selected right after its load, would
-    // make the wave wait for the load at once.
+    // row, whose P the key mask zeroes: lim = -1): a load under a branch, or
+    // a value selected right after its load, would make the wave wait for the
+    // load at once.
     bf16x8 qa[4], qb[4];
     f32x4 lsea, lseb;
-    bool qoka, qokb, loka, lokb;
-    auto load_group = [&](int tl, int u, bf16x8 (&qn)[4], f32x4& lsen, bool& qok, bool& lok) {
+    auto load_group = [&](int tl, int u, bf16x8 (&qn)[4], f32x4& lsen) {
       const int ta = __shfl(tl, u * RPG + n / G);
       const int to = __shfl(tl, u * RPG + (4 * g) / G);
       const long long ba = (long long)b * a.Sq + (ta >= 0 ? ta : 0);
@@ -420,37 +419,31 @@ __global__ void __launch_bounds__(256, 2) kl_entry_kernel(KlArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) qn[ks] = as_bf16x8(qs[4 * ks + g]);
       lsen = *reinterpret_cast<const f32x4*>(lse_h + ((long long)b * a.Sq + (to >= 0 ? to : 0)) * a.Hq);
-      qok = ta >= 0;
-      lok = to >= 0;
     };
     int tl = hj0 + wave < hj1 ? job_rows(hj0 + wave) : -1;
     if (hj0 + wave < hj1) {
-      load_group(tl, 0, qa, lsea, qoka, loka);
-      load_group(tl, 1, qb, lseb, qokb, lokb);
+      load_group(tl, 0, qa, lsea);
+      load_group(tl, 1, qb, lseb);
     }
     for (int j = hj0 + wave; j < hj1; j += 4) {
       const int tnext = j + 4 < hj1 ? job_rows(j + 4) : -1;
       const bool more = j + 4 < hj1;
       // ---- phase 1: P of the job's 16 rows into the wave's LDS tile
-      // group u from set a (u even) or b (u odd); the set is then refilled
-      // with group u + 2, of this job or the next
-      auto group = [&](int u, bf16x8 (&qn)[4], f32x4& lsen, bool& qok, bool& lok) {
-        bf16x8 qf[4];
-        const bf16x8 zero = as_bf16x8(u32x4{0, 0, 0, 0});
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qf[ks] = qok ? qn[ks] : zero;
-        const f32x4 lse2 = lok ? lsen : f32x4{0.f, 0.f, 0.f, 0.f};
+      // group u from set a (u even) or b (u odd); once its products are
+      // issued the set is refilled with group u + 2, of this job or the next
+      auto group = [&](int u, bf16x8 (&qn)[4], f32x4& lsen) {
         const int to = __shfl(tl, u * RPG + (4 * g) / G);
-        if (u + 2 < G) load_group(tl, u + 2, qn, lsen, qok, lok);
-        else if (more) load_group(tnext, u + 2 - G, qn, lsen, qok, lok);
         f32x4 sv[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           sv[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks)
-            sv[mt] = mfma16(qf[ks], as_bf16x8(ktile[swz_slot(16 * mt + n, 4 * ks + g)]), sv[mt]);
+            sv[mt] = mfma16(qn[ks], as_bf16x8(ktile[swz_slot(16 * mt + n, 4 * ks + g)]), sv[mt]);
         }
+        const f32x4 lse2 = lsen;
+        if (u + 2 < G) load_group(tl, u + 2, qn, lsen);
+        else if (more) load_group(tnext, u + 2 - G, qn, lsen);
         // lane (n, g): register r of sv[mt] is head 4 (g % HQ4) + r of row
         // u RPG + 4g / G for key 16mt + n
         const int lim = to >= 0 ? a.q_start + to - key0 : -1;  // last attended key of the block
@@ -485,8 +478,8 @@ __global__ void __launch_bounds__(256, 2) kl_entry_kernel(KlArgs a) {
       };
 #pragma unroll
       for (int u = 0; u < G; u += 2) {
-        group(u, qa, lsea, qoka, loka);
-        group(u + 1, qb, lseb, qokb, lokb);
+        group(u, qa, lsea);
+        group(u + 1, qb, lseb);
       }
       __builtin_amdgcn_wave_barrier();
       // ---- phase 2: per index head, the rows' index scores, C, loss and diq
