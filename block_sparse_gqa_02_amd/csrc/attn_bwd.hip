@@ -9,7 +9,8 @@
 //   Dsum = dout . o,  dp_a = dout . v_a,  ds_a = p_a (dp_a - Dsum),
 //   dq = scale sum ds_a k_a,  dk_a += scale ds_a q,  dv_a += p_a dout.
 // The selection gets no gradient.  Softmax weights are recomputed from the
-// forward's log-sum-exp; Dsum uses the forward's (bf16) output.
+// forward's log-sum-exp with v_exp_f32 directly, as the forward forms them
+// (weights below 2^-126 flush to zero); Dsum uses the forward's (bf16) output.
 //
 // Kernels, in launch order:
 //   dsum_kernel      Dsum per (sequence, query head, row).
@@ -317,7 +318,7 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int key = c * kBlock + 16 * mt + 4 * g + rr;
-        const float p = (col_ok && key <= pos) ? exp2f(s[mt][rr] * a.scale_log2 - lse2) : 0.f;
+        const float p = (col_ok && key <= pos) ? __builtin_amdgcn_exp2f(s[mt][rr] * a.scale_log2 - lse2) : 0.f;
         s[mt][rr] = p * (dp[mt][rr] - ds0);
       }
     pv_tr(s, tile, acc);  // dQ^T += K^T dS^T
@@ -452,7 +453,7 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
       for (int rr = 0; rr < 4; ++rr) {
         const int col = 16 * mt + 4 * g + rr;
         const float p = (n < nkeys && key <= cpos[bf][col])
-                            ? exp2f(x[mt][rr] * a.scale_log2 - clse[bf][col]) : 0.f;
+                            ? __builtin_amdgcn_exp2f(x[mt][rr] * a.scale_log2 - clse[bf][col]) : 0.f;
         x[mt][rr] = p;                              // P (columns x keys)
         y[mt][rr] = p * (y[mt][rr] - cds[bf][col]);  // dS
       }
@@ -635,7 +636,7 @@ __global__ void __launch_bounds__(kDqWaves * kWave, 1) dq_union_kernel(BwdArgs a
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = c * kBlock + 16 * mt + 4 * g + r;
-          const float p = (wants && key <= pos[j]) ? exp2f(sv[mt][r] * a.scale_log2 - lse2[j]) : 0.f;
+          const float p = (wants && key <= pos[j]) ? __builtin_amdgcn_exp2f(sv[mt][r] * a.scale_log2 - lse2[j]) : 0.f;
           sv[mt][r] = p * (dp[mt][r] - dsv[j]);
         }
       pv_tr(sv, kt, acc[j]);  // dQ^T += K^T dS^T
