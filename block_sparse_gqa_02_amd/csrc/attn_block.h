@@ -151,7 +151,8 @@ struct WaveAttn {
       for (int ks = 0; ks < 4; ++ks) sc[mt] = mfma16(as_bf16x8(kr[mt][ks]), qf[ks], sc[mt]);
     }
     after_s();
-    // online softmax (log2 domain); keys beyond pos are masked
+    // online softmax (log2 domain, v_exp_f32 directly: weights below 2^-126
+    // flush to zero); keys beyond pos are masked
     const int key0 = c * kBlock + 4 * g;
     const bool partial = c * kBlock + kBlock - 1 > pos;
     float bmax = -__builtin_huge_valf();
@@ -166,14 +167,14 @@ struct WaveAttn {
       }
     bmax = wave_max_xor16_32(bmax);
     const float m_new = fmaxf(m, bmax);
-    const float alpha = exp2f(m - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
     m = m_new;
     float psum = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(sc[mt][r] - m_new);
+        const float p = __builtin_amdgcn_exp2f(sc[mt][r] - m_new);
         sc[mt][r] = p;
         psum += p;
       }
