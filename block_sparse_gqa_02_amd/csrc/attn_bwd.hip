@@ -631,14 +631,28 @@ __global__ void __launch_bounds__(kDqWaves * kWave, 1) dq_union_kernel(BwdArgs a
           dp[mt] = mfma16(vf, gf[j][ks], dp[mt]);
         }
       }
+      // a column whose row did not pick the block gets P = 0 through an
+      // infinite log-sum-exp; the key mask is needed only where the block
+      // reaches past a column's row
+      const float lsew = wants ? lse2[j] : __builtin_huge_valf();
+      if (ballot(c * kBlock + kBlock - 1 <= pos[j]) == ~0ull) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = c * kBlock + 16 * mt + 4 * g + r;
-          const float p = (wants && key <= pos[j]) ? __builtin_amdgcn_exp2f(sv[mt][r] * a.scale_log2 - lse2[j]) : 0.f;
-          sv[mt][r] = p * (dp[mt][r] - dsv[j]);
-        }
+          for (int r = 0; r < 4; ++r) {
+            const float p = __builtin_amdgcn_exp2f(sv[mt][r] * a.scale_log2 - lsew);
+            sv[mt][r] = p * (dp[mt][r] - dsv[j]);
+          }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = c * kBlock + 16 * mt + 4 * g + r;
+            const float p = key <= pos[j] ? __builtin_amdgcn_exp2f(sv[mt][r] * a.scale_log2 - lsew) : 0.f;
+            sv[mt][r] = p * (dp[mt][r] - dsv[j]);
+          }
+      }
       pv_tr(sv, kt, acc[j]);  // dQ^T += K^T dS^T
     }
   };
