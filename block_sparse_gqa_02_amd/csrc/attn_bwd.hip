@@ -335,7 +335,7 @@ __global__ void __launch_bounds__(256) dq_kernel(BwdArgs a) {
 // Q and dO some of them find in cache.  Chunk j+1's Q and dO rows
 // travel by LDS-bound loads into the second pair of tiles while chunk j is
 // computed; the row indices that address them are loaded a chunk earlier.
-__global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256, 2) dkdv_kernel(BwdArgs a) {
   // Two tile pairs (64 columns x 128 dims of Q and of dO, swz_slot layout),
   // each tile its own LDS object and the chunk loop unrolled by two, so that
   // every access names its tile and the compiler does not make the reads of
@@ -344,6 +344,7 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
   __shared__ u32x4 gtile0[kBlock * 16], gtile1[kBlock * 16];
   __shared__ float clse[2][64], cds[2][64];
   __shared__ int cpos[2][64];
+  __shared__ int cpart[2];  // the chunk holds a row the block reaches past
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n = lane % 16, g = lane / 16;
@@ -419,10 +420,12 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
   auto step = [&](int j, int bf, const u32x4* qcur, const u32x4* gcur, u32x4* qnext,
                   u32x4* gnext) {
     wait_all_loads();  // chunk j's tiles (issued last iteration) and its metadata values
-    if (tid < 64) {
-      clse[bf][tid] = mok ? ml * kLog2eB : 0.f;
+    if (tid < 64) {  // wave 0, one lane per column; a column past the list gets P = 0
+      clse[bf][tid] = mok ? ml * kLog2eB : __builtin_huge_valf();
       cds[bf][tid] = mok ? md : 0.f;
       cpos[bf][tid] = mok ? a.q_start + mrow : -1;
+      const uint64_t part = ballot(mok && a.q_start + mrow < c * kBlock + kBlock - 1);
+      if (tid == 0) cpart[bf] = part != 0ull;
     }
     __syncthreads();
     if (j + 1 < nchunk) {
@@ -447,16 +450,28 @@ __global__ void __launch_bounds__(256) dkdv_kernel(BwdArgs a) {
       }
     }
     const int key = key0 + n;
+    if (!cpart[bf] && nkeys == 16) {  // every key of the wave attended by every row
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int col = 16 * mt + 4 * g + rr;
-        const float p = (n < nkeys && key <= cpos[bf][col])
-                            ? __builtin_amdgcn_exp2f(x[mt][rr] * a.scale_log2 - clse[bf][col]) : 0.f;
-        x[mt][rr] = p;                              // P (columns x keys)
-        y[mt][rr] = p * (y[mt][rr] - cds[bf][col]);  // dS
-      }
+        for (int rr = 0; rr < 4; ++rr) {
+          const int col = 16 * mt + 4 * g + rr;
+          const float p = __builtin_amdgcn_exp2f(x[mt][rr] * a.scale_log2 - clse[bf][col]);
+          x[mt][rr] = p;                              // P (columns x keys)
+          y[mt][rr] = p * (y[mt][rr] - cds[bf][col]);  // dS
+        }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int col = 16 * mt + 4 * g + rr;
+          const float p = (n < nkeys && key <= cpos[bf][col])
+                              ? __builtin_amdgcn_exp2f(x[mt][rr] * a.scale_log2 - clse[bf][col]) : 0.f;
+          x[mt][rr] = p;
+          y[mt][rr] = p * (y[mt][rr] - cds[bf][col]);
+        }
+    }
     pv_tr(x, gcur, dva);  // dV^T += dO^T P
     pv_tr(y, qcur, dka);  // dK^T += Q^T dS
     __syncthreads();      // tiles (qcur, gcur) free for chunk j + 2
