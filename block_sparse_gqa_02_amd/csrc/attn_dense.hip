@@ -157,7 +157,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) dense_prefill_kernel(DenseA
       float bm = -__builtin_huge_valf();
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        bm = fmaxf(bm, fmaxf(fmaxf(sc[gq][mt][0], sc[gq][mt][1]), fmaxf(sc[gq][mt][2], sc[gq][mt][3])));
+        bm = fmax_nn(bm, fmax_nn(fmax_nn(sc[gq][mt][0], sc[gq][mt][1]), fmax_nn(sc[gq][mt][2], sc[gq][mt][3])));
       bm = wave_max_xor16_32(bm) * a.scale_log2;
       const bool grow = bm > mref[gq] + kRescale;
       if (ballot(grow) != 0ull) {

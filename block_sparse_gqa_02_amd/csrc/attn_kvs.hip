@@ -241,7 +241,7 @@ __global__ void __launch_bounds__(kKvsWaves * kWave) kvs_attn_kernel(KvsArgs a) 
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) bm = fmaxf(bm, sc[mt][r]);
+      for (int r = 0; r < 4; ++r) bm = fmax_nn(bm, sc[mt][r]);
     const float m = wave_max_xor16_32(bm) * a.scale_log2;
     float ps = 0.f;
     bf16x8 pb[2];

@@ -277,10 +277,10 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) union_prefill_kernel(UnionA
           for (int r = 0; r < 4; ++r)
             if (key0 + 16 * mt + r > pc) sc[mt][r] = -__builtin_huge_valf();
       }
-      float bm = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-      bm = fmaxf(bm, fmaxf(fmaxf(fmaxf(sc[2][0], sc[2][1]), fmaxf(sc[2][2], sc[2][3])),
-                           fmaxf(fmaxf(sc[3][0], sc[3][1]), fmaxf(sc[3][2], sc[3][3]))));
+      float bm = fmax_nn(fmax_nn(fmax_nn(sc[0][0], sc[0][1]), fmax_nn(sc[0][2], sc[0][3])),
+                       fmax_nn(fmax_nn(sc[1][0], sc[1][1]), fmax_nn(sc[1][2], sc[1][3])));
+      bm = fmax_nn(bm, fmax_nn(fmax_nn(fmax_nn(sc[2][0], sc[2][1]), fmax_nn(sc[2][2], sc[2][3])),
+                           fmax_nn(fmax_nn(sc[3][0], sc[3][1]), fmax_nn(sc[3][2], sc[3][3]))));
       bm = act ? bm : -__builtin_huge_valf();
       bm = wave_max_xor16_32(bm) * a.scale_log2;
       // lazy rescale: move the reference max only when a block exceeds it by > 2^8

@@ -80,14 +80,21 @@ __device__ __forceinline__ float swap_lane_pairs(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xb1, 0xf, 0xf, false));
 }
 
+// max(a, b) of values that are never NaN (scores, -inf for masked ones).
+// It is the IEEE maximum (a NaN would propagate; -0 orders below +0), which
+// the compiler issues as is: fmaxf on values it cannot prove canonical (MFMA
+// results, lane-swap results) first quiets each operand with one more
+// v_max_f32.  gfx950 fuses chains of it into v_maximum3_f32.
+__device__ __forceinline__ float fmax_nn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Reductions over the four lanes l, l^16, l^32, l^48 (the same MFMA column
 // in every 16-lane row), with lane swaps instead of LDS permutes:
 // v_permlane16_swap pairs rows 0/1 and 2/3, v_permlane32_swap the two halves.
 __device__ __forceinline__ float wave_max_xor16_32(float v) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  v = fmax_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float wave_sum_xor16_32(float v) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -100,7 +107,7 @@ __device__ __forceinline__ float wave_sum_xor16_32(float v) {
 // max(b[l-32], b[l]) (one v_permlane32_swap).
 __device__ __forceinline__ float halves_max(float a, float b) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }

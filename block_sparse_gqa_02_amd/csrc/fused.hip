@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(256) fused_sweep_kernel(FusedArgs a) {
         const int r = 2 * p + half;
         float v = lds.stage[h][r][e];
 #pragma unroll
-        for (int j = 1; j < kIdxHeads / HKV; ++j) v = fmaxf(v, lds.stage[h + j * HKV][r][e]);
+        for (int j = 1; j < kIdxHeads / HKV; ++j) v = fmax_nn(v, lds.stage[h + j * HKV][r][e]);
         const uint32_t key = score_key(v);
         const int cnt0 = __builtin_amdgcn_readlane(cnt, 2 * p);
         const int cnt1 = __builtin_amdgcn_readlane(cnt, 2 * p + 1);

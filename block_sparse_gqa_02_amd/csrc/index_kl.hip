@@ -129,7 +129,7 @@ __device__ __forceinline__ float max16(const f32x4 (&v)[4]) {
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) m = fmaxf(m, v[mt][r]);
+    for (int r = 0; r < 4; ++r) m = fmax_nn(m, v[mt][r]);
   return m;
 }
 

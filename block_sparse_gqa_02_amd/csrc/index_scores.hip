@@ -79,7 +79,7 @@ index_scores_prefill_kernel(IndexArgs a) {
           for (int k = 0; k < 4; ++k) {
             float x = lds.stage[h][row][e4 + k];
 #pragma unroll
-            for (int i = h + HKV; i < kIdxHeads; i += HKV) x = fmaxf(x, lds.stage[i][row][e4 + k]);
+            for (int i = h + HKV; i < kIdxHeads; i += HKV) x = fmax_nn(x, lds.stage[i][row][e4 + k]);
             v[k] = x;
           }
           float* dst = a.scores + (((size_t)b * HKV + h) * a.Sq + t0 + row) * a.nblk + c;
@@ -161,11 +161,11 @@ __device__ __forceinline__ void decode_block_scores(const IndexArgs& a, int b, i
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       acc = mfma16(as_bf16x8(kr[mt]), qf, acc);
       const float hi0 = swap_lane_pairs(acc[1]), hi1 = swap_lane_pairs(acc[3]);
-      m = fmaxf(m, fmaxf(acc[0] + hi0, acc[2] + hi1));
+      m = fmax_nn(m, fmax_nn(acc[0] + hi0, acc[2] + hi1));
     }
     m = wave_max_xor16_32(m);  // lane 2i: block max of index head i
-    if (HKV <= 2) m = fmaxf(m, __shfl_xor(m, 4));
-    if (HKV == 1) m = fmaxf(m, __shfl_xor(m, 2));
+    if (HKV <= 2) m = fmax_nn(m, __shfl_xor(m, 4));
+    if (HKV == 1) m = fmax_nn(m, __shfl_xor(m, 2));
     if (!page_ok(c)) m = -__builtin_huge_valf();
     return m;
   };

@@ -118,11 +118,11 @@ __device__ __forceinline__ void index_sweep(const IndexTile& T, int cbeg, int ce
       acc[1][0] = mfma32(kfr[ks][1], qf[0][ks], acc[1][0]);
       acc[1][1] = mfma32(kfr[ks][1], qf[1][ks], acc[1][1]);
     }
-    float m0 = fmaxf(acc[0][0][0], acc[1][0][0]), m1 = fmaxf(acc[0][1][0], acc[1][1][0]);
+    float m0 = fmax_nn(acc[0][0][0], acc[1][0][0]), m1 = fmax_nn(acc[0][1][0], acc[1][1][0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) {
-      m0 = fmaxf(m0, fmaxf(acc[0][0][r], acc[1][0][r]));
-      m1 = fmaxf(m1, fmaxf(acc[0][1][r], acc[1][1][r]));
+      m0 = fmax_nn(m0, fmax_nn(acc[0][0][r], acc[1][0][r]));
+      m1 = fmax_nn(m1, fmax_nn(acc[0][1][r], acc[1][1][r]));
     }
     // lane l now holds the block max of row l for head `wave`
     L.stage[wave][lane][c - c0] = halves_max(m0, m1);
