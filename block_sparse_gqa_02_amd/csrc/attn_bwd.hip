@@ -461,15 +461,19 @@ __global__ void __launch_bounds__(256, 2) dkdv_kernel(BwdArgs a) {
           y[mt][rr] = p * (y[mt][rr] - cds[bf][col]);  // dS
         }
     } else {
+      // (the metadata is read before the mask is applied, so that the reads
+      // are not each put behind a branch)
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int col = 16 * mt + 4 * g + rr;
-          const float p = (n < nkeys && key <= cpos[bf][col])
-                              ? __builtin_amdgcn_exp2f(x[mt][rr] * a.scale_log2 - clse[bf][col]) : 0.f;
+          const float ls = clse[bf][col], ds = cds[bf][col];
+          const int cp = cpos[bf][col];
+          const float e = __builtin_amdgcn_exp2f(x[mt][rr] * a.scale_log2 - ls);
+          const float p = (n < nkeys && key <= cp) ? e : 0.f;
           x[mt][rr] = p;
-          y[mt][rr] = p * (y[mt][rr] - cds[bf][col]);
+          y[mt][rr] = p * (y[mt][rr] - ds);
         }
     }
     pv_tr(x, gcur, dva);  // dV^T += dO^T P
