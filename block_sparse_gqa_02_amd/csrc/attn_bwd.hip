@@ -388,23 +388,32 @@ __global__ void __launch_bounds__(256, 2) dkdv_kernel(BwdArgs a) {
   float ml = 0.f, md = 0.f;
   int mrow = 0;
   bool mok = false;
+  // the parts of the staging addresses that do not change from chunk to
+  // chunk: the sequence's Q and dO, each slot's head and chunk offset within
+  // a row, and the column's (sequence, head) row of the LSE and Dsum
+  const long long seq_elems = (long long)b * a.Sq * a.Hq * kHeadDim;
+  const uint16_t* qseq = a.q + seq_elems;
+  const uint16_t* gseq = a.dout + seq_elems;
+  const int rstride = a.Hq * kHeadDim;  // elements per query row
+  int coff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) coff[t] = (h * a.G + colt[t] % a.G) * kHeadDim + 8 * cht[t];
+  const long long lrow = ((long long)b * a.Hq + h * a.G + lane % a.G) * a.Sq;
   auto stage = [&](int j, u32x4* qdst, u32x4* gdst) {  // chunk j's loads (rows in rt / rmeta)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const long long e = (((long long)b * a.Sq + rt[t]) * a.Hq + h * a.G + colt[t] % a.G) *
-                          kHeadDim + 8 * cht[t];
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.q + e),
+      const long long e = (long long)rt[t] * rstride + coff[t];
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qseq + e),
                                        (__attribute__((address_space(3))) void*)(qdst + 64 * (4 * wave + t)),
                                        16, 0, 0);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(a.dout + e),
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gseq + e),
                                        (__attribute__((address_space(3))) void*)(gdst + 64 * (4 * wave + t)),
                                        16, 0, 0);
     }
     mok = (nchunk - 1 - j) * R + lane / a.G < len;
     mrow = rmeta;
-    const long long li = ((long long)b * a.Hq + h * a.G + lane % a.G) * a.Sq + rmeta;
-    ml = a.lse[li];
-    md = a.dsum[li];
+    ml = a.lse[lrow + rmeta];
+    md = a.dsum[lrow + rmeta];
   };
   auto fetch_rows = [&](int j) {  // row indices of chunk j into rt / rmeta
 #pragma unroll
